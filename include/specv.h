@@ -1,0 +1,154 @@
+/*
+ * specv — batched speculative-sampling verification for AMD Instinct MI355X (gfx950).
+ *
+ * For each of B sequences the library takes the draft model's logits at N
+ * positions and the verifier's logits at N+1 positions over one shared
+ * vocabulary of V tokens (the draft and verifier must share a tokenizer: blog
+ * post "LLM 추론 지연을 2배 이상 단축하는 투기적 디코딩(Speculative Decoding)과
+ * 검증 샘플링 아키텍처", tech.blogsailing.com, section 3, first design decision),
+ * and decides how many drafts to keep and which token to emit after them.
+ *
+ * The rule (lesson "추측 디코딩 — 초안 작성, 검증, 반복", factory.pai-world.com,
+ * section "핵심 알고리즘(Core algorithm)", steps 4-6, and its Steps 1-3):
+ *   p_i = softmax(draft_i / T), q_i = softmax(target_i / T) with the
+ *   sequence's temperature T; draft token d_i is accepted, left to right, iff
+ *   u_i < q_i(d_i) / p_i(d_i) (probability min(1, q/p)); a draft token with
+ *   p_i(d_i) = 0 is accepted. At the first rejection j the emitted token is
+ *   drawn from (q_j - p_j)_+ normalised; if all N are accepted it is drawn
+ *   from q_N (the bonus token). T = 0 is greedy: d_i is accepted iff it is the
+ *   first (lowest-index) argmax of target row i, and the emitted token is the
+ *   first argmax of target row j.
+ * Every draw uses an inverse CDF in ascending token order: the smallest k with
+ *   C_k > u * S, C_k = sum_{x<=k} w_x, S = sum_x w_x (the pages call a
+ *   categorical sampler without defining one; this is the library's choice).
+ * All randomness is passed in as uniforms, so outputs are a deterministic
+ * function of the inputs (bitwise reproducible across calls).
+ *
+ * Threading and streams: a handle owns scratch device memory and is not
+ * thread-safe. Calls on one handle must be ordered (one stream, or explicit
+ * synchronisation); use one handle per concurrent stream.
+ *
+ * Device pointers are plain HIP device addresses on the handle's device; the
+ * caller owns every buffer passed in and the library never frees them.
+ * `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define SPECV_API __attribute__((visibility("default")))
+#else
+#define SPECV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque handle; created by specv_create, released by specv_destroy. */
+typedef struct specv_ctx* specv_handle;
+
+/* Storage type of the logits. */
+enum specv_dtype {
+  SPECV_F32 = 0,  /* IEEE float32 */
+  SPECV_BF16 = 1, /* bfloat16 (upper half of a float32) */
+};
+
+/* Return codes. Host-detectable errors return before anything is enqueued. */
+enum specv_status {
+  SPECV_OK = 0,
+  SPECV_EINVAL = -1, /* bad argument: null pointer, size out of range, bad dtype */
+  SPECV_ENOMEM = -2, /* device allocation failed in specv_create */
+  SPECV_EHIP = -3,   /* a HIP runtime call or kernel launch failed */
+  SPECV_EALIGN = -4, /* a device pointer is not aligned as required */
+  SPECV_ESTATE = -5, /* specv_row_stats before any successful specv_verify */
+};
+
+/* Largest n_draft a handle accepts (one 64-lane wavefront holds a sequence's decisions). */
+#define SPECV_MAX_DRAFT 64
+
+/*
+ * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,
+ * vocabulary size `vocab` (V >= 1) and logits stored as `dtype`, on HIP device
+ * `device`. Allocates the scratch workspace on that device (size grows with
+ * max_batch * (2*max_draft+1) * ceil(V/8192)). On success *out is set and
+ * SPECV_OK returned; on failure *out is NULL.
+ * Errors: SPECV_EINVAL (out NULL, max_batch < 1, max_draft outside
+ * [1, SPECV_MAX_DRAFT], vocab < 1 or > 2^30, unknown dtype, bad device),
+ * SPECV_ENOMEM, SPECV_EHIP.
+ */
+SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int dtype, int device);
+
+/*
+ * Verify one batch. All pointers are device pointers; layouts are row-major
+ * and contiguous:
+ *   draft_logits    [batch][n_draft][V]    dtype; 16-byte aligned
+ *   target_logits   [batch][n_draft+1][V]  dtype; 16-byte aligned
+ *   draft_tokens    [batch][n_draft]       int32 in [0, V)
+ *   accept_uniforms [batch][n_draft]       float32 in [0, 1): u_i of decision i
+ *   sample_uniforms [batch]                float32 in [0, 1): the one draw per sequence
+ *   temperature     [batch]                float32; 0 = greedy, > 0 finite = sampled
+ *   out_tokens      [batch][n_draft+1]     int32, written: d_0..d_{j-1}, the drawn
+ *                                          token at index j, then -1
+ *   out_n_accepted  [batch]                int32, written: j in [0, n_draft]
+ * Logits must be finite or -inf (a masked token), with at least one finite
+ * logit per row. Work is enqueued on `stream` and the call returns without
+ * waiting; outputs are valid once the stream reaches this point.
+ * Per-sequence input faults that only the device can see — a draft token
+ * outside [0, V), a temperature that is negative, NaN or infinite — make that
+ * sequence's out_n_accepted = -1 and all its out_tokens = -1; other sequences
+ * are unaffected.
+ * batch == 0 is a no-op returning SPECV_OK.
+ * Errors (nothing enqueued): SPECV_EINVAL (null handle or pointer, batch < 0
+ * or > max_batch, n_draft < 1 or > max_draft), SPECV_EALIGN (logits not
+ * 16-byte aligned, other arrays not 4-byte aligned), SPECV_EHIP (launch failure).
+ */
+SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
+                 const void* draft_logits, const void* target_logits,
+                 const int32_t* draft_tokens, const float* accept_uniforms,
+                 const float* sample_uniforms, const float* temperature,
+                 int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
+
+/*
+ * Diagnostics of the most recent specv_verify on this handle: for every
+ * sequence b and row r (draft rows 0..n_draft-1, then target rows 0..n_draft),
+ *   out_lse    [batch][2*n_draft+1] float32: log sum_x exp(z_x / T), the row's
+ *              tempered log-normaliser (lesson, "Core algorithm" step 2-3
+ *              probabilities p_i, q_i are exp(z/T - lse)); NaN for T = 0 rows,
+ *              for rows a greedy sequence never reads, and for invalid sequences;
+ *   out_argmax [batch][2*n_draft+1] int32: first index of the row's largest
+ *              logit; -1 where the row was not read.
+ * Both device pointers, 4-byte aligned. Enqueued on `stream`, which must be
+ * ordered after that verify call. Errors: SPECV_EINVAL, SPECV_ESTATE (no
+ * verify yet), SPECV_EHIP.
+ */
+SPECV_API int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream);
+
+/*
+ * Kernel timing (diagnostic). With enable != 0, every later specv_verify on
+ * this handle records a HIP event on its stream before each kernel stage and
+ * after the last one; specv_last_timings then waits for the most recent call's
+ * final event and writes the duration of each stage in milliseconds to
+ * ms[0..*count-1] (at most `capacity` entries; *count is the number of stages
+ * the call launched). specv_stage_name(i) names stage i. Recording events
+ * adds a few microseconds per call, so leave it off when timing whole calls.
+ * Errors: SPECV_EINVAL (null handle/pointers, capacity < 1), SPECV_ESTATE (no
+ * timed call yet), SPECV_EHIP.
+ */
+SPECV_API int specv_set_timing(specv_handle h, int enable);
+SPECV_API int specv_last_timings(specv_handle h, float* ms, int capacity, int* count);
+SPECV_API const char* specv_stage_name(int stage);
+
+/* Release the handle and its workspace (synchronises the handle's device first). NULL is ignored. */
+SPECV_API void specv_destroy(specv_handle h);
+
+/* Static description of a return code. */
+SPECV_API const char* specv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECV_H */

@@ -1,0 +1,84 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+The library must load, export every entry point that include/specv.h declares
+(and the binding must name the same ones), agree with the header on status
+codes, and reject bad arguments that are caught before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_sampling_verification_specv_amd as specv
+from speculative_sampling_verification_specv_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specv.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    return re.findall(r"SPECV_API\s+[\w\s\*]+?\b(specv_\w+)\s*\(", _header_text())
+
+
+def test_header_declares_the_boundary():
+    assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
+                                          "specv_strerror", "specv_set_timing", "specv_last_timings",
+                                          "specv_stage_name"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = specv.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(_lib._SIGNATURES)
+
+
+def test_status_codes_match_header():
+    text = _header_text()
+    for name in ("SPECV_OK", "SPECV_EINVAL", "SPECV_ENOMEM", "SPECV_EHIP", "SPECV_EALIGN", "SPECV_ESTATE",
+                 "SPECV_F32", "SPECV_BF16"):
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(_lib, name), name
+    m = re.search(r"#define\s+SPECV_MAX_DRAFT\s+(\d+)", text)
+    assert int(m.group(1)) == _lib.SPECV_MAX_DRAFT
+
+
+def test_strerror_covers_codes():
+    seen = set()
+    for code in (0, -1, -2, -3, -4, -5):
+        s = specv.specv_strerror(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in specv.specv_strerror(-99)
+
+
+def test_argument_errors_before_any_device_call():
+    lib = specv.load_library()
+    h = ctypes.c_void_p()
+    assert lib.specv_create(None, 1, 1, 16, 0, 0) == _lib.SPECV_EINVAL
+    for args in ((0, 4, 16, 0), (1, 0, 16, 0), (1, 65, 16, 0), (1, 4, 0, 0), (1, 4, (1 << 30) + 1, 0),
+                 (1, 4, 16, 2), (1, 4, 16, -1)):
+        assert lib.specv_create(ctypes.byref(h), *args, 0) == _lib.SPECV_EINVAL, args
+        assert h.value is None
+    null = [None] * 9
+    assert lib.specv_verify(None, 1, 1, *null) == _lib.SPECV_EINVAL
+    assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
+    lib.specv_destroy(None)  # no-op
+    assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
+    n = ctypes.c_int()
+    assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
+    assert specv.specv_stage_name(0) == "row_stats"
+    assert specv.specv_stage_name(99) is None
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load_library(str(tmp_path / "libspecv.so"))
