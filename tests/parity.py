@@ -145,8 +145,9 @@ def check_row_stats(batch: synth.Batch, gpu: GpuResult, seqs=None):
         d64 = synth.widen(batch.draft_logits[s], batch.dtype)
         t64 = synth.widen(batch.target_logits[s], batch.dtype)
         rows = np.concatenate([d64, t64], axis=0)
-        if not (np.isfinite(T) and T >= 0):
-            assert np.all(gpu.argmax[s] == -1)
+        toks = batch.draft_tokens[s]
+        if not (np.isfinite(T) and T >= 0) or np.any((toks < 0) | (toks >= batch.vocab)):
+            assert np.all(gpu.argmax[s] == -1) and np.all(np.isnan(gpu.lse[s]))
             continue
         read = np.arange(2 * N + 1) >= (N if T == 0.0 else 0)
         want_arg = np.argmax(rows, axis=-1)
