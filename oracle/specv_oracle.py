@@ -40,6 +40,9 @@ Readings where the pages are silent (each also listed in the design notes):
   back to q_j.
 * One accept uniform per position (u_i) and one sample uniform per sequence are
   passed in; the accept test is strict.
+* The temperature domain is 0 or a finite T >= 2^-60; other values mark the
+  sequence invalid (n_accepted = -1, all tokens -1), as do draft tokens outside
+  [0, V).
 * Decision margins, the distance of a float decision from its boundary, are
   recorded so that a parity check can tell rounding ties from real errors:
   |u_i - q_i(d_i)/p_i(d_i)| for each accept test made, and
@@ -136,8 +139,14 @@ def inverse_cdf(w: np.ndarray, u: float):
     return k, margin, S
 
 
+# Temperatures the verification contract accepts: 0 (greedy) or a finite
+# T >= 2^-60. Anything else (negative, NaN, infinite, or positive below 2^-60)
+# marks the sequence invalid.
+MIN_TEMPERATURE = 2.0 ** -60
+
+
 def _valid(T: float, tokens: np.ndarray, V: int) -> bool:
-    if not math.isfinite(T) or T < 0.0:
+    if not math.isfinite(T) or T < 0.0 or 0.0 < T < MIN_TEMPERATURE:
         return False
     return bool(np.all((tokens >= 0) & (tokens < V)))
 

@@ -1,14 +1,17 @@
 // C-ABI host side of libspecv: handle, workspace, argument checks, launches.
 // The public contract (layouts, ownership, errors) is in include/specv.h.
 
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "specv.h"
 #include "specv_internal.h"
+#include "specv_math.h"
 
 struct specv_ctx {
   int device;
@@ -21,6 +24,8 @@ struct specv_ctx {
   specv::Workspace ws;
   int last_batch;  // -1 until a verify succeeds
   int last_n_draft;
+  unsigned epoch;               // epoch of the last launched call (0: none yet)
+  specv::LaunchConfig config;   // grid cap, item lags and wait timeout
   bool timing;                                  // record stage events on every verify
   bool timed_call;                              // the last verify recorded them
   int timed_stages;                             // stages the last timed verify launched
@@ -52,6 +57,34 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+long env_long(const char* name, long fallback) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == 0) return fallback;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (end != nullptr && *end == 0) ? x : fallback;
+}
+
+// Grid cap, item lags and wait timeout. Defaults suit MI355X; the environment
+// variables SPECV_BLOCKS_PER_CU, SPECV_LAG_DECIDE, SPECV_LAG_DRAW1,
+// SPECV_LAG_DRAW2 and SPECV_WAIT_TIMEOUT_US override them (tuning and tests).
+bool init_config(specv_ctx* h) {
+  int cus = 0, clock_khz = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess) return false;
+  const int occ = specv::max_blocks_per_cu(h->dtype);
+  if (occ < 1) return false;
+  const long per_cu = std::max(1L, std::min<long>(occ, env_long("SPECV_BLOCKS_PER_CU", 3)));
+  h->config.max_blocks = static_cast<long long>(per_cu) * cus;
+  h->config.lag_decide = static_cast<int>(std::max(0L, env_long("SPECV_LAG_DECIDE", 4)));
+  h->config.lag_draw1 = static_cast<int>(std::max<long>(h->config.lag_decide, env_long("SPECV_LAG_DRAW1", 8)));
+  h->config.lag_draw2 = static_cast<int>(std::max<long>(h->config.lag_draw1, env_long("SPECV_LAG_DRAW2", 12)));
+  const long timeout_us = std::max(0L, env_long("SPECV_WAIT_TIMEOUT_US", 200));
+  h->config.timeout_ticks = static_cast<unsigned long long>(timeout_us) * static_cast<unsigned long long>(clock_khz) / 1000ULL;
+  h->config.epoch = 0;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,19 +114,20 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const int nch = specv::ceil_div(vocab, specv::kStatsChunk);
   const int nsch = specv::ceil_div(vocab, specv::kSampChunk);
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
+  const size_t n_stat = rows * size_t(nch) * 2;
+  const size_t n_seq = size_t(max_batch) * 2;
+  const size_t n_norm = size_t(max_batch) * size_t(nsch) * 4;
+  const size_t n_wsum = size_t(max_batch) * size_t(nsch) * 2;
+  const size_t n_words = n_stat + n_seq + n_norm + n_wsum;
   size_t off = 0;
-  const size_t off_partials = off;
-  off = align_up(off + rows * nch * sizeof(specv::RowPartial), 256);
+  const size_t off_words = off;
+  off = align_up(off + n_words * sizeof(uint64_t), 256);
+  const size_t off_table = off;
+  off = align_up(off + specv::kExpTableSize * sizeof(double), 256);
   const size_t off_lse = off;
   off = align_up(off + rows * sizeof(float), 256);
   const size_t off_argmax = off;
   off = align_up(off + rows * sizeof(int), 256);
-  const size_t off_seq = off;
-  off = align_up(off + size_t(max_batch) * sizeof(specv::SeqState), 256);
-  const size_t off_norm = off;
-  off = align_up(off + size_t(max_batch) * nsch * sizeof(double2), 256);
-  const size_t off_wsum = off;
-  off = align_up(off + size_t(max_batch) * nsch * sizeof(double), 256);
 
   DeviceGuard guard(device);
   if (!guard.ok()) return SPECV_EHIP;
@@ -111,14 +145,31 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->vocab = vocab;
   h->dtype = dtype;
   h->mem_bytes = off;
-  h->ws.partials = reinterpret_cast<specv::RowPartial*>(base + off_partials);
+  uint64_t* words = reinterpret_cast<uint64_t*>(base + off_words);
+  h->ws.stat_words = words;
+  h->ws.seq_words = words + n_stat;
+  h->ws.norm_words = words + n_stat + n_seq;
+  h->ws.wsum_words = words + n_stat + n_seq + n_norm;
+  h->ws.n_words = static_cast<long long>(n_words);
+  h->ws.exp_table = reinterpret_cast<double*>(base + off_table);
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
   h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
-  h->ws.seq = reinterpret_cast<specv::SeqState*>(base + off_seq);
-  h->ws.norm_part = reinterpret_cast<double2*>(base + off_norm);
-  h->ws.wsum_part = reinterpret_cast<double*>(base + off_wsum);
   h->ws.n_stats_chunks = nch;
   h->ws.n_samp_chunks = nsch;
+  double table[specv::kExpTableSize];
+  for (int j = 0; j < specv::kExpTableSize; ++j) table[j] = double(exp2l((long double)j / specv::kExpTableSize));
+  if (hipMemset(words, 0, n_words * sizeof(uint64_t)) != hipSuccess ||
+      hipMemcpy(h->ws.exp_table, table, sizeof table, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(h->mem);
+    delete h;
+    return SPECV_EHIP;
+  }
+  if (!init_config(h)) {
+    (void)hipFree(h->mem);
+    delete h;
+    return SPECV_EHIP;
+  }
+  h->epoch = 0;
   h->last_batch = -1;
   h->last_n_draft = 0;
   h->timing = false;
@@ -159,10 +210,19 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned epoch = h->epoch + 1;
+  if (epoch > specv::kMaxEpoch) {
+    // Epoch numbers are about to repeat: clear every tagged word first.
+    if (specv::clear_words(h->ws.stat_words, h->ws.n_words, st) != hipSuccess) return SPECV_EHIP;
+    epoch = 1;
+  }
+  specv::LaunchConfig cfg = h->config;
+  cfg.epoch = epoch;
   int stages = 0;
-  if (specv::launch_verify(a, h->ws, static_cast<hipStream_t>(stream), h->timing ? h->events : nullptr,
-                           &stages) != hipSuccess)
+  if (specv::launch_verify(a, h->ws, cfg, st, h->timing ? h->events : nullptr, &stages) != hipSuccess)
     return SPECV_EHIP;
+  h->epoch = epoch;
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;

@@ -1,4 +1,4 @@
-// Internal interface between the C-ABI host code and the gfx950 kernels.
+// Internal interface between the C-ABI host code and the gfx950 kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,38 +6,30 @@
 
 namespace specv {
 
-constexpr int kThreads = 256;       // threads per workgroup (4 wave64s)
-constexpr int kStatsChunk = 8192;   // logits per row-statistics work item
-constexpr int kSampChunk = 4096;    // logits per sampler work item
-constexpr int kDecideThreads = 64;  // one wave64 per sequence decides
+constexpr int kThreads = 256;      // threads per workgroup (4 wave64s)
+constexpr int kStatsChunk = 8192;  // logits per row-statistics work item
+constexpr int kSampChunk = 2048;   // logits per draw work item
 
-// Partial statistics of one (row, chunk): m = largest raw logit, s = sum of
-// 2^((z - m) * c) with c = log2(e) / T, idx = first index attaining m.
-struct RowPartial {
-  float m;
-  float s;
-  int idx;
-  int pad;
-};
+// Smallest positive temperature accepted: keeps log2(e)/T and max|z|*log2(e)/T
+// finite in fp32 for logits up to 2^64 in magnitude.
+constexpr float kMinTemperature = 0x1p-60f;
+
+// Largest call epoch before the tagged words are cleared and numbering restarts.
+constexpr unsigned kMaxEpoch = 0xffffu;
 
 enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
-// What the decision left for the sampler of one sequence.
-struct SeqState {
-  int mode;        // SeqMode
-  int j;           // first rejected position, or N when all were accepted
-  float m_target;  // largest raw logit of the target row drawn from
-  float m_draft;   // largest raw logit of draft row j (residual only)
-  double inv_t;    // 1 / T in fp64
-};
-
+// Scratch device memory owned by a handle. Every word is 64 bits: a 48-bit
+// payload and the 16-bit epoch of the call that wrote it.
 struct Workspace {
-  RowPartial* partials;  // [max_batch * (2*max_draft+1)][n_stats_chunks]
+  uint64_t* stat_words;  // [max_batch * (2*max_draft+1)][n_stats_chunks][2]
+  uint64_t* seq_words;   // [max_batch][2]
+  uint64_t* norm_words;  // [max_batch][n_samp_chunks][4]
+  uint64_t* wsum_words;  // [max_batch][n_samp_chunks][2]
+  long long n_words;     // total words, all four arrays (contiguous from stat_words)
+  double* exp_table;     // [64]: 2^(j/64)
   float* row_lse;        // [batch][2N+1] of the last call
   int* row_argmax;       // [batch][2N+1] of the last call
-  SeqState* seq;         // [max_batch]
-  double2* norm_part;    // [max_batch][n_samp_chunks]: fp64 sums of exp((z - m)/T), target and draft
-  double* wsum_part;     // [max_batch][n_samp_chunks]: fp64 sums of the draw's weights
   int n_stats_chunks;
   int n_samp_chunks;
 };
@@ -57,6 +49,16 @@ struct VerifyArgs {
   int* out_n;
 };
 
+// Per-call launch parameters chosen by the host.
+struct LaunchConfig {
+  long long max_blocks;              // persistent grid cap
+  int lag_decide;                    // slots groups (sequences) between STAT(b) and DECIDE(b)
+  int lag_draw1;                     // ... and DRAW1(b, *)
+  int lag_draw2;                     // ... and DRAW2(b)
+  unsigned epoch;                    // 1..kMaxEpoch
+  unsigned long long timeout_ticks;  // wall-clock ticks a wait lasts before it computes the item itself
+};
+
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kMaxStages = 8;
@@ -64,10 +66,16 @@ constexpr int kMaxStages = 8;
 // Names of the kernel stages launch_verify enqueues, in order.
 const char* stage_name(int stage);
 
+// Workgroups of the verify kernel one CU can hold.
+int max_blocks_per_cu(int dtype);
+
+// Zero n words (epoch 0 is never used, so cleared words read as stale).
+hipError_t clear_words(uint64_t* p, long long n, hipStream_t stream);
+
 // Enqueue the whole verification on `stream`. If `events` is non-null it holds
 // kMaxStages + 1 events: events[k] is recorded before stage k and
 // events[*n_stages] after the last stage.
-hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* events,
-                         int* n_stages);
+hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, const LaunchConfig& cfg, hipStream_t stream,
+                         hipEvent_t* events, int* n_stages);
 
 }  // namespace specv

@@ -1,45 +1,67 @@
-// gfx950 kernels for batched speculative-sampling verification.
+// gfx950 kernel for batched speculative-sampling verification: one persistent launch.
 //
 // Pages: lesson "추측 디코딩 — 초안 작성, 검증, 반복" (factory.pai-world.com),
-// section "핵심 알고리즘(Core algorithm)" steps 4-6 with its "Step 1" (accept
-// test) and "Step 2" (residual distribution); blog "…투기적 디코딩(Speculative
-// Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
+// section "핵심 알고리즘(Core algorithm)" steps 4-6 with "Step 1: 거절 단계" (the
+// accept test) and "Step 2: 잔차 분포" (the residual); blog "…투기적 디코딩
+// (Speculative Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
 // verification loop.
 //
-// Pipeline for one call (B sequences, N drafts, vocabulary V):
-//   1. row_stats: every (row, 8192-logit chunk) reduces to (max, sum 2^((z-max)c),
-//      first argmax) in fp32; streaming, HBM-bound. Greedy sequences skip
-//      their draft rows.
-//   2. decide: one wave per sequence merges the chunk partials into per-row
-//      log-normalisers, runs the N accept tests in fp64 and finds the first
-//      rejection with a ballot.
-//   3. resid_norm: for sequences that rejected, fp64 normalisers of target and
-//      draft row j, recomputed from the logits (fp32 normalisers are not
-//      accurate enough for the residual draw).
-//   4. weights: fp64 per-chunk sums of the draw weights, (q_j - p_j)_+ after a
-//      rejection or exp((z - max)/T) of target row N for the bonus.
-//   5. draw: one workgroup per sequence finds the chunk where the cumulative
-//      weight crosses u * S and scans it in fp64 to find the token.
+// Work items, per sequence b (B sequences, N drafts, 2N+1 rows of V logits):
+//   STAT(b, r, c)  fp32 (max, sum 2^(z*c - K), first argmax) of 8192 logits of row r.
+//   DECIDE(b)      merge STAT partials into per-row log-normalisers, run the N
+//                  accept tests in fp64, find the first rejection j.
+//   DRAW1(b, c)    fp64 exp of 2048 logits of the row(s) the draw needs; after a
+//                  rejection, the two fp64 normalisers (sum over all chunks) then
+//                  the weight sum of (q_j - p_j)_+ over the chunk; for the bonus,
+//                  the sum of exp((z - max)/T) of target row N.
+//   DRAW2(b)       inverse CDF: find the chunk where the cumulative weight
+//                  crosses u*S, rescan it in fp64, write the token.
+// Items are laid out in slots, sequence-major, with DECIDE, DRAW1 and DRAW2 of
+// sequence b placed a few sequences after STAT(b, ...); slot s belongs to
+// workgroup s mod G, so the sampler's fp64 work overlaps later sequences' HBM
+// streaming.
+//
+// Communication between workgroups uses no fences and no read-modify-write
+// atomics (both are very slow across this GPU's per-XCD L2 caches). Each result
+// travels in 64-bit words written and read with relaxed agent-scope atomics
+// (single-copy atomic, coherent across XCDs); every word carries the call's
+// 16-bit epoch, so a reader knows a word is from this call without any reset.
+// A reader polls until all the words it needs carry the epoch. If that takes
+// longer than a timeout (the producer's workgroup may not be resident), it
+// computes the missing items itself: every item is a deterministic function of
+// the inputs, so a duplicate write stores identical bits. Progress therefore
+// never depends on workgroups being co-resident.
+//
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
 #include <float.h>
 #include <limits.h>
 #include <math.h>
 
+#include <numeric>
+
 #include "specv_internal.h"
+#include "specv_math.h"
 
 namespace specv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
+constexpr int kSampPer = kSampChunk / kThreads;  // logits per thread in a DRAW1 item
+constexpr int kMaxRows = 2 * 64 + 1;
 
-__device__ __forceinline__ bool temperature_valid(float t) { return t >= 0.0f && t <= kFltMax; }
+__device__ __forceinline__ bool temperature_valid(float t) {
+  return t == 0.0f || (t >= kMinTemperature && t <= kFltMax);
+}
 
-// c in 2^((z - m) * c) == exp((z - m) / T); clamped so a denormal T yields a
-// huge finite factor rather than inf (0 * inf would give NaN at z == m).
-__device__ __forceinline__ float exp2_coef(float t) { return fminf(kLog2e / t, kFltMax); }
+// c in 2^(z*c) == exp(z/T); finite for T >= kMinTemperature.
+__device__ __forceinline__ float exp2_coef(float t) { return kLog2e / t; }
+
+// K = fl(m * c), never contracted into a neighbouring add.
+__device__ __forceinline__ float scaled_max(float m, float c) { return __fmul_rn(m, c); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -75,28 +97,166 @@ struct Logit<uint16_t> {  // bfloat16 bits
 };
 
 // ---------------------------------------------------------------------------
-// Row statistics (max, tempered sum-exp, first argmax), fp32.
+// Epoch-tagged words.
 
-// Running state of one thread: m = largest logit seen, idx = its first index,
-// s = sum of 2^((z - shift) * c) where shift == m once a finite logit was seen
-// (0 before, when s is 0 too).
+__device__ __forceinline__ void publish(uint64_t* p, uint64_t payload48, unsigned epoch) {
+  __hip_atomic_store(p, (payload48 << 16) | (epoch & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tagged(uint64_t w, unsigned epoch) { return (w & 0xffffu) == (epoch & 0xffffu); }
+__device__ __forceinline__ uint64_t payload(uint64_t w) { return w >> 16; }
+
+// STAT partial: (m, s, idx) in two words.
+__device__ __forceinline__ void publish_partial(uint64_t* w, float m, float s, int idx, unsigned epoch) {
+  const uint32_t mb = __float_as_uint(m), sb = __float_as_uint(s);
+  publish(w, (uint64_t(mb) << 16) | (sb >> 16), epoch);
+  publish(w + 1, (uint64_t(sb & 0xffffu) << 32) | uint32_t(idx), epoch);
+}
+__device__ __forceinline__ void unpack_partial(uint64_t w0, uint64_t w1, float& m, float& s, int& idx) {
+  const uint64_t p0 = payload(w0), p1 = payload(w1);
+  m = __uint_as_float(uint32_t(p0 >> 16));
+  s = __uint_as_float((uint32_t(p0 & 0xffffu) << 16) | uint32_t(p1 >> 32));
+  idx = int(uint32_t(p1 & 0xffffffffu));
+}
+
+// fp64 value in two words.
+__device__ __forceinline__ void publish_f64(uint64_t* w, double v, unsigned epoch) {
+  const uint64_t b = double_to_bits(v);
+  publish(w, b >> 32, epoch);
+  publish(w + 1, b & 0xffffffffu, epoch);
+}
+__device__ __forceinline__ double unpack_f64(uint64_t w0, uint64_t w1) {
+  return bits_to_double((payload(w0) << 32) | (payload(w1) & 0xffffffffu));
+}
+
+// What DECIDE leaves for the draw of one sequence.
+struct SeqInfo {
+  int mode;  // SeqMode
+  int j;
+  float m_target;
+  float m_draft;
+};
+__device__ __forceinline__ void publish_seq(uint64_t* w, const SeqInfo& s, unsigned epoch) {
+  publish(w, (uint64_t(__float_as_uint(s.m_target)) << 16) | (uint64_t(s.j & 0xff) << 8) | uint64_t(s.mode & 0xff),
+          epoch);
+  publish(w + 1, uint64_t(__float_as_uint(s.m_draft)) << 16, epoch);
+}
+__device__ __forceinline__ SeqInfo unpack_seq(uint64_t w0, uint64_t w1) {
+  SeqInfo s;
+  const uint64_t p0 = payload(w0);
+  s.m_target = __uint_as_float(uint32_t(p0 >> 16));
+  s.j = int((p0 >> 8) & 0xff);
+  s.mode = int(p0 & 0xff);
+  s.m_draft = __uint_as_float(uint32_t(payload(w1) >> 16));
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameters and shared memory.
+
+struct Params {
+  const void* draft;
+  const void* target;
+  const int* tokens;
+  const float* accept_u;
+  const float* sample_u;
+  const float* temperature;
+  int* out_tokens;
+  int* out_n;
+  float* row_lse;
+  int* row_argmax;
+  uint64_t* stat_words;  // [B*R][nch][2]
+  uint64_t* seq_words;   // [B][2]
+  uint64_t* norm_words;  // [B][nsch][4]
+  uint64_t* wsum_words;  // [B][nsch][2]
+  const double* exp_table;
+  int batch;
+  int n_draft;
+  int vocab;
+  int nch;
+  int nsch;
+  int spg;  // slots per group
+  long long total_slots;
+  int lag_decide;
+  int lag_draw1;
+  int lag_draw2;
+  unsigned epoch;
+  unsigned long long timeout_ticks;
+};
+
+struct Shared {
+  double exp_table[kExpTableSize];
+  double red[kWaves * 2];
+  float row_m[kMaxRows];
+  double row_logz[kMaxRows];
+  int row_idx[kMaxRows];
+  int flag;
+  int pick[2];
+};
+
+__device__ __forceinline__ double block_sum(double v, Shared& sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double total = sh.red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) total += sh.red[w];
+  return total;
+}
+
+// True (in every thread) once all n words carry the epoch; false on timeout.
+__device__ bool block_wait(uint64_t* words, int n, const Params P) {
+  const unsigned long long t0 = wall_clock64();
+  while (true) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < n; i += kThreads) ok = ok && tagged(fetch(words + i), P.epoch);
+    if (__syncthreads_and(ok)) return true;
+    const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
+    if (__syncthreads_or(expired)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// True (in every thread) if the k words at p all carry the epoch.
+__device__ bool block_has(uint64_t* p, int k, const Params P, Shared& sh) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    for (int i = 0; i < k; ++i) ok = ok && tagged(fetch(p + i), P.epoch);
+    sh.flag = ok;
+  }
+  __syncthreads();
+  return sh.flag != 0;
+}
+
+// ---------------------------------------------------------------------------
+// STAT: fp32 row statistics of one chunk.
+
+// Running state: m = largest logit seen, idx = its first index, s = sum of
+// 2^(z*c - k) with k = fl(m*c) once a finite logit was seen (0 before, while
+// s is 0 too). The exact product m*c differs from k by r = fma(m, c, -k); the
+// decision step removes it.
 struct StatAcc {
   float m;
+  float k;
   float s;
-  float shift;
   int idx;
 };
 
 __device__ __forceinline__ void acc_init(StatAcc& a) {
   a.m = -INFINITY;
+  a.k = 0.0f;
   a.s = 0.0f;
-  a.shift = 0.0f;
   a.idx = INT_MAX;
 }
 
-// Fold n logits with consecutive indices base..base+n-1 into the state. Each
-// thread visits its indices in increasing order, so a strict '>' keeps the
-// first index of a repeated maximum.
+// Fold n logits with consecutive indices base..base+n-1. A thread visits its
+// indices in increasing order, so a strict '>' keeps a repeated maximum's
+// first index.
 template <bool kSampled, int n>
 __device__ __forceinline__ void acc_values(StatAcc& a, const float (&v)[n], int base, float c) {
   float vmax = v[0];
@@ -107,8 +267,9 @@ __device__ __forceinline__ void acc_values(StatAcc& a, const float (&v)[n], int 
 #pragma unroll
     for (int k = n - 1; k >= 0; --k) first = (v[k] == vmax) ? k : first;
     if (kSampled) {
-      a.s = (a.s == 0.0f) ? 0.0f : a.s * fast_exp2((a.shift - vmax) * c);
-      a.shift = vmax;
+      const float k_new = scaled_max(vmax, c);
+      a.s = (a.s == 0.0f) ? 0.0f : a.s * fast_exp2(a.k - k_new);
+      a.k = k_new;
     }
     a.m = vmax;
     a.idx = base + first;
@@ -116,7 +277,7 @@ __device__ __forceinline__ void acc_values(StatAcc& a, const float (&v)[n], int 
   if (kSampled) {
     float e[n];
 #pragma unroll
-    for (int k = 0; k < n; ++k) e[k] = fast_exp2((v[k] - a.shift) * c);
+    for (int k = 0; k < n; ++k) e[k] = fast_exp2(fmaf(v[k], c, -a.k));
 #pragma unroll
     for (int w = 1; w < n; w *= 2)
 #pragma unroll
@@ -125,14 +286,14 @@ __device__ __forceinline__ void acc_values(StatAcc& a, const float (&v)[n], int 
   }
 }
 
-// Merge partial (m2, s2, i2) into (m, s, i): larger max wins, sums are
-// rescaled to the common max, ties in the max keep the lower index.
+// Merge partial (m2, s2, i2) into (m, s, idx).
 template <bool kSampled>
 __device__ __forceinline__ void acc_merge(float& m, float& s, int& idx, float m2, float s2, int i2, float c) {
   const float mm = fmaxf(m, m2);
   if (kSampled) {
-    const float a = (m == mm) ? s : s * fast_exp2((m - mm) * c);
-    const float b = (m2 == mm) ? s2 : s2 * fast_exp2((m2 - mm) * c);
+    const float km = scaled_max(mm, c);
+    const float a = (m == mm) ? s : s * fast_exp2(scaled_max(m, c) - km);
+    const float b = (m2 == mm) ? s2 : s2 * fast_exp2(scaled_max(m2, c) - km);
     s = a + b;
   }
   idx = (m > m2) ? idx : ((m2 > m) ? i2 : min(idx, i2));
@@ -140,12 +301,12 @@ __device__ __forceinline__ void acc_merge(float& m, float& s, int& idx, float m2
 }
 
 template <typename T, bool kSampled>
-__device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t row_flat, int e0, int e1,
-                                            float c, StatAcc& a) {
+__device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t row_flat, int e0, int e1, float c,
+                                            StatAcc& a) {
   constexpr int kVec = Logit<T>::kVec;
   const int tid = threadIdx.x;
   // Element g of the flat buffer is 16-byte aligned iff g % kVec == 0 (the
-  // base pointer is 16-byte aligned).
+  // buffer base is 16-byte aligned); a misaligned row start peels a head.
   const int mis = int((row_flat + e0) % kVec);
   int ea = e0 + (kVec - mis) % kVec;
   if (ea > e1) ea = e1;
@@ -155,27 +316,25 @@ __device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t r
     const float v[1] = {Logit<T>::at(row, e0 + tid)};
     acc_values<kSampled>(a, v, e0 + tid, c);
   }
+  // A chunk holds at most kMaxVec 16-byte vectors per thread: issue all loads
+  // before any use so they are in flight together.
+  constexpr int kMaxVec = kStatsChunk / kVec / kThreads;
   const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row + ea);
-  int k = tid;
-  for (; k + 3 * kThreads < nv; k += 4 * kThreads) {
-    const uint4 x0 = vrow[k];
-    const uint4 x1 = vrow[k + kThreads];
-    const uint4 x2 = vrow[k + 2 * kThreads];
-    const uint4 x3 = vrow[k + 3 * kThreads];
-    float v[kVec];
-    Logit<T>::unpack(x0, v);
-    acc_values<kSampled>(a, v, ea + k * kVec, c);
-    Logit<T>::unpack(x1, v);
-    acc_values<kSampled>(a, v, ea + (k + kThreads) * kVec, c);
-    Logit<T>::unpack(x2, v);
-    acc_values<kSampled>(a, v, ea + (k + 2 * kThreads) * kVec, c);
-    Logit<T>::unpack(x3, v);
-    acc_values<kSampled>(a, v, ea + (k + 3 * kThreads) * kVec, c);
+  uint4 x[kMaxVec];
+#pragma unroll
+  for (int u = 0; u < kMaxVec; ++u) {
+    const int k = tid + u * kThreads;
+    if (k < nv) x[u] = vrow[k];
   }
-  for (; k < nv; k += kThreads) {
-    float v[kVec];
-    Logit<T>::unpack(vrow[k], v);
-    acc_values<kSampled>(a, v, ea + k * kVec, c);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < kMaxVec; ++u) {
+    const int k = tid + u * kThreads;
+    if (k < nv) {
+      float v[kVec];
+      Logit<T>::unpack(x[u], v);
+      acc_values<kSampled>(a, v, ea + k * kVec, c);
+    }
   }
   if (tid < e1 - et) {
     const float v[1] = {Logit<T>::at(row, et + tid)};
@@ -184,9 +343,7 @@ __device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t r
 }
 
 template <bool kSampled>
-__device__ __forceinline__ void block_merge(StatAcc& a, float c) {
-  __shared__ float sm_m[kWaves], sm_s[kWaves];
-  __shared__ int sm_i[kWaves];
+__device__ __forceinline__ void block_merge(StatAcc& a, float c, Shared& sh) {
   float m = a.m, s = a.s;
   int idx = a.idx;
 #pragma unroll
@@ -196,18 +353,21 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c) {
     const int i2 = __shfl_xor(idx, off);
     acc_merge<kSampled>(m, s, idx, m2, s2, i2, c);
   }
-  const int wave = threadIdx.x >> 6;
+  float* sm = reinterpret_cast<float*>(sh.red);  // 4 floats m, 4 floats s, 4 ints idx fit in red[8]
+  float* ss = sm + kWaves;
+  int* si = reinterpret_cast<int*>(ss + kWaves);
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) {
-    sm_m[wave] = m;
-    sm_s[wave] = s;
-    sm_i[wave] = idx;
+    sm[threadIdx.x >> 6] = m;
+    ss[threadIdx.x >> 6] = s;
+    si[threadIdx.x >> 6] = idx;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    m = sm_m[0];
-    s = sm_s[0];
-    idx = sm_i[0];
-    for (int w = 1; w < kWaves; ++w) acc_merge<kSampled>(m, s, idx, sm_m[w], sm_s[w], sm_i[w], c);
+    m = sm[0];
+    s = ss[0];
+    idx = si[0];
+    for (int w = 1; w < kWaves; ++w) acc_merge<kSampled>(m, s, idx, sm[w], ss[w], si[w], c);
     a.m = m;
     a.s = s;
     a.idx = idx;
@@ -215,400 +375,552 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(const T* __restrict__ draft,
-                                                             const T* __restrict__ target,
-                                                             const float* __restrict__ temperature, int n_draft,
-                                                             int vocab, int nch, RowPartial* __restrict__ partials) {
-  const int R = 2 * n_draft + 1;
-  const int item = blockIdx.x;
-  const int row = item / nch;
-  const int chunk = item - row * nch;
-  const int b = row / R;
-  const int lr = row - b * R;
-  const float t = temperature[b];
+__device__ __forceinline__ const T* row_ptr(const Params P, int b, int r, int64_t& row_flat) {
+  const int N = P.n_draft;
+  if (r < N) {
+    row_flat = (int64_t(b) * N + r) * P.vocab;
+    return static_cast<const T*>(P.draft) + row_flat;
+  }
+  row_flat = (int64_t(b) * (N + 1) + (r - N)) * P.vocab;
+  return static_cast<const T*>(P.target) + row_flat;
+}
+
+// Computes and publishes STAT(b, r, chunk). Skips rows the sequence never needs.
+template <typename T>
+__device__ void stat_item(const Params P, Shared& sh, int b, int r, int chunk) {
+  const float t = P.temperature[b];
   if (!temperature_valid(t)) return;
   const bool greedy = (t == 0.0f);
-  if (greedy && lr < n_draft) return;  // greedy verification never needs the draft rows
-  const bool is_draft = lr < n_draft;
-  const int64_t row_flat = is_draft ? (int64_t(b) * n_draft + lr) * vocab
-                                    : (int64_t(b) * (n_draft + 1) + (lr - n_draft)) * vocab;
-  const T* rowp = (is_draft ? draft : target) + row_flat;
+  if (greedy && r < P.n_draft) return;
+  int64_t row_flat;
+  const T* rowp = row_ptr<T>(P, b, r, row_flat);
   const int e0 = chunk * kStatsChunk;
-  const int e1 = min(vocab, e0 + kStatsChunk);
+  const int e1 = min(P.vocab, e0 + kStatsChunk);
   StatAcc a;
   acc_init(a);
   if (greedy) {
     stats_chunk<T, false>(rowp, row_flat, e0, e1, 0.0f, a);
-    block_merge<false>(a, 0.0f);
+    block_merge<false>(a, 0.0f, sh);
   } else {
     const float c = exp2_coef(t);
     stats_chunk<T, true>(rowp, row_flat, e0, e1, c, a);
-    block_merge<true>(a, c);
+    block_merge<true>(a, c, sh);
   }
   if (threadIdx.x == 0) {
-    RowPartial p;
-    p.m = a.m;
-    p.s = a.s;
-    p.idx = a.idx;
-    p.pad = 0;
-    partials[item] = p;
+    const int R = 2 * P.n_draft + 1;
+    publish_partial(P.stat_words + ((int64_t(b) * R + r) * P.nch + chunk) * 2, a.m, a.s, a.idx, P.epoch);
   }
 }
 
+// Ensures STAT partials of rows [r0, r1) of sequence b carry the epoch.
+template <typename T>
+__device__ void ensure_stats(const Params P, Shared& sh, int b, int r0, int r1) {
+  const int R = 2 * P.n_draft + 1;
+  uint64_t* base = P.stat_words + (int64_t(b) * R + r0) * P.nch * 2;
+  const int n = (r1 - r0) * P.nch * 2;
+  if (block_wait(base, n, P)) return;
+  for (int r = r0; r < r1; ++r)
+    for (int c = 0; c < P.nch; ++c)
+      if (!block_has(P.stat_words + ((int64_t(b) * R + r) * P.nch + c) * 2, 2, P, sh)) stat_item<T>(P, sh, b, r, c);
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// Decision: per-row log-normalisers, N accept tests, first rejection.
+// DECIDE: log-normalisers, accept tests, first rejection, outputs.
 
 template <typename T>
-__global__ __launch_bounds__(kDecideThreads) void decide_kernel(
-    const T* __restrict__ draft, const T* __restrict__ target, const int* __restrict__ tokens,
-    const float* __restrict__ accept_u, const float* __restrict__ temperature, int n_draft, int vocab, int nch,
-    const RowPartial* __restrict__ partials, float* __restrict__ row_lse, int* __restrict__ row_argmax,
-    SeqState* __restrict__ seq, int* __restrict__ out_tokens, int* __restrict__ out_n) {
-  constexpr int kMaxRows = 2 * 64 + 1;
-  __shared__ float sm_m[kMaxRows];
-  __shared__ double sm_logs[kMaxRows];
-  __shared__ int sm_idx[kMaxRows];
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int N = n_draft;
+__device__ void decide_item(const Params P, Shared& sh, int b) {
+  const int N = P.n_draft;
   const int R = 2 * N + 1;
-  const int* tok = tokens + int64_t(b) * N;
-  int* otok = out_tokens + int64_t(b) * (N + 1);
-  float* lse = row_lse + int64_t(b) * R;
-  int* amax = row_argmax + int64_t(b) * R;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int* tok = P.tokens + int64_t(b) * N;
+  int* otok = P.out_tokens + int64_t(b) * (N + 1);
+  float* lse = P.row_lse + int64_t(b) * R;
+  int* amax = P.row_argmax + int64_t(b) * R;
+  uint64_t* seqw = P.seq_words + int64_t(b) * 2;
 
-  const float t = temperature[b];
+  const float t = P.temperature[b];
   bool bad = !temperature_valid(t);
-  for (int i = lane; i < N; i += kDecideThreads) {
+  for (int i = tid; i < N; i += kThreads) {
     const int d = tok[i];
-    bad = bad || d < 0 || d >= vocab;
+    bad = bad || d < 0 || d >= P.vocab;
   }
-  if (__ballot(bad) != 0) {
-    for (int i = lane; i <= N; i += kDecideThreads) otok[i] = -1;
-    for (int r = lane; r < R; r += kDecideThreads) {
+  if (__syncthreads_or(bad)) {
+    for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
+    for (int r = tid; r < R; r += kThreads) {
       lse[r] = NAN;
       amax[r] = -1;
     }
-    if (lane == 0) {
-      out_n[b] = -1;
-      seq[b].mode = kModeNone;
+    if (tid == 0) {
+      P.out_n[b] = -1;
+      SeqInfo s{kModeNone, 0, 0.0f, 0.0f};
+      publish_seq(seqw, s, P.epoch);
     }
     return;
   }
 
   const bool greedy = (t == 0.0f);
+  const int r_first = greedy ? N : 0;
+  ensure_stats<T>(P, sh, b, r_first, R);
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
-  for (int r = lane; r < R; r += kDecideThreads) {
-    if (greedy && r < N) {
-      lse[r] = NAN;
-      amax[r] = -1;
+
+  // Merge each row's chunk partials: lanes take chunks lane, lane+64, ...,
+  // then a butterfly; waves take rows wave, wave+4, ...
+  for (int r = wave; r < R; r += kWaves) {
+    if (r < r_first) {
+      if (lane == 0) {
+        lse[r] = NAN;
+        amax[r] = -1;
+      }
       continue;
     }
-    const RowPartial* rp = partials + (int64_t(b) * R + r) * nch;
-    float m = rp[0].m, s = rp[0].s;
-    int idx = rp[0].idx;
-    for (int k = 1; k < nch; ++k) {
+    uint64_t* rw = P.stat_words + (int64_t(b) * R + r) * P.nch * 2;
+    float m = -INFINITY, s = 0.0f;
+    int idx = INT_MAX;
+    for (int k = lane; k < P.nch; k += 64) {
+      float m2, s2;
+      int i2;
+      unpack_partial(fetch(rw + 2 * k), fetch(rw + 2 * k + 1), m2, s2, i2);
       if (greedy)
-        acc_merge<false>(m, s, idx, rp[k].m, rp[k].s, rp[k].idx, c);
+        acc_merge<false>(m, s, idx, m2, s2, i2, c);
       else
-        acc_merge<true>(m, s, idx, rp[k].m, rp[k].s, rp[k].idx, c);
+        acc_merge<true>(m, s, idx, m2, s2, i2, c);
     }
-    if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
-    const double logs = greedy ? 0.0 : log(double(s));
-    sm_m[r] = m;
-    sm_logs[r] = logs;
-    sm_idx[r] = idx;
-    lse[r] = greedy ? NAN : float(double(m) * inv_t + logs);
-    amax[r] = idx;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const float s2 = __shfl_xor(s, off);
+      const int i2 = __shfl_xor(idx, off);
+      if (greedy)
+        acc_merge<false>(m, s, idx, m2, s2, i2, c);
+      else
+        acc_merge<true>(m, s, idx, m2, s2, i2, c);
+    }
+    if (lane == 0) {
+      if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
+      // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c) exactly.
+      const double logz = greedy ? 0.0 : kLn2 * (log2(double(s)) - double(fmaf(m, c, -scaled_max(m, c))));
+      sh.row_m[r] = m;
+      sh.row_logz[r] = logz;
+      sh.row_idx[r] = idx;
+      lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
+      amax[r] = idx;
+    }
   }
   __syncthreads();
 
-  // Lane i < N makes decision i.
-  bool accept = true;
-  if (lane < N) {
-    const int d = tok[lane];
-    if (greedy) {
-      accept = (d == sm_idx[N + lane]);
-    } else {
-      const float zt = Logit<T>::at(target, (int64_t(b) * (N + 1) + lane) * vocab + d);
-      const float zd = Logit<T>::at(draft, (int64_t(b) * N + lane) * vocab + d);
-      if (zd == -INFINITY) {
-        accept = true;  // p(d) == 0: the ratio is infinite
+  if (wave == 0) {
+    bool accept = true;
+    if (lane < N) {
+      const int d = tok[lane];
+      if (greedy) {
+        accept = (d == sh.row_idx[N + lane]);
       } else {
-        const double log_q = (double(zt) - double(sm_m[N + lane])) * inv_t - sm_logs[N + lane];
-        const double log_p = (double(zd) - double(sm_m[lane])) * inv_t - sm_logs[lane];
-        accept = double(accept_u[int64_t(b) * N + lane]) < exp(log_q - log_p);
+        const float zt = Logit<T>::at(static_cast<const T*>(P.target), (int64_t(b) * (N + 1) + lane) * P.vocab + d);
+        const float zd = Logit<T>::at(static_cast<const T*>(P.draft), (int64_t(b) * N + lane) * P.vocab + d);
+        if (zd == -INFINITY) {
+          accept = true;  // p(d) == 0: the ratio is infinite
+        } else {
+          const double log_q = (double(zt) - double(sh.row_m[N + lane])) * inv_t - sh.row_logz[N + lane];
+          const double log_p = (double(zd) - double(sh.row_m[lane])) * inv_t - sh.row_logz[lane];
+          accept = double(P.accept_u[int64_t(b) * N + lane]) < exp(log_q - log_p);
+        }
       }
     }
+    const unsigned long long rej = __ballot(lane < N && !accept);
+    const int j = rej ? (__ffsll(rej) - 1) : N;
+    // Position j of a sampled sequence is left to DRAW2: a duplicate DECIDE
+    // running after it must not overwrite the drawn token.
+    for (int i = lane; i <= N; i += 64) {
+      if (i < j)
+        otok[i] = tok[i];
+      else if (i > j)
+        otok[i] = -1;
+      else if (greedy)
+        otok[i] = sh.row_idx[N + j];
+    }
+    if (lane == 0) {
+      P.out_n[b] = j;
+      SeqInfo s;
+      s.mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
+      s.j = j;
+      s.m_target = sh.row_m[N + j];
+      s.m_draft = (j < N && !greedy) ? sh.row_m[j] : 0.0f;
+      publish_seq(seqw, s, P.epoch);
+    }
   }
-  const unsigned long long rej = __ballot(lane < N && !accept);
-  const int j = rej ? (__ffsll(rej) - 1) : N;
-  for (int i = lane; i <= N; i += kDecideThreads) {
-    int v = -1;
-    if (i < j)
-      v = tok[i];
-    else if (i == j && greedy)
-      v = sm_idx[N + j];
-    otok[i] = v;
-  }
-  if (lane == 0) {
-    out_n[b] = j;
-    SeqState st;
-    st.mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
-    st.j = j;
-    st.m_target = sm_m[N + j];
-    st.m_draft = (j < N) ? sm_m[j] : 0.0f;
-    st.inv_t = inv_t;
-    seq[b] = st;
-  }
+  __syncthreads();
+}
+
+template <typename T>
+__device__ SeqInfo ensure_decided(const Params P, Shared& sh, int b) {
+  uint64_t* w = P.seq_words + int64_t(b) * 2;
+  if (!block_wait(w, 2, P)) decide_item<T>(P, sh, b);
+  return unpack_seq(fetch(w), fetch(w + 1));
 }
 
 // ---------------------------------------------------------------------------
-// Residual / bonus draw, fp64.
-
-__device__ __forceinline__ double block_sum(double v) {
-  __shared__ double sm[kWaves];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm[wave] = v;
-  __syncthreads();
-  double total = sm[0];
-  for (int w = 1; w < kWaves; ++w) total += sm[w];
-  return total;
-}
+// Draw: fp64 weights, chunk sums, inverse CDF.
 
 template <typename T>
-struct DrawRow {
+struct DrawRows {
   const T* trow;
   const T* drow;
   double mt, md, inv_t;
-  double rt, rd;  // 1 / normalisers (residual only)
   bool residual;
-
-  // Weight of token e: (q - p)_+ after a rejection, exp((z - m)/T) of the
-  // target row otherwise (the bonus, self-normalised by its own sum).
-  __device__ __forceinline__ double weight(int e) const {
-    const double et = exp((double(Logit<T>::at(trow, e)) - mt) * inv_t);
-    if (!residual) return et;
-    const double ed = exp((double(Logit<T>::at(drow, e)) - md) * inv_t);
-    return fmax(0.0, et * rt - ed * rd);
-  }
 };
 
 template <typename T>
-__device__ __forceinline__ DrawRow<T> make_draw_row(const T* draft, const T* target, int b, int N, int vocab,
-                                                    const SeqState& st, const double2* norm, int nsch) {
-  DrawRow<T> p;
-  p.trow = target + (int64_t(b) * (N + 1) + st.j) * vocab;
-  p.drow = (st.j < N) ? draft + (int64_t(b) * N + st.j) * vocab : nullptr;
-  p.mt = st.m_target;
-  p.md = st.m_draft;
-  p.inv_t = st.inv_t;
-  p.residual = (st.mode == kModeResidual);
-  p.rt = p.rd = 0.0;
-  if (p.residual) {
-    double zt = 0.0, zd = 0.0;
-    for (int c = 0; c < nsch; ++c) {
-      zt += norm[c].x;
-      zd += norm[c].y;
-    }
-    p.rt = 1.0 / zt;
-    p.rd = 1.0 / zd;
-  }
-  return p;
+__device__ __forceinline__ DrawRows<T> draw_rows(const Params P, int b, const SeqInfo& s) {
+  const int N = P.n_draft;
+  DrawRows<T> d;
+  d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
+  d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
+  d.mt = s.m_target;
+  d.md = s.m_draft;
+  d.inv_t = 1.0 / double(P.temperature[b]);
+  d.residual = (s.mode == kModeResidual);
+  return d;
 }
 
+// exp((z - max)/T) of token e of the target (and draft) row; 0 past the row end.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_norm_kernel(const T* __restrict__ draft,
-                                                              const T* __restrict__ target, int n_draft,
-                                                              int vocab, int nsch, const SeqState* __restrict__ seq,
-                                                              double2* __restrict__ norm_part) {
-  const int b = blockIdx.x / nsch;
-  const int c = blockIdx.x - b * nsch;
-  const SeqState st = seq[b];
-  if (st.mode != kModeResidual) return;
-  const T* trow = target + (int64_t(b) * (n_draft + 1) + st.j) * vocab;
-  const T* drow = draft + (int64_t(b) * n_draft + st.j) * vocab;
-  const int e0 = c * kSampChunk;
-  const int e1 = min(vocab, e0 + kSampChunk);
-  const double mt = st.m_target, md = st.m_draft;
-  double zt = 0.0, zd = 0.0;
-  for (int e = e0 + threadIdx.x; e < e1; e += kThreads) {
-    zt += exp((double(Logit<T>::at(trow, e)) - mt) * st.inv_t);
-    zd += exp((double(Logit<T>::at(drow, e)) - md) * st.inv_t);
+__device__ __forceinline__ void draw_exps(const DrawRows<T>& d, int e, int vocab, const double* tbl, double& et,
+                                          double& ed) {
+  et = 0.0;
+  ed = 0.0;
+  if (e < vocab) {
+    et = exp_nonpos((double(Logit<T>::at(d.trow, e)) - d.mt) * d.inv_t, tbl);
+    if (d.residual) ed = exp_nonpos((double(Logit<T>::at(d.drow, e)) - d.md) * d.inv_t, tbl);
   }
-  zt = block_sum(zt);
-  zd = block_sum(zd);
-  if (threadIdx.x == 0) norm_part[int64_t(b) * nsch + c] = make_double2(zt, zd);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void weights_kernel(const T* __restrict__ draft, const T* __restrict__ target,
-                                                           int n_draft, int vocab, int nsch,
-                                                           const SeqState* __restrict__ seq,
-                                                           const double2* __restrict__ norm_part,
-                                                           double* __restrict__ wsum_part) {
-  const int b = blockIdx.x / nsch;
-  const int c = blockIdx.x - b * nsch;
-  const SeqState st = seq[b];
-  if (st.mode == kModeNone) return;
-  const DrawRow<T> p = make_draw_row(draft, target, b, n_draft, vocab, st, norm_part + int64_t(b) * nsch, nsch);
-  const int e0 = c * kSampChunk;
-  const int e1 = min(vocab, e0 + kSampChunk);
-  double w = 0.0;
-  for (int e = e0 + threadIdx.x; e < e1; e += kThreads) w += p.weight(e);
-  w = block_sum(w);
-  if (threadIdx.x == 0) wsum_part[int64_t(b) * nsch + c] = w;
+// Weight of a token given its exps: (q - p)_+ after a rejection, else the
+// self-normalised target exp (the bonus).
+__device__ __forceinline__ double draw_weight(bool residual, double et, double ed, double rt, double rd) {
+  return residual ? fmax(0.0, et * rt - ed * rd) : et;
 }
 
+// Per-chunk fp64 sums of exp((z - m)/T) over target and draft row j.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void draw_kernel(const T* __restrict__ draft, const T* __restrict__ target,
-                                                        const float* __restrict__ sample_u, int n_draft, int vocab,
-                                                        int nsch, const SeqState* __restrict__ seq,
-                                                        const double2* __restrict__ norm_part,
-                                                        double* __restrict__ wsum_part, int* __restrict__ out_tokens) {
-  constexpr int kPer = kSampChunk / kThreads;  // consecutive weights per thread in the scan
-  __shared__ double w_lds[kSampChunk];
-  __shared__ double wave_tot[kWaves];
-  __shared__ double sh_before, sh_target;
-  __shared__ int sh_chunk, sh_first, sh_last;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const SeqState st = seq[b];
-  if (st.mode == kModeNone) return;
-  DrawRow<T> p = make_draw_row(draft, target, b, n_draft, vocab, st, norm_part + int64_t(b) * nsch, nsch);
-  double* wsum = wsum_part + int64_t(b) * nsch;
-  const double u = double(sample_u[b]);
-
-  // A residual whose weights all rounded to zero falls back to q_j itself.
-  if (p.residual) {
-    double S = 0.0;
-    for (int c = 0; c < nsch; ++c) S += wsum[c];
-    if (!(S > 0.0)) {
-      p.residual = false;
-      for (int c = 0; c < nsch; ++c) {
-        const int e1 = min(vocab, (c + 1) * kSampChunk);
-        double w = 0.0;
-        for (int e = c * kSampChunk + tid; e < e1; e += kThreads) w += p.weight(e);
-        w = block_sum(w);
-        __syncthreads();
-        if (tid == 0) wsum[c] = w;
-      }
-      __syncthreads();
-    }
-  }
-
-  if (tid == 0) {
-    double S = 0.0;
-    for (int c = 0; c < nsch; ++c) S += wsum[c];
-    const double target_mass = u * S;
-    double before = 0.0;
-    int chunk = -1;
-    for (int c = 0; c < nsch; ++c) {
-      const double next = before + wsum[c];
-      if (next > target_mass) {
-        chunk = c;
-        break;
-      }
-      before = next;
-    }
-    if (chunk < 0) {  // rounding left u*S at or past the total: last chunk with weight
-      chunk = nsch - 1;
-      while (chunk > 0 && !(wsum[chunk] > 0.0)) --chunk;
-      before = 0.0;
-      for (int c = 0; c < chunk; ++c) before += wsum[c];
-    }
-    sh_chunk = chunk;
-    sh_before = before;
-    sh_target = target_mass;
-    sh_first = INT_MAX;
-    sh_last = -1;
-  }
-  __syncthreads();
-  const int chunk = sh_chunk;
-  const int e0 = chunk * kSampChunk;
-  for (int i = tid; i < kSampChunk; i += kThreads) {
-    const int e = e0 + i;
-    w_lds[i] = (e < vocab) ? p.weight(e) : 0.0;
-  }
-  __syncthreads();
-
-  // Inclusive scan: each thread owns kPer consecutive weights.
-  double local[kPer];
-  double run = 0.0;
+__device__ void norm_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d) {
+  double st = 0.0, sd = 0.0;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    run += w_lds[tid * kPer + k];
-    local[k] = run;
+  for (int k = 0; k < kSampPer; ++k) {
+    double et, ed;
+    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
+    st += et;
+    sd += ed;
   }
-  // Exclusive scan of the per-thread totals across the block.
-  double incl = run;
-  const int lane = tid & 63;
+  st = block_sum(st, sh);
+  sd = block_sum(sd, sh);
+  if (threadIdx.x == 0) {
+    uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * 4;
+    publish_f64(w, st, P.epoch);
+    publish_f64(w + 2, sd, P.epoch);
+  }
+}
+
+// Reciprocal normalisers 1/Z of target and draft row j, waiting for (or
+// computing) every chunk's fp64 sums. Fixed summation order.
+template <typename T>
+__device__ void normalisers(const Params P, Shared& sh, int b, const DrawRows<T>& d, double& rt, double& rd) {
+  uint64_t* base = P.norm_words + int64_t(b) * P.nsch * 4;
+  if (!block_wait(base, P.nsch * 4, P)) {
+    for (int c = 0; c < P.nsch; ++c)
+      if (!block_has(base + 4 * c, 4, P, sh)) norm_item<T>(P, sh, b, c, d);
+    __syncthreads();
+  }
+  double zt = 0.0, zd = 0.0;
+  for (int c = threadIdx.x; c < P.nsch; c += kThreads) {
+    zt += unpack_f64(fetch(base + 4 * c), fetch(base + 4 * c + 1));
+    zd += unpack_f64(fetch(base + 4 * c + 2), fetch(base + 4 * c + 3));
+  }
+  zt = block_sum(zt, sh);
+  zd = block_sum(zd, sh);
+  rt = 1.0 / zt;
+  rd = 1.0 / zd;
+}
+
+// Weight sum of one chunk from scratch (used when a DRAW1 result is missing).
+template <typename T>
+__device__ void wsum_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d, double rt, double rd) {
+  double w = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampPer; ++k) {
+    double et, ed;
+    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
+    w += draw_weight(d.residual, et, ed, rt, rd);
+  }
+  w = block_sum(w, sh);
+  if (threadIdx.x == 0) publish_f64(P.wsum_words + (int64_t(b) * P.nsch + c) * 2, w, P.epoch);
+}
+
+// DRAW1(b, c): exps held in registers across both reductions.
+template <typename T>
+__device__ void draw1_item(const Params P, Shared& sh, int b, int c) {
+  const SeqInfo s = ensure_decided<T>(P, sh, b);
+  if (s.mode == kModeNone) return;
+  const DrawRows<T> d = draw_rows<T>(P, b, s);
+  double et[kSampPer], ed[kSampPer];
+  double st = 0.0, sd = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampPer; ++k) {
+    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et[k], ed[k]);
+    st += et[k];
+    sd += ed[k];
+  }
+  double rt = 0.0, rd = 0.0;
+  if (d.residual) {
+    st = block_sum(st, sh);
+    sd = block_sum(sd, sh);
+    if (threadIdx.x == 0) {
+      uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * 4;
+      publish_f64(w, st, P.epoch);
+      publish_f64(w + 2, sd, P.epoch);
+    }
+    normalisers<T>(P, sh, b, d, rt, rd);
+  }
+  double w = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampPer; ++k) w += draw_weight(d.residual, et[k], ed[k], rt, rd);
+  w = block_sum(w, sh);
+  if (threadIdx.x == 0) publish_f64(P.wsum_words + (int64_t(b) * P.nsch + c) * 2, w, P.epoch);
+}
+
+// Block-wide inclusive scan of one double per thread (fixed order); returns
+// the thread's inclusive prefix and sets total.
+__device__ __forceinline__ double block_scan(double v, double& total, Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  double incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double up = __shfl_up(incl, off);
     if (lane >= off) incl += up;
   }
-  const int wave = tid >> 6;
-  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  double base = sh_before;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  base += incl - run;
-  const double target_mass = sh_target;
+  if (lane == 63) sh.red[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  double before = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < (int(threadIdx.x) >> 6)) before += sh.red[w];
+    total += sh.red[w];
+  }
+  return before + incl;
+}
+
+// Sum over one chunk of q_j = exp((z - m)/T) / Z (the fallback draw's weights).
+template <typename T>
+__device__ double q_chunk_sum(const Params P, Shared& sh, int c, const DrawRows<T>& d, double inv_z) {
+  double w = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampPer; ++k) {
+    double et, ed;
+    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
+    w += et * inv_z;
+  }
+  return block_sum(w, sh);
+}
+
+// DRAW2(b): chunk crossing, then an fp64 scan of that chunk.
+template <typename T>
+__device__ void draw2_item(const Params P, Shared& sh, int b) {
+  const SeqInfo s = ensure_decided<T>(P, sh, b);
+  if (s.mode == kModeNone) return;
+  DrawRows<T> d = draw_rows<T>(P, b, s);
+  const int tid = threadIdx.x;
+  double rt = 0.0, rd = 0.0;
+  if (d.residual) normalisers<T>(P, sh, b, d, rt, rd);
+  uint64_t* ws = P.wsum_words + int64_t(b) * P.nsch * 2;
+  if (!block_wait(ws, P.nsch * 2, P)) {
+    for (int c = 0; c < P.nsch; ++c)
+      if (!block_has(ws + 2 * c, 2, P, sh)) wsum_item<T>(P, sh, b, c, d, rt, rd);
+    __syncthreads();
+  }
+  // Total S as a scan over chunk sums in groups of 256 chunks.
+  double S = 0.0;
+  for (int g = 0; g < P.nsch; g += kThreads) {
+    const int c = g + tid;
+    const double w = (c < P.nsch) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
+    double tot;
+    block_scan(w, tot, sh);
+    S += tot;
+  }
+  const double u = double(P.sample_u[b]);
+  double target_mass, before = 0.0;
+  int chunk = -1;
+  bool fallback = false;
+  if (d.residual && !(S > 0.0)) {
+    // Every residual weight rounded to zero: draw from q_j itself. Chunk sums
+    // are recomputed here (twice, in the same order) and kept local.
+    fallback = true;
+    S = 0.0;
+    for (int c = 0; c < P.nsch; ++c) S += q_chunk_sum<T>(P, sh, c, d, rt);
+    target_mass = u * S;
+    int last_pos = 0;
+    for (int c = 0; c < P.nsch; ++c) {
+      const double w = q_chunk_sum<T>(P, sh, c, d, rt);
+      if (w > 0.0) last_pos = c;
+      if (before + w > target_mass) {
+        chunk = c;
+        break;
+      }
+      before += w;
+    }
+    if (chunk < 0) {
+      chunk = last_pos;
+      before = 0.0;
+      for (int c = 0; c < chunk; ++c) before += q_chunk_sum<T>(P, sh, c, d, rt);
+    }
+  } else {
+    target_mass = u * S;
+    // First chunk whose inclusive prefix exceeds target_mass.
+    int last_pos = -1;
+    for (int g = 0; g < P.nsch && chunk < 0; g += kThreads) {
+      const int c = g + tid;
+      const double w = (c < P.nsch) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
+      double tot;
+      const double incl = before + block_scan(w, tot, sh);
+      if (tid == 0) {
+        sh.pick[0] = INT_MAX;
+        sh.pick[1] = -1;
+      }
+      __syncthreads();
+      if (c < P.nsch && incl > target_mass && w > 0.0) atomicMin(&sh.pick[0], c);
+      if (c < P.nsch && w > 0.0) atomicMax(&sh.pick[1], c);
+      __syncthreads();
+      if (sh.pick[1] >= 0) last_pos = sh.pick[1];
+      if (sh.pick[0] != INT_MAX) chunk = sh.pick[0];
+      before += tot;
+      __syncthreads();
+    }
+    if (chunk < 0) chunk = max(last_pos, 0);  // rounding left u*S at or past the total
+    // Exclusive prefix of the chosen chunk, in the same group-scan order.
+    before = 0.0;
+    for (int g = 0; g < chunk; g += kThreads) {
+      const int c = g + tid;
+      const double w = (c < chunk) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
+      double tot;
+      block_scan(w, tot, sh);
+      before += tot;
+    }
+  }
+  // Scan the chunk: thread t owns kSampPer consecutive tokens.
+  const int e_base = chunk * kSampChunk + tid * kSampPer;
+  double w[kSampPer];
+  double run = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampPer; ++k) {
+    double et, ed;
+    draw_exps(d, e_base + k, P.vocab, sh.exp_table, et, ed);
+    w[k] = fallback ? et * rt : draw_weight(d.residual, et, ed, rt, rd);
+    run += w[k];
+  }
+  double tot;
+  const double incl = block_scan(run, tot, sh);
+  double cum = before + (incl - run);
+  if (tid == 0) {
+    sh.pick[0] = INT_MAX;
+    sh.pick[1] = -1;
+  }
+  __syncthreads();
   int first = INT_MAX, last = -1;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = tid * kPer + k;
-    if (first == INT_MAX && base + local[k] > target_mass) first = i;
-    if (w_lds[i] > 0.0) last = i;
+  for (int k = 0; k < kSampPer; ++k) {
+    cum += w[k];
+    if (first == INT_MAX && cum > target_mass && w[k] > 0.0) first = k;
+    if (w[k] > 0.0) last = k;
   }
-  if (first != INT_MAX) atomicMin(&sh_first, first);
-  if (last >= 0) atomicMax(&sh_last, last);
+  if (first != INT_MAX) atomicMin(&sh.pick[0], e_base + first);
+  if (last >= 0) atomicMax(&sh.pick[1], e_base + last);
   __syncthreads();
   if (tid == 0) {
-    const int k = (sh_first != INT_MAX) ? sh_first : sh_last;
-    out_tokens[int64_t(b) * (n_draft + 1) + st.j] = e0 + k;
+    const int token = (sh.pick[0] != INT_MAX) ? sh.pick[0] : sh.pick[1];
+    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = token;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// The persistent kernel.
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 4) void verify_kernel(Params P) {
+  __shared__ Shared sh;
+  if (threadIdx.x < kExpTableSize) sh.exp_table[threadIdx.x] = P.exp_table[threadIdx.x];
+  __syncthreads();
+  const int R = 2 * P.n_draft + 1;
+  const int n_stat = R * P.nch;
+  for (long long s = blockIdx.x; s < P.total_slots; s += gridDim.x) {
+    const int g = int(s / P.spg);
+    const int o = int(s - (long long)g * P.spg);
+    if (o < n_stat) {
+      if (g < P.batch) stat_item<T>(P, sh, g, o / P.nch, o % P.nch);
+    } else if (o == n_stat) {
+      const int b = g - P.lag_decide;
+      if (b >= 0 && b < P.batch) decide_item<T>(P, sh, b);
+    } else if (o < n_stat + 1 + P.nsch) {
+      const int b = g - P.lag_draw1;
+      if (b >= 0 && b < P.batch) draw1_item<T>(P, sh, b, o - n_stat - 1);
+    } else {
+      const int b = g - P.lag_draw2;
+      if (b >= 0 && b < P.batch) draw2_item<T>(P, sh, b);
+    }
   }
 }
 
-const char* const kStageNames[] = {"row_stats", "decide", "resid_norm", "weights", "draw"};
-constexpr int kNumStages = 5;
+__global__ void clear_words_kernel(uint64_t* p, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+const char* const kStageNames[] = {"verify"};
+constexpr int kNumStages = 1;
 
 template <typename T>
-hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* ev) {
-  const T* draft = static_cast<const T*>(a.draft);
-  const T* target = static_cast<const T*>(a.target);
+hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, const LaunchConfig& cfg, hipStream_t stream,
+                        hipEvent_t* ev) {
+  Params P;
+  P.draft = a.draft;
+  P.target = a.target;
+  P.tokens = a.tokens;
+  P.accept_u = a.accept_u;
+  P.sample_u = a.sample_u;
+  P.temperature = a.temperature;
+  P.out_tokens = a.out_tokens;
+  P.out_n = a.out_n;
+  P.row_lse = w.row_lse;
+  P.row_argmax = w.row_argmax;
+  P.stat_words = w.stat_words;
+  P.seq_words = w.seq_words;
+  P.norm_words = w.norm_words;
+  P.wsum_words = w.wsum_words;
+  P.exp_table = w.exp_table;
+  P.batch = a.batch;
+  P.n_draft = a.n_draft;
+  P.vocab = a.vocab;
+  P.nch = w.n_stats_chunks;
+  P.nsch = w.n_samp_chunks;
   const int R = 2 * a.n_draft + 1;
-  const int nch = w.n_stats_chunks;
-  const int nsch = w.n_samp_chunks;
-  const int64_t stat_items = int64_t(a.batch) * R * nch;
-  const unsigned samp_items = unsigned(int64_t(a.batch) * nsch);
-  int stage = 0;
-  auto mark = [&]() {
-    if (ev != nullptr) (void)hipEventRecord(ev[stage], stream);
-    ++stage;
-  };
-  mark();
-  hipLaunchKernelGGL(row_stats_kernel<T>, dim3(unsigned(stat_items)), dim3(kThreads), 0, stream, draft, target,
-                     a.temperature, a.n_draft, a.vocab, nch, w.partials);
-  mark();
-  hipLaunchKernelGGL(decide_kernel<T>, dim3(a.batch), dim3(kDecideThreads), 0, stream, draft, target, a.tokens,
-                     a.accept_u, a.temperature, a.n_draft, a.vocab, nch, w.partials, w.row_lse, w.row_argmax, w.seq,
-                     a.out_tokens, a.out_n);
-  mark();
-  hipLaunchKernelGGL(resid_norm_kernel<T>, dim3(samp_items), dim3(kThreads), 0, stream, draft, target, a.n_draft,
-                     a.vocab, nsch, w.seq, w.norm_part);
-  mark();
-  hipLaunchKernelGGL(weights_kernel<T>, dim3(samp_items), dim3(kThreads), 0, stream, draft, target, a.n_draft,
-                     a.vocab, nsch, w.seq, w.norm_part, w.wsum_part);
-  mark();
-  hipLaunchKernelGGL(draw_kernel<T>, dim3(a.batch), dim3(kThreads), 0, stream, draft, target, a.sample_u,
-                     a.n_draft, a.vocab, nsch, w.seq, w.norm_part, w.wsum_part, a.out_tokens);
-  if (ev != nullptr) (void)hipEventRecord(ev[stage], stream);
+  P.spg = R * P.nch + 1 + P.nsch + 1;
+  P.lag_decide = cfg.lag_decide;
+  P.lag_draw1 = cfg.lag_draw1;
+  P.lag_draw2 = cfg.lag_draw2;
+  P.total_slots = (long long)(a.batch + cfg.lag_draw2) * P.spg;
+  P.epoch = cfg.epoch;
+  P.timeout_ticks = cfg.timeout_ticks;
+  // A grid size sharing a factor with the group size would give every
+  // workgroup the same item types (e.g. only DRAW2 items); keep them coprime.
+  long long grid = std::min<long long>(P.total_slots, cfg.max_blocks);
+  while (grid > 1 && std::gcd(grid, (long long)P.spg) != 1) --grid;
+  if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
+  hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, P);
+  if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
   return hipGetLastError();
 }
 
@@ -618,11 +930,25 @@ const char* stage_name(int stage) {
   return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
 }
 
-hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* events,
-                         int* n_stages) {
+int max_blocks_per_cu(int dtype) {
+  int occ = 0;
+  if (dtype == 0)
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, verify_kernel<float>, kThreads, 0);
+  else
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, verify_kernel<uint16_t>, kThreads, 0);
+  return occ;
+}
+
+hipError_t clear_words(uint64_t* p, long long n, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, const LaunchConfig& cfg, hipStream_t stream,
+                         hipEvent_t* events, int* n_stages) {
   if (n_stages != nullptr) *n_stages = kNumStages;
-  if (a.dtype == 0) return launch_typed<float>(a, w, stream, events);
-  return launch_typed<uint16_t>(a, w, stream, events);
+  if (a.dtype == 0) return launch_typed<float>(a, w, cfg, stream, events);
+  return launch_typed<uint16_t>(a, w, cfg, stream, events);
 }
 
 }  // namespace specv

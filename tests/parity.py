@@ -146,7 +146,8 @@ def check_row_stats(batch: synth.Batch, gpu: GpuResult, seqs=None):
         t64 = synth.widen(batch.target_logits[s], batch.dtype)
         rows = np.concatenate([d64, t64], axis=0)
         toks = batch.draft_tokens[s]
-        if not (np.isfinite(T) and T >= 0) or np.any((toks < 0) | (toks >= batch.vocab)):
+        t_ok = np.isfinite(T) and (T == 0.0 or T >= oracle.specv_oracle.MIN_TEMPERATURE)
+        if not t_ok or np.any((toks < 0) | (toks >= batch.vocab)):
             assert np.all(gpu.argmax[s] == -1) and np.all(np.isnan(gpu.lse[s]))
             continue
         read = np.arange(2 * N + 1) >= (N if T == 0.0 else 0)

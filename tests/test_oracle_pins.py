@@ -353,9 +353,10 @@ def test_invalid_inputs_give_sentinel():
     draft = np.zeros((2, 4))
     target = np.zeros((3, 4))
     for T, toks in ((float("nan"), [0, 1]), (-1.0, [0, 1]), (float("inf"), [0, 1]), (1.0, [0, 4]),
-                    (1.0, [-1, 0]), (0.0, [7, 0])):
+                    (1.0, [-1, 0]), (0.0, [7, 0]), (1e-30, [0, 1]), (2.0 ** -61, [0, 1])):
         r = oracle.verify_sequence(draft, target, toks, [0.5, 0.5], 0.5, T)
         assert r.n_accepted == -1 and r.tokens == [-1, -1, -1]
+    assert oracle.verify_sequence(draft, target, [0, 1], [0.5, 0.5], 0.5, 2.0 ** -60).n_accepted >= 0
 
 
 # ------------------------------------------------------ planted mistakes
