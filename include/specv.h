@@ -69,6 +69,9 @@ enum specv_status {
 /* Largest n_draft a handle accepts (one 64-lane wavefront holds a sequence's decisions). */
 #define SPECV_MAX_DRAFT 64
 
+/* Largest vocabulary a handle accepts (2^22 tokens). */
+#define SPECV_MAX_VOCAB 4194304
+
 /*
  * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,
  * vocabulary size `vocab` (V >= 1) and logits stored as `dtype`, on HIP device
@@ -76,7 +79,7 @@ enum specv_status {
  * max_batch * (2*max_draft+1) * ceil(V/8192)). On success *out is set and
  * SPECV_OK returned; on failure *out is NULL.
  * Errors: SPECV_EINVAL (out NULL, max_batch < 1, max_draft outside
- * [1, SPECV_MAX_DRAFT], vocab < 1 or > 2^30, unknown dtype, bad device),
+ * [1, SPECV_MAX_DRAFT], vocab < 1 or > SPECV_MAX_VOCAB, unknown dtype, bad device),
  * SPECV_ENOMEM, SPECV_EHIP.
  */
 SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int dtype, int device);
@@ -94,10 +97,12 @@ SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int 
  *                                          token at index j, then -1
  *   out_n_accepted  [batch]                int32, written: j in [0, n_draft]
  * Logits must be finite or -inf (a masked token), with at least one finite
- * logit per row. Work is enqueued on `stream` and the call returns without
+ * logit per row, and |logit| <= 2^64. Temperatures are 0 (greedy) or finite
+ * and >= 2^-60. Work is enqueued on `stream` and the call returns without
  * waiting; outputs are valid once the stream reaches this point.
  * Per-sequence input faults that only the device can see — a draft token
- * outside [0, V), a temperature that is negative, NaN or infinite — make that
+ * outside [0, V), a temperature that is negative, NaN, infinite or positive
+ * below 2^-60 — make that
  * sequence's out_n_accepted = -1 and all its out_tokens = -1; other sequences
  * are unaffected.
  * batch == 0 is a no-op returning SPECV_OK.

@@ -66,8 +66,9 @@ long env_long(const char* name, long fallback) {
 }
 
 // Grid cap, item lags and wait timeout. Defaults suit MI355X; the environment
-// variables SPECV_BLOCKS_PER_CU, SPECV_LAG_DECIDE, SPECV_LAG_DRAW1,
-// SPECV_LAG_DRAW2 and SPECV_WAIT_TIMEOUT_US override them (tuning and tests).
+// variables SPECV_BLOCKS_PER_CU, SPECV_LAG_DECIDE, SPECV_LAG_NORM,
+// SPECV_LAG_DRAW (each at most 64) and SPECV_WAIT_TIMEOUT_US override them
+// (tuning and tests).
 bool init_config(specv_ctx* h) {
   int cus = 0, clock_khz = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) return false;
@@ -76,9 +77,9 @@ bool init_config(specv_ctx* h) {
   if (occ < 1) return false;
   const long per_cu = std::max(1L, std::min<long>(occ, env_long("SPECV_BLOCKS_PER_CU", 3)));
   h->config.max_blocks = static_cast<long long>(per_cu) * cus;
-  h->config.lag_decide = static_cast<int>(std::max(0L, env_long("SPECV_LAG_DECIDE", 4)));
-  h->config.lag_draw1 = static_cast<int>(std::max<long>(h->config.lag_decide, env_long("SPECV_LAG_DRAW1", 8)));
-  h->config.lag_draw2 = static_cast<int>(std::max<long>(h->config.lag_draw1, env_long("SPECV_LAG_DRAW2", 12)));
+  h->config.lag_decide = static_cast<int>(std::min(64L, std::max(0L, env_long("SPECV_LAG_DECIDE", 4))));
+  h->config.lag_norm = static_cast<int>(std::min(64L, std::max<long>(h->config.lag_decide, env_long("SPECV_LAG_NORM", 8))));
+  h->config.lag_draw = static_cast<int>(std::min(64L, std::max<long>(h->config.lag_norm, env_long("SPECV_LAG_DRAW", 12))));
   const long timeout_us = std::max(0L, env_long("SPECV_WAIT_TIMEOUT_US", 200));
   h->config.timeout_ticks = static_cast<unsigned long long>(timeout_us) * static_cast<unsigned long long>(clock_khz) / 1000ULL;
   h->config.epoch = 0;
@@ -105,7 +106,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   if (out == nullptr) return SPECV_EINVAL;
   *out = nullptr;
   if (max_batch < 1 || max_draft < 1 || max_draft > SPECV_MAX_DRAFT) return SPECV_EINVAL;
-  if (vocab < 1 || vocab > (1 << 30)) return SPECV_EINVAL;
+  if (vocab < 1 || vocab > specv::kMaxVocab) return SPECV_EINVAL;
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
@@ -115,10 +116,9 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const int nsch = specv::ceil_div(vocab, specv::kSampChunk);
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
   const size_t n_stat = rows * size_t(nch) * 2;
-  const size_t n_seq = size_t(max_batch) * 2;
-  const size_t n_norm = size_t(max_batch) * size_t(nsch) * 4;
-  const size_t n_wsum = size_t(max_batch) * size_t(nsch) * 2;
-  const size_t n_words = n_stat + n_seq + n_norm + n_wsum;
+  const size_t n_seq = size_t(max_batch) * specv::seq_words_per_sequence();
+  const size_t n_norm = size_t(max_batch) * size_t(nsch) * specv::norm_words_per_chunk();
+  const size_t n_words = n_stat + n_seq + n_norm;
   size_t off = 0;
   const size_t off_words = off;
   off = align_up(off + n_words * sizeof(uint64_t), 256);
@@ -149,7 +149,6 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->ws.stat_words = words;
   h->ws.seq_words = words + n_stat;
   h->ws.norm_words = words + n_stat + n_seq;
-  h->ws.wsum_words = words + n_stat + n_seq + n_norm;
   h->ws.n_words = static_cast<long long>(n_words);
   h->ws.exp_table = reinterpret_cast<double*>(base + off_table);
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
@@ -164,6 +163,16 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
     delete h;
     return SPECV_EHIP;
   }
+#ifdef SPECV_TRACE
+  // Diagnostic builds: one 32-byte record per item slot of the largest call.
+  h->ws.trace_slots = (long long)(max_batch + 64) *
+                      ((2 * max_draft + 1) * nch + 1 + nsch + 1);
+  if (hipMalloc(&h->ws.trace, h->ws.trace_slots * 32) != hipSuccess) {
+    (void)hipFree(h->mem);
+    delete h;
+    return SPECV_ENOMEM;
+  }
+#endif
   if (!init_config(h)) {
     (void)hipFree(h->mem);
     delete h;
@@ -277,6 +286,19 @@ int specv_last_timings(specv_handle h, float* ms, int capacity, int* count) {
 }
 
 const char* specv_stage_name(int stage) { return specv::stage_name(stage); }
+
+#ifdef SPECV_TRACE
+// Diagnostic builds only: copy the item records of the last call to host memory.
+SPECV_API int specv_debug_trace(specv_handle h, void* host, long long max_slots, long long* n_slots) {
+  if (h == nullptr || host == nullptr || n_slots == nullptr) return SPECV_EINVAL;
+  DeviceGuard guard(h->device);
+  if (hipDeviceSynchronize() != hipSuccess) return SPECV_EHIP;
+  const long long n = std::min(max_slots, h->ws.trace_slots);
+  if (hipMemcpy(host, h->ws.trace, n * 32, hipMemcpyDeviceToHost) != hipSuccess) return SPECV_EHIP;
+  *n_slots = n;
+  return SPECV_OK;
+}
+#endif
 
 void specv_destroy(specv_handle h) {
   if (h == nullptr) return;

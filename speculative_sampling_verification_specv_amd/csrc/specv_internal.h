@@ -8,7 +8,11 @@ namespace specv {
 
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64s)
 constexpr int kStatsChunk = 8192;  // logits per row-statistics work item
-constexpr int kSampChunk = 2048;   // logits per draw work item
+constexpr int kSampChunk = 4096;   // logits per draw (NORM) work item
+
+// Largest vocabulary a handle accepts, so a sequence's draw chunks fit in LDS.
+constexpr int kMaxVocab = 1 << 22;
+constexpr int kMaxSampChunks = kMaxVocab / kSampChunk;
 
 // Smallest positive temperature accepted: keeps log2(e)/T and max|z|*log2(e)/T
 // finite in fp32 for logits up to 2^64 in magnitude.
@@ -23,15 +27,18 @@ enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 // payload and the 16-bit epoch of the call that wrote it.
 struct Workspace {
   uint64_t* stat_words;  // [max_batch * (2*max_draft+1)][n_stats_chunks][2]
-  uint64_t* seq_words;   // [max_batch][2]
-  uint64_t* norm_words;  // [max_batch][n_samp_chunks][4]
-  uint64_t* wsum_words;  // [max_batch][n_samp_chunks][2]
-  long long n_words;     // total words, all four arrays (contiguous from stat_words)
+  uint64_t* seq_words;   // [max_batch][seq_words_per_sequence()]
+  uint64_t* norm_words;  // [max_batch][n_samp_chunks][norm_words_per_chunk()]
+  long long n_words;     // total words, all three arrays (contiguous from stat_words)
   double* exp_table;     // [64]: 2^(j/64)
   float* row_lse;        // [batch][2N+1] of the last call
   int* row_argmax;       // [batch][2N+1] of the last call
   int n_stats_chunks;
   int n_samp_chunks;
+#ifdef SPECV_TRACE
+  unsigned long long* trace;  // per-slot item records (diagnostic builds only)
+  long long trace_slots;
+#endif
 };
 
 struct VerifyArgs {
@@ -52,9 +59,9 @@ struct VerifyArgs {
 // Per-call launch parameters chosen by the host.
 struct LaunchConfig {
   long long max_blocks;              // persistent grid cap
-  int lag_decide;                    // slots groups (sequences) between STAT(b) and DECIDE(b)
-  int lag_draw1;                     // ... and DRAW1(b, *)
-  int lag_draw2;                     // ... and DRAW2(b)
+  int lag_decide;                    // item groups (sequences) between STAT(b) and DECIDE(b)
+  int lag_norm;                      // ... and NORM(b, *)
+  int lag_draw;                      // ... and DRAW(b)
   unsigned epoch;                    // 1..kMaxEpoch
   unsigned long long timeout_ticks;  // wall-clock ticks a wait lasts before it computes the item itself
 };
@@ -68,6 +75,10 @@ const char* stage_name(int stage);
 
 // Workgroups of the verify kernel one CU can hold.
 int max_blocks_per_cu(int dtype);
+
+// Tagged words per draw chunk and per sequence.
+int norm_words_per_chunk();
+int seq_words_per_sequence();
 
 // Zero n words (epoch 0 is never used, so cleared words read as stale).
 hipError_t clear_words(uint64_t* p, long long n, hipStream_t stream);

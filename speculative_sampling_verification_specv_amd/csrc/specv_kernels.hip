@@ -10,16 +10,26 @@
 //   STAT(b, r, c)  fp32 (max, sum 2^(z*c - K), first argmax) of 8192 logits of row r.
 //   DECIDE(b)      merge STAT partials into per-row log-normalisers, run the N
 //                  accept tests in fp64, find the first rejection j.
-//   DRAW1(b, c)    fp64 exp of 2048 logits of the row(s) the draw needs; after a
-//                  rejection, the two fp64 normalisers (sum over all chunks) then
-//                  the weight sum of (q_j - p_j)_+ over the chunk; for the bonus,
-//                  the sum of exp((z - max)/T) of target row N.
-//   DRAW2(b)       inverse CDF: find the chunk where the cumulative weight
-//                  crosses u*S, rescan it in fp64, write the token.
-// Items are laid out in slots, sequence-major, with DECIDE, DRAW1 and DRAW2 of
+//   NORM(b, c)     fp64 exp of 4096 logits of the row(s) the draw needs. After a
+//                  rejection: fp64 sums Zt, Zd of exp((z - max)/T) over target and
+//                  draft row j, and the sums A, B of the same over the tokens whose
+//                  residual weight is certainly positive, plus the indices of the
+//                  few tokens whose sign is uncertain (see below). For the bonus:
+//                  the sum of exp((z - max)/T) over target row N.
+//   DRAW(b)        chunk weights, inverse CDF over them, an fp64 rescan of the
+//                  crossing chunk, the token.
+// Items are laid out in slots, sequence-major, with DECIDE, NORM and DRAW of
 // sequence b placed a few sequences after STAT(b, ...); slot s belongs to
-// workgroup s mod G, so the sampler's fp64 work overlaps later sequences' HBM
+// workgroup s mod G, so the draw's fp64 work overlaps later sequences' HBM
 // streaming.
+//
+// The residual weight of token x is w_x = max(0, et_x/Zt - ed_x/Zd)
+// = max(0, et_x - rho*ed_x)/Zt with rho = Zt/Zd, so its sign only depends on
+// whether log(et_x/ed_x) exceeds log(rho). DECIDE knows log(rho) from the fp32
+// row sums to ~1e-6; NORM treats tokens more than 1e-4 away from it as certain
+// and sums their exps into A and B, so that a chunk's weight is (A - rho*B)/Zt
+// plus the exact terms of its uncertain tokens. No chunk has to wait for the
+// global normalisers.
 //
 // Communication between workgroups uses no fences and no read-modify-write
 // atomics (both are very slow across this GPU's per-XCD L2 caches). Each result
@@ -50,8 +60,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSampPer = kSampChunk / kThreads;  // logits per thread in a DRAW1 item
+constexpr int kSampPer = kSampChunk / kThreads;  // logits per thread in a NORM item
 constexpr int kMaxRows = 2 * 64 + 1;
+constexpr int kUncMax = 16;                      // uncertain tokens a NORM item records
+constexpr int kNormWords = 9 + kUncMax;          // Zt, Zd, A, B (2 words each), count, indices
+constexpr int kSeqWords = 4;
+constexpr double kSignBand = 1e-4;               // |log(et/ed) - log(rho)| below this is uncertain
+constexpr int kStageCap = 1024;                  // STAT partials DECIDE stages in LDS
 
 __device__ __forceinline__ bool temperature_valid(float t) {
   return t == 0.0f || (t >= kMinTemperature && t <= kFltMax);
@@ -135,21 +150,24 @@ __device__ __forceinline__ double unpack_f64(uint64_t w0, uint64_t w1) {
 struct SeqInfo {
   int mode;  // SeqMode
   int j;
-  float m_target;
-  float m_draft;
+  float m_target;  // largest logit of target row j
+  float m_draft;   // largest logit of draft row j (residual only)
+  double log_rho;  // log(Zt/Zd) from the fp32 row sums (residual only)
 };
 __device__ __forceinline__ void publish_seq(uint64_t* w, const SeqInfo& s, unsigned epoch) {
   publish(w, (uint64_t(__float_as_uint(s.m_target)) << 16) | (uint64_t(s.j & 0xff) << 8) | uint64_t(s.mode & 0xff),
           epoch);
   publish(w + 1, uint64_t(__float_as_uint(s.m_draft)) << 16, epoch);
+  publish_f64(w + 2, s.log_rho, epoch);
 }
-__device__ __forceinline__ SeqInfo unpack_seq(uint64_t w0, uint64_t w1) {
+__device__ __forceinline__ SeqInfo unpack_seq(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3) {
   SeqInfo s;
   const uint64_t p0 = payload(w0);
   s.m_target = __uint_as_float(uint32_t(p0 >> 16));
   s.j = int((p0 >> 8) & 0xff);
   s.mode = int(p0 & 0xff);
   s.m_draft = __uint_as_float(uint32_t(payload(w1) >> 16));
+  s.log_rho = unpack_f64(w2, w3);
   return s;
 }
 
@@ -168,9 +186,8 @@ struct Params {
   float* row_lse;
   int* row_argmax;
   uint64_t* stat_words;  // [B*R][nch][2]
-  uint64_t* seq_words;   // [B][2]
-  uint64_t* norm_words;  // [B][nsch][4]
-  uint64_t* wsum_words;  // [B][nsch][2]
+  uint64_t* seq_words;   // [B][kSeqWords]
+  uint64_t* norm_words;  // [B][nsch][kNormWords]
   const double* exp_table;
   int batch;
   int n_draft;
@@ -180,10 +197,14 @@ struct Params {
   int spg;  // slots per group
   long long total_slots;
   int lag_decide;
-  int lag_draw1;
-  int lag_draw2;
+  int lag_norm;
+  int lag_draw;
   unsigned epoch;
   unsigned long long timeout_ticks;
+#ifdef SPECV_TRACE
+  unsigned long long* trace;  // [total_slots][4]: kind|block<<8, start, end, wait ticks|timeouts<<48
+  long long trace_slots;
+#endif
 };
 
 struct Shared {
@@ -194,6 +215,23 @@ struct Shared {
   int row_idx[kMaxRows];
   int flag;
   int pick[2];
+  int unc_base[kWaves];
+  // DECIDE stages STAT partials here; DRAW keeps chunk weights and flags here.
+  union {
+    struct {
+      float m[kStageCap];
+      float s[kStageCap];
+      int idx[kStageCap];
+    } part;
+    struct {
+      double w[kMaxSampChunks];
+      int dirty[kMaxSampChunks];
+    } draw;
+  } u;
+#ifdef SPECV_TRACE
+  unsigned long long wait_ticks;
+  unsigned long long timeouts;
+#endif
 };
 
 __device__ __forceinline__ double block_sum(double v, Shared& sh) {
@@ -208,15 +246,53 @@ __device__ __forceinline__ double block_sum(double v, Shared& sh) {
   return total;
 }
 
+// Block-wide inclusive scan of one double per thread (fixed order); returns
+// the thread's inclusive prefix and sets total.
+__device__ __forceinline__ double block_scan(double v, double& total, Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  double incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  __syncthreads();
+  if (lane == 63) sh.red[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  double before = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < (int(threadIdx.x) >> 6)) before += sh.red[w];
+    total += sh.red[w];
+  }
+  return before + incl;
+}
+
+__device__ __forceinline__ void note_wait(Shared& sh, unsigned long long t0, bool timed_out) {
+#ifdef SPECV_TRACE
+  if (threadIdx.x == 0) {
+    sh.wait_ticks += wall_clock64() - t0;
+    sh.timeouts += timed_out ? 1 : 0;
+  }
+#endif
+}
+
 // True (in every thread) once all n words carry the epoch; false on timeout.
-__device__ bool block_wait(uint64_t* words, int n, const Params P) {
+__device__ bool block_wait(uint64_t* words, int n, const Params P, Shared& sh) {
   const unsigned long long t0 = wall_clock64();
   while (true) {
     bool ok = true;
     for (int i = threadIdx.x; i < n; i += kThreads) ok = ok && tagged(fetch(words + i), P.epoch);
-    if (__syncthreads_and(ok)) return true;
+    if (__syncthreads_and(ok)) {
+      note_wait(sh, t0, false);
+      return true;
+    }
     const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
-    if (__syncthreads_or(expired)) return false;
+    if (__syncthreads_or(expired)) {
+      note_wait(sh, t0, true);
+      return false;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -385,10 +461,10 @@ __device__ __forceinline__ const T* row_ptr(const Params P, int b, int r, int64_
   return static_cast<const T*>(P.target) + row_flat;
 }
 
-// Computes and publishes STAT(b, r, chunk). Skips rows the sequence never needs.
+// Computes and publishes STAT(b, r, chunk); t is sequence b's temperature.
+// Skips rows the sequence never needs.
 template <typename T>
-__device__ void stat_item(const Params P, Shared& sh, int b, int r, int chunk) {
-  const float t = P.temperature[b];
+__device__ void stat_item(const Params P, Shared& sh, int b, int r, int chunk, float t) {
   if (!temperature_valid(t)) return;
   const bool greedy = (t == 0.0f);
   if (greedy && r < P.n_draft) return;
@@ -412,21 +488,49 @@ __device__ void stat_item(const Params P, Shared& sh, int b, int r, int chunk) {
   }
 }
 
-// Ensures STAT partials of rows [r0, r1) of sequence b carry the epoch.
-template <typename T>
-__device__ void ensure_stats(const Params P, Shared& sh, int b, int r0, int r1) {
-  const int R = 2 * P.n_draft + 1;
-  uint64_t* base = P.stat_words + (int64_t(b) * R + r0) * P.nch * 2;
-  const int n = (r1 - r0) * P.nch * 2;
-  if (block_wait(base, n, P)) return;
-  for (int r = r0; r < r1; ++r)
-    for (int c = 0; c < P.nch; ++c)
-      if (!block_has(P.stat_words + ((int64_t(b) * R + r) * P.nch + c) * 2, 2, P, sh)) stat_item<T>(P, sh, b, r, c);
-  __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
 // DECIDE: log-normalisers, accept tests, first rejection, outputs.
+
+// Waits for (or computes) the STAT partials of rows [r0, R); when they fit,
+// leaves them unpacked in shared memory (returns true).
+template <typename T>
+__device__ bool gather_stats(const Params P, Shared& sh, int b, int r0, float t) {
+  const int R = 2 * P.n_draft + 1;
+  const int n_part = (R - r0) * P.nch;
+  uint64_t* base = P.stat_words + (int64_t(b) * R + r0) * P.nch * 2;
+  const bool staged = n_part <= kStageCap;
+  const unsigned long long t0 = wall_clock64();
+  bool waited_out = false;
+  while (true) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < n_part; i += kThreads) {
+      const uint64_t w0 = fetch(base + 2 * i), w1 = fetch(base + 2 * i + 1);
+      ok = ok && tagged(w0, P.epoch) && tagged(w1, P.epoch);
+      if (staged) unpack_partial(w0, w1, sh.u.part.m[i], sh.u.part.s[i], sh.u.part.idx[i]);
+    }
+    if (__syncthreads_and(ok)) break;
+    const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
+    if (__syncthreads_or(expired)) {
+      waited_out = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  note_wait(sh, t0, waited_out);
+  if (waited_out) {
+    for (int r = r0; r < R; ++r)
+      for (int c = 0; c < P.nch; ++c)
+        if (!block_has(P.stat_words + ((int64_t(b) * R + r) * P.nch + c) * 2, 2, P, sh)) stat_item<T>(P, sh, b, r, c, t);
+    __syncthreads();
+    if (staged) {
+      for (int i = threadIdx.x; i < n_part; i += kThreads)
+        unpack_partial(fetch(base + 2 * i), fetch(base + 2 * i + 1), sh.u.part.m[i], sh.u.part.s[i],
+                       sh.u.part.idx[i]);
+    }
+  }
+  __syncthreads();
+  return staged;
+}
 
 template <typename T>
 __device__ void decide_item(const Params P, Shared& sh, int b) {
@@ -439,13 +543,17 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   float* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  uint64_t* seqw = P.seq_words + int64_t(b) * 2;
+  uint64_t* seqw = P.seq_words + int64_t(b) * kSeqWords;
 
+  // Issue the inputs of the accept tests before waiting for the row sums.
   const float t = P.temperature[b];
+  int d = 0;
+  float zt = 0.0f, zd = 0.0f, ua = 0.0f;
   bool bad = !temperature_valid(t);
-  for (int i = tid; i < N; i += kThreads) {
-    const int d = tok[i];
+  if (tid < N) {
+    d = tok[tid];
     bad = bad || d < 0 || d >= P.vocab;
+    ua = P.accept_u[int64_t(b) * N + tid];
   }
   if (__syncthreads_or(bad)) {
     for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
@@ -455,15 +563,18 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
     }
     if (tid == 0) {
       P.out_n[b] = -1;
-      SeqInfo s{kModeNone, 0, 0.0f, 0.0f};
+      SeqInfo s{kModeNone, 0, 0.0f, 0.0f, 0.0};
       publish_seq(seqw, s, P.epoch);
     }
     return;
   }
-
   const bool greedy = (t == 0.0f);
+  if (tid < N && !greedy) {
+    zt = Logit<T>::at(static_cast<const T*>(P.target), (int64_t(b) * (N + 1) + tid) * P.vocab + d);
+    zd = Logit<T>::at(static_cast<const T*>(P.draft), (int64_t(b) * N + tid) * P.vocab + d);
+  }
   const int r_first = greedy ? N : 0;
-  ensure_stats<T>(P, sh, b, r_first, R);
+  const bool staged = gather_stats<T>(P, sh, b, r_first, t);
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
 
@@ -478,12 +589,19 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
       continue;
     }
     uint64_t* rw = P.stat_words + (int64_t(b) * R + r) * P.nch * 2;
+    const int pbase = (r - r_first) * P.nch;
     float m = -INFINITY, s = 0.0f;
     int idx = INT_MAX;
     for (int k = lane; k < P.nch; k += 64) {
       float m2, s2;
       int i2;
-      unpack_partial(fetch(rw + 2 * k), fetch(rw + 2 * k + 1), m2, s2, i2);
+      if (staged) {
+        m2 = sh.u.part.m[pbase + k];
+        s2 = sh.u.part.s[pbase + k];
+        i2 = sh.u.part.idx[pbase + k];
+      } else {
+        unpack_partial(fetch(rw + 2 * k), fetch(rw + 2 * k + 1), m2, s2, i2);
+      }
       if (greedy)
         acc_merge<false>(m, s, idx, m2, s2, i2, c);
       else
@@ -515,24 +633,19 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
   if (wave == 0) {
     bool accept = true;
     if (lane < N) {
-      const int d = tok[lane];
       if (greedy) {
         accept = (d == sh.row_idx[N + lane]);
+      } else if (zd == -INFINITY) {
+        accept = true;  // p(d) == 0: the ratio is infinite
       } else {
-        const float zt = Logit<T>::at(static_cast<const T*>(P.target), (int64_t(b) * (N + 1) + lane) * P.vocab + d);
-        const float zd = Logit<T>::at(static_cast<const T*>(P.draft), (int64_t(b) * N + lane) * P.vocab + d);
-        if (zd == -INFINITY) {
-          accept = true;  // p(d) == 0: the ratio is infinite
-        } else {
-          const double log_q = (double(zt) - double(sh.row_m[N + lane])) * inv_t - sh.row_logz[N + lane];
-          const double log_p = (double(zd) - double(sh.row_m[lane])) * inv_t - sh.row_logz[lane];
-          accept = double(P.accept_u[int64_t(b) * N + lane]) < exp(log_q - log_p);
-        }
+        const double log_q = (double(zt) - double(sh.row_m[N + lane])) * inv_t - sh.row_logz[N + lane];
+        const double log_p = (double(zd) - double(sh.row_m[lane])) * inv_t - sh.row_logz[lane];
+        accept = double(ua) < exp(log_q - log_p);
       }
     }
     const unsigned long long rej = __ballot(lane < N && !accept);
     const int j = rej ? (__ffsll(rej) - 1) : N;
-    // Position j of a sampled sequence is left to DRAW2: a duplicate DECIDE
+    // Position j of a sampled sequence is left to DRAW: a duplicate DECIDE
     // running after it must not overwrite the drawn token.
     for (int i = lane; i <= N; i += 64) {
       if (i < j)
@@ -549,6 +662,7 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
       s.j = j;
       s.m_target = sh.row_m[N + j];
       s.m_draft = (j < N && !greedy) ? sh.row_m[j] : 0.0f;
+      s.log_rho = (j < N && !greedy) ? sh.row_logz[N + j] - sh.row_logz[j] : 0.0;
       publish_seq(seqw, s, P.epoch);
     }
   }
@@ -557,13 +671,13 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
 
 template <typename T>
 __device__ SeqInfo ensure_decided(const Params P, Shared& sh, int b) {
-  uint64_t* w = P.seq_words + int64_t(b) * 2;
-  if (!block_wait(w, 2, P)) decide_item<T>(P, sh, b);
-  return unpack_seq(fetch(w), fetch(w + 1));
+  uint64_t* w = P.seq_words + int64_t(b) * kSeqWords;
+  if (!block_wait(w, kSeqWords, P, sh)) decide_item<T>(P, sh, b);
+  return unpack_seq(fetch(w), fetch(w + 1), fetch(w + 2), fetch(w + 3));
 }
 
 // ---------------------------------------------------------------------------
-// Draw: fp64 weights, chunk sums, inverse CDF.
+// Draw: fp64 exps, chunk sums, inverse CDF.
 
 template <typename T>
 struct DrawRows {
@@ -586,229 +700,250 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params P, int b, const Se
   return d;
 }
 
-// exp((z - max)/T) of token e of the target (and draft) row; 0 past the row end.
+// Arguments (z - max)/T of token e's exps; -inf past the row end.
 template <typename T>
-__device__ __forceinline__ void draw_exps(const DrawRows<T>& d, int e, int vocab, const double* tbl, double& et,
-                                          double& ed) {
-  et = 0.0;
-  ed = 0.0;
+__device__ __forceinline__ void draw_args(const DrawRows<T>& d, int e, int vocab, double& at, double& ad) {
+  at = -INFINITY;
+  ad = -INFINITY;
   if (e < vocab) {
-    et = exp_nonpos((double(Logit<T>::at(d.trow, e)) - d.mt) * d.inv_t, tbl);
-    if (d.residual) ed = exp_nonpos((double(Logit<T>::at(d.drow, e)) - d.md) * d.inv_t, tbl);
+    at = (double(Logit<T>::at(d.trow, e)) - d.mt) * d.inv_t;
+    if (d.residual) ad = (double(Logit<T>::at(d.drow, e)) - d.md) * d.inv_t;
   }
 }
 
-// Weight of a token given its exps: (q - p)_+ after a rejection, else the
-// self-normalised target exp (the bonus).
-__device__ __forceinline__ double draw_weight(bool residual, double et, double ed, double rt, double rd) {
-  return residual ? fmax(0.0, et * rt - ed * rd) : et;
+// Residual weight of a token from its exps and the reciprocal normalisers.
+__device__ __forceinline__ double resid_weight(double et, double ed, double rt, double rd) {
+  return fmax(0.0, et * rt - ed * rd);
 }
 
-// Per-chunk fp64 sums of exp((z - m)/T) over target and draft row j.
+// NORM(b, c): publishes Zt, Zd, A, B and the uncertain tokens of one chunk
+// (bonus: only Zt, the chunk's weight).
 template <typename T>
-__device__ void norm_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d) {
-  double st = 0.0, sd = 0.0;
+__device__ void norm_compute(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d, double log_rho) {
+  const int tid = threadIdx.x;
+  double zt = 0.0, zd = 0.0, sa = 0.0, sb = 0.0;
+  uint32_t unc = 0;  // bit k: token c*kSampChunk + tid + k*kThreads is uncertain
 #pragma unroll
   for (int k = 0; k < kSampPer; ++k) {
-    double et, ed;
-    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
-    st += et;
-    sd += ed;
-  }
-  st = block_sum(st, sh);
-  sd = block_sum(sd, sh);
-  if (threadIdx.x == 0) {
-    uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * 4;
-    publish_f64(w, st, P.epoch);
-    publish_f64(w + 2, sd, P.epoch);
-  }
-}
-
-// Reciprocal normalisers 1/Z of target and draft row j, waiting for (or
-// computing) every chunk's fp64 sums. Fixed summation order.
-template <typename T>
-__device__ void normalisers(const Params P, Shared& sh, int b, const DrawRows<T>& d, double& rt, double& rd) {
-  uint64_t* base = P.norm_words + int64_t(b) * P.nsch * 4;
-  if (!block_wait(base, P.nsch * 4, P)) {
-    for (int c = 0; c < P.nsch; ++c)
-      if (!block_has(base + 4 * c, 4, P, sh)) norm_item<T>(P, sh, b, c, d);
-    __syncthreads();
-  }
-  double zt = 0.0, zd = 0.0;
-  for (int c = threadIdx.x; c < P.nsch; c += kThreads) {
-    zt += unpack_f64(fetch(base + 4 * c), fetch(base + 4 * c + 1));
-    zd += unpack_f64(fetch(base + 4 * c + 2), fetch(base + 4 * c + 3));
+    double at, ad;
+    draw_args(d, c * kSampChunk + tid + k * kThreads, P.vocab, at, ad);
+    const double et = exp_nonpos(at, sh.exp_table);
+    zt += et;
+    if (d.residual) {
+      const double ed = exp_nonpos(ad, sh.exp_table);
+      zd += ed;
+      if (et > 0.0) {
+        const double lr = at - ad;  // +inf when the draft gives the token zero mass
+        if (ed == 0.0 || lr > log_rho + kSignBand) {
+          sa += et;
+          sb += ed;
+        } else if (lr >= log_rho - kSignBand) {
+          unc |= 1u << k;
+        }
+      }
+    }
   }
   zt = block_sum(zt, sh);
+  uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * kNormWords;
+  if (!d.residual) {
+    if (tid == 0) publish_f64(w, zt, P.epoch);
+    __syncthreads();
+    return;
+  }
   zd = block_sum(zd, sh);
-  rt = 1.0 / zt;
-  rd = 1.0 / zd;
-}
-
-// Weight sum of one chunk from scratch (used when a DRAW1 result is missing).
-template <typename T>
-__device__ void wsum_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d, double rt, double rd) {
-  double w = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampPer; ++k) {
-    double et, ed;
-    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
-    w += draw_weight(d.residual, et, ed, rt, rd);
-  }
-  w = block_sum(w, sh);
-  if (threadIdx.x == 0) publish_f64(P.wsum_words + (int64_t(b) * P.nsch + c) * 2, w, P.epoch);
-}
-
-// DRAW1(b, c): exps held in registers across both reductions.
-template <typename T>
-__device__ void draw1_item(const Params P, Shared& sh, int b, int c) {
-  const SeqInfo s = ensure_decided<T>(P, sh, b);
-  if (s.mode == kModeNone) return;
-  const DrawRows<T> d = draw_rows<T>(P, b, s);
-  double et[kSampPer], ed[kSampPer];
-  double st = 0.0, sd = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampPer; ++k) {
-    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et[k], ed[k]);
-    st += et[k];
-    sd += ed[k];
-  }
-  double rt = 0.0, rd = 0.0;
-  if (d.residual) {
-    st = block_sum(st, sh);
-    sd = block_sum(sd, sh);
-    if (threadIdx.x == 0) {
-      uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * 4;
-      publish_f64(w, st, P.epoch);
-      publish_f64(w + 2, sd, P.epoch);
-    }
-    normalisers<T>(P, sh, b, d, rt, rd);
-  }
-  double w = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampPer; ++k) w += draw_weight(d.residual, et[k], ed[k], rt, rd);
-  w = block_sum(w, sh);
-  if (threadIdx.x == 0) publish_f64(P.wsum_words + (int64_t(b) * P.nsch + c) * 2, w, P.epoch);
-}
-
-// Block-wide inclusive scan of one double per thread (fixed order); returns
-// the thread's inclusive prefix and sets total.
-__device__ __forceinline__ double block_scan(double v, double& total, Shared& sh) {
-  const int lane = threadIdx.x & 63;
-  double incl = v;
+  sa = block_sum(sa, sh);
+  sb = block_sum(sb, sh);
+  // Uncertain tokens, listed in (thread, k) order.
+  const int cnt = __popc(unc);
+  int incl = cnt;
+  const int lane = tid & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const double up = __shfl_up(incl, off);
+    const int up = __shfl_up(incl, off);
     if (lane >= off) incl += up;
   }
   __syncthreads();
-  if (lane == 63) sh.red[threadIdx.x >> 6] = incl;
+  if (lane == 63) sh.unc_base[tid >> 6] = incl;
   __syncthreads();
-  double before = 0.0;
-  total = 0.0;
+  int slot = incl - cnt, total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < (int(threadIdx.x) >> 6)) before += sh.red[w];
-    total += sh.red[w];
+  for (int wv = 0; wv < kWaves; ++wv) {
+    if (wv < (tid >> 6)) slot += sh.unc_base[wv];
+    total += sh.unc_base[wv];
   }
-  return before + incl;
+  if (total <= kUncMax) {
+#pragma unroll
+    for (int k = 0; k < kSampPer; ++k)
+      if (unc & (1u << k)) publish(w + 9 + slot++, uint64_t(c * kSampChunk + tid + k * kThreads), P.epoch);
+  }
+  if (tid == 0) {
+    publish_f64(w, zt, P.epoch);
+    publish_f64(w + 2, zd, P.epoch);
+    publish_f64(w + 4, sa, P.epoch);
+    publish_f64(w + 6, sb, P.epoch);
+    publish(w + 8, uint64_t(total), P.epoch);
+    // Unused index words still need the epoch: a reader waits on all of them.
+    for (int k = min(total, kUncMax); k < kUncMax; ++k) publish(w + 9 + k, 0, P.epoch);
+  }
+  __syncthreads();
 }
 
-// Sum over one chunk of q_j = exp((z - m)/T) / Z (the fallback draw's weights).
 template <typename T>
-__device__ double q_chunk_sum(const Params P, Shared& sh, int c, const DrawRows<T>& d, double inv_z) {
+__device__ void norm_item(const Params P, Shared& sh, int b, int c) {
+  const SeqInfo s = ensure_decided<T>(P, sh, b);
+  if (s.mode == kModeNone) return;
+  norm_compute<T>(P, sh, b, c, draw_rows<T>(P, b, s), s.log_rho);
+}
+
+// Weight sum of one chunk from its logits (after a rejection): used for
+// chunks with too many uncertain tokens.
+template <typename T>
+__device__ double chunk_weight(const Params P, Shared& sh, int c, const DrawRows<T>& d, double rt, double rd) {
   double w = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampPer; ++k) {
-    double et, ed;
-    draw_exps(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, sh.exp_table, et, ed);
-    w += et * inv_z;
+    double at, ad;
+    draw_args(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, at, ad);
+    w += resid_weight(exp_nonpos(at, sh.exp_table), exp_nonpos(ad, sh.exp_table), rt, rd);
   }
   return block_sum(w, sh);
 }
 
-// DRAW2(b): chunk crossing, then an fp64 scan of that chunk.
+// DRAW(b): chunk weights, the crossing chunk, an fp64 scan of it.
 template <typename T>
-__device__ void draw2_item(const Params P, Shared& sh, int b) {
+__device__ void draw_item(const Params P, Shared& sh, int b) {
   const SeqInfo s = ensure_decided<T>(P, sh, b);
   if (s.mode == kModeNone) return;
   DrawRows<T> d = draw_rows<T>(P, b, s);
   const int tid = threadIdx.x;
-  double rt = 0.0, rd = 0.0;
-  if (d.residual) normalisers<T>(P, sh, b, d, rt, rd);
-  uint64_t* ws = P.wsum_words + int64_t(b) * P.nsch * 2;
-  if (!block_wait(ws, P.nsch * 2, P)) {
-    for (int c = 0; c < P.nsch; ++c)
-      if (!block_has(ws + 2 * c, 2, P, sh)) wsum_item<T>(P, sh, b, c, d, rt, rd);
-    __syncthreads();
-  }
-  // Total S as a scan over chunk sums in groups of 256 chunks.
-  double S = 0.0;
-  for (int g = 0; g < P.nsch; g += kThreads) {
-    const int c = g + tid;
-    const double w = (c < P.nsch) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
-    double tot;
-    block_scan(w, tot, sh);
-    S += tot;
-  }
-  const double u = double(P.sample_u[b]);
-  double target_mass, before = 0.0;
-  int chunk = -1;
-  bool fallback = false;
-  if (d.residual && !(S > 0.0)) {
-    // Every residual weight rounded to zero: draw from q_j itself. Chunk sums
-    // are recomputed here (twice, in the same order) and kept local.
-    fallback = true;
-    S = 0.0;
-    for (int c = 0; c < P.nsch; ++c) S += q_chunk_sum<T>(P, sh, c, d, rt);
-    target_mass = u * S;
-    int last_pos = 0;
-    for (int c = 0; c < P.nsch; ++c) {
-      const double w = q_chunk_sum<T>(P, sh, c, d, rt);
-      if (w > 0.0) last_pos = c;
-      if (before + w > target_mass) {
-        chunk = c;
+  const int nsch = P.nsch;
+  uint64_t* nw = P.norm_words + int64_t(b) * nsch * kNormWords;
+  const int words_per_chunk = d.residual ? kNormWords : 2;
+  // Wait for every chunk's NORM words (bonus: the first two of each chunk).
+  {
+    const unsigned long long t0 = wall_clock64();
+    bool waited_out = false;
+    while (true) {
+      bool ok = true;
+      for (int i = tid; i < nsch * words_per_chunk; i += kThreads) {
+        const int cc = i / words_per_chunk, k = i - cc * words_per_chunk;
+        ok = ok && tagged(fetch(nw + cc * kNormWords + k), P.epoch);
+      }
+      if (__syncthreads_and(ok)) break;
+      const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
+      if (__syncthreads_or(expired)) {
+        waited_out = true;
         break;
       }
-      before += w;
+      __builtin_amdgcn_s_sleep(1);
     }
-    if (chunk < 0) {
-      chunk = last_pos;
-      before = 0.0;
-      for (int c = 0; c < chunk; ++c) before += q_chunk_sum<T>(P, sh, c, d, rt);
+    note_wait(sh, t0, waited_out);
+    if (waited_out) {
+      for (int cc = 0; cc < nsch; ++cc)
+        if (!block_has(nw + cc * kNormWords, words_per_chunk, P, sh)) norm_compute<T>(P, sh, b, cc, d, s.log_rho);
+      __syncthreads();
     }
-  } else {
-    target_mass = u * S;
-    // First chunk whose inclusive prefix exceeds target_mass.
-    int last_pos = -1;
-    for (int g = 0; g < P.nsch && chunk < 0; g += kThreads) {
-      const int c = g + tid;
-      const double w = (c < P.nsch) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
-      double tot;
-      const double incl = before + block_scan(w, tot, sh);
-      if (tid == 0) {
-        sh.pick[0] = INT_MAX;
-        sh.pick[1] = -1;
+  }
+  // Normalisers (fixed order) and the chunk weights.
+  double rt = 0.0, rd = 0.0, rho = 0.0;
+  if (d.residual) {
+    double zt = 0.0, zd = 0.0;
+    for (int cc = tid; cc < nsch; cc += kThreads) {
+      zt += unpack_f64(fetch(nw + cc * kNormWords), fetch(nw + cc * kNormWords + 1));
+      zd += unpack_f64(fetch(nw + cc * kNormWords + 2), fetch(nw + cc * kNormWords + 3));
+    }
+    zt = block_sum(zt, sh);
+    zd = block_sum(zd, sh);
+    rt = 1.0 / zt;
+    rd = 1.0 / zd;
+    rho = zt * rd;
+  }
+  for (int cc = tid; cc < nsch; cc += kThreads) {
+    uint64_t* w = nw + cc * kNormWords;
+    double wc = unpack_f64(fetch(w), fetch(w + 1));
+    int dirty = 0;
+    if (d.residual) {
+      const double sa = unpack_f64(fetch(w + 4), fetch(w + 5));
+      const double sb = unpack_f64(fetch(w + 6), fetch(w + 7));
+      const int nu = int(payload(fetch(w + 8)));
+      wc = rt * (sa - rho * sb);
+      if (nu > kUncMax) {
+        dirty = 1;
+      } else {
+        for (int k = 0; k < nu; ++k) {
+          const int e = int(payload(fetch(w + 9 + k)));
+          double at, ad;
+          draw_args(d, e, P.vocab, at, ad);
+          wc += resid_weight(exp_nonpos(at, sh.exp_table), exp_nonpos(ad, sh.exp_table), rt, rd);
+        }
       }
-      __syncthreads();
-      if (c < P.nsch && incl > target_mass && w > 0.0) atomicMin(&sh.pick[0], c);
-      if (c < P.nsch && w > 0.0) atomicMax(&sh.pick[1], c);
-      __syncthreads();
-      if (sh.pick[1] >= 0) last_pos = sh.pick[1];
-      if (sh.pick[0] != INT_MAX) chunk = sh.pick[0];
-      before += tot;
+    }
+    sh.u.draw.w[cc] = wc;
+    sh.u.draw.dirty[cc] = dirty;
+  }
+  __syncthreads();
+  for (int cc = 0; cc < nsch; ++cc) {
+    if (sh.u.draw.dirty[cc]) {
+      const double wc = chunk_weight<T>(P, sh, cc, d, rt, rd);
+      if (tid == 0) sh.u.draw.w[cc] = wc;
       __syncthreads();
     }
-    if (chunk < 0) chunk = max(last_pos, 0);  // rounding left u*S at or past the total
-    // Exclusive prefix of the chosen chunk, in the same group-scan order.
-    before = 0.0;
-    for (int g = 0; g < chunk; g += kThreads) {
-      const int c = g + tid;
-      const double w = (c < chunk) ? unpack_f64(fetch(ws + 2 * c), fetch(ws + 2 * c + 1)) : 0.0;
+  }
+  // Total S, as a scan over the chunk weights in groups of 256 chunks.
+  double S = 0.0;
+  for (int g = 0; g < nsch; g += kThreads) {
+    const int cc = g + tid;
+    double tot;
+    block_scan(cc < nsch ? sh.u.draw.w[cc] : 0.0, tot, sh);
+    S += tot;
+  }
+  bool fallback = false;
+  if (d.residual && !(S > 0.0)) {
+    // Every residual weight rounded to zero: draw from q_j itself, whose
+    // chunk weights are the chunks' Zt scaled by 1/Zt.
+    fallback = true;
+    __syncthreads();
+    for (int cc = tid; cc < nsch; cc += kThreads)
+      sh.u.draw.w[cc] = rt * unpack_f64(fetch(nw + cc * kNormWords), fetch(nw + cc * kNormWords + 1));
+    __syncthreads();
+    S = 0.0;
+    for (int g = 0; g < nsch; g += kThreads) {
+      const int cc = g + tid;
       double tot;
-      block_scan(w, tot, sh);
-      before += tot;
+      block_scan(cc < nsch ? sh.u.draw.w[cc] : 0.0, tot, sh);
+      S += tot;
     }
+  }
+  const double target_mass = double(P.sample_u[b]) * S;
+  // First chunk whose inclusive prefix exceeds target_mass.
+  double before = 0.0;
+  int chunk = -1, last_pos = -1;
+  for (int g = 0; g < nsch && chunk < 0; g += kThreads) {
+    const int cc = g + tid;
+    const double w = cc < nsch ? sh.u.draw.w[cc] : 0.0;
+    double tot;
+    const double incl = before + block_scan(w, tot, sh);
+    if (tid == 0) {
+      sh.pick[0] = INT_MAX;
+      sh.pick[1] = -1;
+    }
+    __syncthreads();
+    if (cc < nsch && incl > target_mass && w > 0.0) atomicMin(&sh.pick[0], cc);
+    if (cc < nsch && w > 0.0) atomicMax(&sh.pick[1], cc);
+    __syncthreads();
+    if (sh.pick[1] >= 0) last_pos = sh.pick[1];
+    if (sh.pick[0] != INT_MAX) chunk = sh.pick[0];
+    before += tot;
+    __syncthreads();
+  }
+  if (chunk < 0) chunk = max(last_pos, 0);  // rounding left u*S at or past the total
+  // Exclusive prefix of the chosen chunk, in the same group-scan order.
+  before = 0.0;
+  for (int g = 0; g < chunk; g += kThreads) {
+    const int cc = g + tid;
+    double tot;
+    block_scan(cc < chunk ? sh.u.draw.w[cc] : 0.0, tot, sh);
+    before += tot;
   }
   // Scan the chunk: thread t owns kSampPer consecutive tokens.
   const int e_base = chunk * kSampChunk + tid * kSampPer;
@@ -816,9 +951,15 @@ __device__ void draw2_item(const Params P, Shared& sh, int b) {
   double run = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampPer; ++k) {
-    double et, ed;
-    draw_exps(d, e_base + k, P.vocab, sh.exp_table, et, ed);
-    w[k] = fallback ? et * rt : draw_weight(d.residual, et, ed, rt, rd);
+    double at, ad;
+    draw_args(d, e_base + k, P.vocab, at, ad);
+    const double et = exp_nonpos(at, sh.exp_table);
+    if (!d.residual)
+      w[k] = et;
+    else if (fallback)
+      w[k] = et * rt;
+    else
+      w[k] = resid_weight(et, exp_nonpos(ad, sh.exp_table), rt, rd);
     run += w[k];
   }
   double tot;
@@ -840,7 +981,8 @@ __device__ void draw2_item(const Params P, Shared& sh, int b) {
   if (last >= 0) atomicMax(&sh.pick[1], e_base + last);
   __syncthreads();
   if (tid == 0) {
-    const int token = (sh.pick[0] != INT_MAX) ? sh.pick[0] : sh.pick[1];
+    int token = (sh.pick[0] != INT_MAX) ? sh.pick[0] : sh.pick[1];
+    if (token < 0) token = 0;
     P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = token;
   }
   __syncthreads();
@@ -849,28 +991,82 @@ __device__ void draw2_item(const Params P, Shared& sh, int b) {
 // ---------------------------------------------------------------------------
 // The persistent kernel.
 
+enum ItemKind : int { kNoItem = 0, kStat = 1, kDecide = 2, kNorm = 3, kDraw = 4 };
+
+struct Slot {
+  int kind;
+  int b;
+  int r;  // STAT row
+  int c;  // STAT or NORM chunk
+};
+
+__device__ __forceinline__ Slot slot_item(const Params P, long long s) {
+  Slot it{kNoItem, 0, 0, 0};
+  const int n_stat = (2 * P.n_draft + 1) * P.nch;
+  const int g = int(s / P.spg);
+  const int o = int(s - (long long)g * P.spg);
+  if (o < n_stat) {
+    if (g < P.batch) it = Slot{kStat, g, o / P.nch, o % P.nch};
+  } else if (o == n_stat) {
+    const int b = g - P.lag_decide;
+    if (b >= 0 && b < P.batch) it = Slot{kDecide, b, 0, 0};
+  } else if (o < n_stat + 1 + P.nsch) {
+    const int b = g - P.lag_norm;
+    if (b >= 0 && b < P.batch) it = Slot{kNorm, b, 0, o - n_stat - 1};
+  } else {
+    const int b = g - P.lag_draw;
+    if (b >= 0 && b < P.batch) it = Slot{kDraw, b, 0, 0};
+  }
+  return it;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads, 4) void verify_kernel(Params P) {
   __shared__ Shared sh;
   if (threadIdx.x < kExpTableSize) sh.exp_table[threadIdx.x] = P.exp_table[threadIdx.x];
   __syncthreads();
-  const int R = 2 * P.n_draft + 1;
-  const int n_stat = R * P.nch;
-  for (long long s = blockIdx.x; s < P.total_slots; s += gridDim.x) {
-    const int g = int(s / P.spg);
-    const int o = int(s - (long long)g * P.spg);
-    if (o < n_stat) {
-      if (g < P.batch) stat_item<T>(P, sh, g, o / P.nch, o % P.nch);
-    } else if (o == n_stat) {
-      const int b = g - P.lag_decide;
-      if (b >= 0 && b < P.batch) decide_item<T>(P, sh, b);
-    } else if (o < n_stat + 1 + P.nsch) {
-      const int b = g - P.lag_draw1;
-      if (b >= 0 && b < P.batch) draw1_item<T>(P, sh, b, o - n_stat - 1);
-    } else {
-      const int b = g - P.lag_draw2;
-      if (b >= 0 && b < P.batch) draw2_item<T>(P, sh, b);
+  long long s = blockIdx.x;
+  Slot it = slot_item(P, s);
+  // The temperature of the next STAT item is loaded one item ahead.
+  float t_next = (it.kind == kStat) ? P.temperature[it.b] : 0.0f;
+  for (; s < P.total_slots; s += gridDim.x) {
+    const Slot cur = it;
+    const float t_cur = t_next;
+    it = slot_item(P, s + gridDim.x);
+    if (s + gridDim.x < P.total_slots && it.kind == kStat) t_next = P.temperature[it.b];
+#ifdef SPECV_TRACE
+    const unsigned long long t_start = wall_clock64();
+    if (threadIdx.x == 0) {
+      sh.wait_ticks = 0;
+      sh.timeouts = 0;
     }
+#endif
+    switch (cur.kind) {
+      case kStat:
+        stat_item<T>(P, sh, cur.b, cur.r, cur.c, t_cur);
+        break;
+      case kDecide:
+        decide_item<T>(P, sh, cur.b);
+        break;
+      case kNorm:
+        norm_item<T>(P, sh, cur.b, cur.c);
+        break;
+      case kDraw:
+        draw_item<T>(P, sh, cur.b);
+        break;
+      default:
+        break;
+    }
+#ifdef SPECV_TRACE
+    __syncthreads();
+    if (threadIdx.x == 0 && cur.kind != kNoItem && s < P.trace_slots) {
+      unsigned long long* rec = P.trace + s * 4;
+      rec[0] = (unsigned long long)cur.kind | ((unsigned long long)blockIdx.x << 8);
+      rec[1] = t_start;
+      rec[2] = wall_clock64();
+      rec[3] = sh.wait_ticks | (sh.timeouts << 48);
+    }
+#endif
   }
 }
 
@@ -899,7 +1095,6 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, const LaunchCon
   P.stat_words = w.stat_words;
   P.seq_words = w.seq_words;
   P.norm_words = w.norm_words;
-  P.wsum_words = w.wsum_words;
   P.exp_table = w.exp_table;
   P.batch = a.batch;
   P.n_draft = a.n_draft;
@@ -909,13 +1104,17 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, const LaunchCon
   const int R = 2 * a.n_draft + 1;
   P.spg = R * P.nch + 1 + P.nsch + 1;
   P.lag_decide = cfg.lag_decide;
-  P.lag_draw1 = cfg.lag_draw1;
-  P.lag_draw2 = cfg.lag_draw2;
-  P.total_slots = (long long)(a.batch + cfg.lag_draw2) * P.spg;
+  P.lag_norm = cfg.lag_norm;
+  P.lag_draw = cfg.lag_draw;
+  P.total_slots = (long long)(a.batch + cfg.lag_draw) * P.spg;
   P.epoch = cfg.epoch;
   P.timeout_ticks = cfg.timeout_ticks;
+#ifdef SPECV_TRACE
+  P.trace = w.trace;
+  P.trace_slots = w.trace_slots;
+#endif
   // A grid size sharing a factor with the group size would give every
-  // workgroup the same item types (e.g. only DRAW2 items); keep them coprime.
+  // workgroup the same item types (e.g. only DRAW items); keep them coprime.
   long long grid = std::min<long long>(P.total_slots, cfg.max_blocks);
   while (grid > 1 && std::gcd(grid, (long long)P.spg) != 1) --grid;
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
@@ -938,6 +1137,9 @@ int max_blocks_per_cu(int dtype) {
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, verify_kernel<uint16_t>, kThreads, 0);
   return occ;
 }
+
+int norm_words_per_chunk() { return kNormWords; }
+int seq_words_per_sequence() { return kSeqWords; }
 
 hipError_t clear_words(uint64_t* p, long long n, hipStream_t stream) {
   hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, p, n);

@@ -48,6 +48,8 @@ def test_status_codes_match_header():
         assert int(m.group(1)) == getattr(_lib, name), name
     m = re.search(r"#define\s+SPECV_MAX_DRAFT\s+(\d+)", text)
     assert int(m.group(1)) == _lib.SPECV_MAX_DRAFT
+    m = re.search(r"#define\s+SPECV_MAX_VOCAB\s+(\d+)", text)
+    assert int(m.group(1)) == _lib.SPECV_MAX_VOCAB
 
 
 def test_strerror_covers_codes():
@@ -63,7 +65,7 @@ def test_argument_errors_before_any_device_call():
     lib = specv.load_library()
     h = ctypes.c_void_p()
     assert lib.specv_create(None, 1, 1, 16, 0, 0) == _lib.SPECV_EINVAL
-    for args in ((0, 4, 16, 0), (1, 0, 16, 0), (1, 65, 16, 0), (1, 4, 0, 0), (1, 4, (1 << 30) + 1, 0),
+    for args in ((0, 4, 16, 0), (1, 0, 16, 0), (1, 65, 16, 0), (1, 4, 0, 0), (1, 4, (1 << 22) + 1, 0),
                  (1, 4, 16, 2), (1, 4, 16, -1)):
         assert lib.specv_create(ctypes.byref(h), *args, 0) == _lib.SPECV_EINVAL, args
         assert h.value is None

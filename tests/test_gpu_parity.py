@@ -265,9 +265,9 @@ STRESS = [
     # every wait times out at once: each workgroup recomputes what it needs itself
     {"SPECV_WAIT_TIMEOUT_US": "0"},
     # one workgroup per CU, items with no lag: most waits are real
-    {"SPECV_BLOCKS_PER_CU": "1", "SPECV_LAG_DECIDE": "0", "SPECV_LAG_DRAW1": "0", "SPECV_LAG_DRAW2": "0"},
+    {"SPECV_BLOCKS_PER_CU": "1", "SPECV_LAG_DECIDE": "0", "SPECV_LAG_NORM": "0", "SPECV_LAG_DRAW": "0"},
     # long lags and a short timeout
-    {"SPECV_LAG_DECIDE": "16", "SPECV_LAG_DRAW1": "40", "SPECV_LAG_DRAW2": "64", "SPECV_WAIT_TIMEOUT_US": "3"},
+    {"SPECV_LAG_DECIDE": "16", "SPECV_LAG_NORM": "40", "SPECV_LAG_DRAW": "64", "SPECV_WAIT_TIMEOUT_US": "3"},
 ]
 
 
