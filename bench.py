@@ -183,7 +183,7 @@ def main() -> int:
     v.set_timing(False)
     stage_ms = {k: s / args.steps for k, s in sums.items()}
     dominant = max(stage_ms, key=stage_ms.get)
-    kernel_bytes = nbytes["total"] if dominant == "verify" else nbytes["stats"]
+    kernel_bytes = {"row_stats": nbytes["stats"]}.get(dominant, nbytes["reread"])
     achieved = kernel_bytes / (stage_ms[dominant] * 1e-3) / 1e9
     traffic = traffic_record(dominant, args.workload)
 

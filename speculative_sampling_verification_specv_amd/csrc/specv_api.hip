@@ -24,12 +24,10 @@ struct specv_ctx {
   specv::Workspace ws;
   int last_batch;  // -1 until a verify succeeds
   int last_n_draft;
-  unsigned epoch;               // epoch of the last launched call (0: none yet)
-  specv::LaunchConfig config;   // grid cap, item lags and wait timeout
-  bool timing;                                  // record stage events on every verify
-  bool timed_call;                              // the last verify recorded them
-  int timed_stages;                             // stages the last timed verify launched
-  hipEvent_t events[specv::kMaxStages + 1];     // created on first enable
+  bool timing;                               // record stage events on every verify
+  bool timed_call;                           // the last verify recorded them
+  int timed_stages;                          // stages the last timed verify launched
+  hipEvent_t events[specv::kMaxStages + 1];  // created on first enable
   bool events_created;
 };
 
@@ -57,35 +55,6 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-long env_long(const char* name, long fallback) {
-  const char* v = getenv(name);
-  if (v == nullptr || *v == 0) return fallback;
-  char* end = nullptr;
-  const long x = strtol(v, &end, 10);
-  return (end != nullptr && *end == 0) ? x : fallback;
-}
-
-// Grid cap, item lags and wait timeout. Defaults suit MI355X; the environment
-// variables SPECV_BLOCKS_PER_CU, SPECV_LAG_DECIDE, SPECV_LAG_NORM,
-// SPECV_LAG_DRAW (each at most 64) and SPECV_WAIT_TIMEOUT_US override them
-// (tuning and tests).
-bool init_config(specv_ctx* h) {
-  int cus = 0, clock_khz = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess) return false;
-  const int occ = specv::max_blocks_per_cu(h->dtype);
-  if (occ < 1) return false;
-  const long per_cu = std::max(1L, std::min<long>(occ, env_long("SPECV_BLOCKS_PER_CU", 3)));
-  h->config.max_blocks = static_cast<long long>(per_cu) * cus;
-  h->config.lag_decide = static_cast<int>(std::min(64L, std::max(0L, env_long("SPECV_LAG_DECIDE", 4))));
-  h->config.lag_norm = static_cast<int>(std::min(64L, std::max<long>(h->config.lag_decide, env_long("SPECV_LAG_NORM", 8))));
-  h->config.lag_draw = static_cast<int>(std::min(64L, std::max<long>(h->config.lag_norm, env_long("SPECV_LAG_DRAW", 12))));
-  const long timeout_us = std::max(0L, env_long("SPECV_WAIT_TIMEOUT_US", 200));
-  h->config.timeout_ticks = static_cast<unsigned long long>(timeout_us) * static_cast<unsigned long long>(clock_khz) / 1000ULL;
-  h->config.epoch = 0;
-  return true;
-}
-
 }  // namespace
 
 extern "C" {
@@ -112,16 +81,17 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
   if (device < 0 || device >= n_dev) return SPECV_EINVAL;
 
-  const int nch = specv::ceil_div(vocab, specv::kStatsChunk);
+  const int chunk = specv::stats_chunk_elems(dtype);
+  const int nch = specv::ceil_div(vocab, chunk);
   const int nsch = specv::ceil_div(vocab, specv::kSampChunk);
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
-  const size_t n_stat = rows * size_t(nch) * 2;
-  const size_t n_seq = size_t(max_batch) * specv::seq_words_per_sequence();
-  const size_t n_norm = size_t(max_batch) * size_t(nsch) * specv::norm_words_per_chunk();
-  const size_t n_words = n_stat + n_seq + n_norm;
   size_t off = 0;
-  const size_t off_words = off;
-  off = align_up(off + n_words * sizeof(uint64_t), 256);
+  const size_t off_partials = off;
+  off = align_up(off + rows * nch * sizeof(specv::RowPartial), 256);
+  const size_t off_seq = off;
+  off = align_up(off + size_t(max_batch) * sizeof(specv::SeqRecord), 256);
+  const size_t off_norm = off;
+  off = align_up(off + size_t(max_batch) * nsch * sizeof(specv::NormRecord), 256);
   const size_t off_table = off;
   off = align_up(off + specv::kExpTableSize * sizeof(double), 256);
   const size_t off_lse = off;
@@ -145,40 +115,22 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->vocab = vocab;
   h->dtype = dtype;
   h->mem_bytes = off;
-  uint64_t* words = reinterpret_cast<uint64_t*>(base + off_words);
-  h->ws.stat_words = words;
-  h->ws.seq_words = words + n_stat;
-  h->ws.norm_words = words + n_stat + n_seq;
-  h->ws.n_words = static_cast<long long>(n_words);
+  h->ws.partials = reinterpret_cast<specv::RowPartial*>(base + off_partials);
+  h->ws.seq = reinterpret_cast<specv::SeqRecord*>(base + off_seq);
+  h->ws.norm = reinterpret_cast<specv::NormRecord*>(base + off_norm);
   h->ws.exp_table = reinterpret_cast<double*>(base + off_table);
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
   h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
   h->ws.n_stats_chunks = nch;
   h->ws.n_samp_chunks = nsch;
+  h->ws.stats_chunk = chunk;
   double table[specv::kExpTableSize];
   for (int j = 0; j < specv::kExpTableSize; ++j) table[j] = double(exp2l((long double)j / specv::kExpTableSize));
-  if (hipMemset(words, 0, n_words * sizeof(uint64_t)) != hipSuccess ||
-      hipMemcpy(h->ws.exp_table, table, sizeof table, hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMemcpy(h->ws.exp_table, table, sizeof table, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(h->mem);
     delete h;
     return SPECV_EHIP;
   }
-#ifdef SPECV_TRACE
-  // Diagnostic builds: one 32-byte record per item slot of the largest call.
-  h->ws.trace_slots = (long long)(max_batch + 64) *
-                      ((2 * max_draft + 1) * nch + 1 + nsch + 1);
-  if (hipMalloc(&h->ws.trace, h->ws.trace_slots * 32) != hipSuccess) {
-    (void)hipFree(h->mem);
-    delete h;
-    return SPECV_ENOMEM;
-  }
-#endif
-  if (!init_config(h)) {
-    (void)hipFree(h->mem);
-    delete h;
-    return SPECV_EHIP;
-  }
-  h->epoch = 0;
   h->last_batch = -1;
   h->last_n_draft = 0;
   h->timing = false;
@@ -219,19 +171,10 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  unsigned epoch = h->epoch + 1;
-  if (epoch > specv::kMaxEpoch) {
-    // Epoch numbers are about to repeat: clear every tagged word first.
-    if (specv::clear_words(h->ws.stat_words, h->ws.n_words, st) != hipSuccess) return SPECV_EHIP;
-    epoch = 1;
-  }
-  specv::LaunchConfig cfg = h->config;
-  cfg.epoch = epoch;
   int stages = 0;
-  if (specv::launch_verify(a, h->ws, cfg, st, h->timing ? h->events : nullptr, &stages) != hipSuccess)
+  if (specv::launch_verify(a, h->ws, static_cast<hipStream_t>(stream), h->timing ? h->events : nullptr, &stages) !=
+      hipSuccess)
     return SPECV_EHIP;
-  h->epoch = epoch;
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;
@@ -286,19 +229,6 @@ int specv_last_timings(specv_handle h, float* ms, int capacity, int* count) {
 }
 
 const char* specv_stage_name(int stage) { return specv::stage_name(stage); }
-
-#ifdef SPECV_TRACE
-// Diagnostic builds only: copy the item records of the last call to host memory.
-SPECV_API int specv_debug_trace(specv_handle h, void* host, long long max_slots, long long* n_slots) {
-  if (h == nullptr || host == nullptr || n_slots == nullptr) return SPECV_EINVAL;
-  DeviceGuard guard(h->device);
-  if (hipDeviceSynchronize() != hipSuccess) return SPECV_EHIP;
-  const long long n = std::min(max_slots, h->ws.trace_slots);
-  if (hipMemcpy(host, h->ws.trace, n * 32, hipMemcpyDeviceToHost) != hipSuccess) return SPECV_EHIP;
-  *n_slots = n;
-  return SPECV_OK;
-}
-#endif
 
 void specv_destroy(specv_handle h) {
   if (h == nullptr) return;

@@ -1,4 +1,4 @@
-// gfx950 kernel for batched speculative-sampling verification: one persistent launch.
+// gfx950 kernels for batched speculative-sampling verification.
 //
 // Pages: lesson "추측 디코딩 — 초안 작성, 검증, 반복" (factory.pai-world.com),
 // section "핵심 알고리즘(Core algorithm)" steps 4-6 with "Step 1: 거절 단계" (the
@@ -6,49 +6,32 @@
 // (Speculative Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
 // verification loop.
 //
-// Work items, per sequence b (B sequences, N drafts, 2N+1 rows of V logits):
-//   STAT(b, r, c)  fp32 (max, sum 2^(z*c - K), first argmax) of 8192 logits of row r.
-//   DECIDE(b)      merge STAT partials into per-row log-normalisers, run the N
-//                  accept tests in fp64, find the first rejection j.
-//   NORM(b, c)     fp64 exp of 4096 logits of the row(s) the draw needs. After a
-//                  rejection: fp64 sums Zt, Zd of exp((z - max)/T) over target and
-//                  draft row j, and the sums A, B of the same over the tokens whose
-//                  residual weight is certainly positive, plus the indices of the
-//                  few tokens whose sign is uncertain (see below). For the bonus:
-//                  the sum of exp((z - max)/T) over target row N.
-//   DRAW(b)        chunk weights, inverse CDF over them, an fp64 rescan of the
-//                  crossing chunk, the token.
-// Items are laid out in slots, sequence-major, with DECIDE, NORM and DRAW of
-// sequence b placed a few sequences after STAT(b, ...); slot s belongs to
-// workgroup s mod G, so the draw's fp64 work overlaps later sequences' HBM
-// streaming.
+// Three launches per call, B sequences, N drafts, 2N+1 rows of V logits each:
+//   stat_kernel     one workgroup per (row, 32 KB chunk): fp32 max, sum of
+//                   2^(z*c - fl(max*c)) with c = log2(e)/T, first argmax.
+//                   Streaming and HBM-bound; greedy sequences skip draft rows.
+//   decide_norm     one workgroup per (sequence, 4096-logit draw chunk). Each
+//                   merges its sequence's row partials into log-normalisers and
+//                   runs the N accept tests in fp64 (the same deterministic
+//                   computation in every workgroup of the sequence; chunk 0
+//                   writes the outputs), then sums the fp64 exps of its chunk of
+//                   the row(s) the draw needs.
+//   draw_kernel     one workgroup per sequence: chunk weights, inverse CDF over
+//                   them, an fp64 rescan of the crossing chunk, the token.
 //
 // The residual weight of token x is w_x = max(0, et_x/Zt - ed_x/Zd)
 // = max(0, et_x - rho*ed_x)/Zt with rho = Zt/Zd, so its sign only depends on
-// whether log(et_x/ed_x) exceeds log(rho). DECIDE knows log(rho) from the fp32
-// row sums to ~1e-6; NORM treats tokens more than 1e-4 away from it as certain
-// and sums their exps into A and B, so that a chunk's weight is (A - rho*B)/Zt
-// plus the exact terms of its uncertain tokens. No chunk has to wait for the
-// global normalisers.
-//
-// Communication between workgroups uses no fences and no read-modify-write
-// atomics (both are very slow across this GPU's per-XCD L2 caches). Each result
-// travels in 64-bit words written and read with relaxed agent-scope atomics
-// (single-copy atomic, coherent across XCDs); every word carries the call's
-// 16-bit epoch, so a reader knows a word is from this call without any reset.
-// A reader polls until all the words it needs carry the epoch. If that takes
-// longer than a timeout (the producer's workgroup may not be resident), it
-// computes the missing items itself: every item is a deterministic function of
-// the inputs, so a duplicate write stores identical bits. Progress therefore
-// never depends on workgroups being co-resident.
+// whether log(et_x/ed_x) exceeds log(rho). The decision knows log(rho) from the
+// fp32 row sums to ~1e-6; a draw chunk treats tokens more than 1e-4 away from it
+// as certain and sums their exps into A and B, so the chunk's weight is
+// (A - rho*B)/Zt plus the exact terms of its few uncertain tokens. One pass over
+// the rows gives the normalisers and every chunk weight.
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
 #include <float.h>
 #include <limits.h>
 #include <math.h>
-
-#include <numeric>
 
 #include "specv_internal.h"
 #include "specv_math.h"
@@ -60,13 +43,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSampPer = kSampChunk / kThreads;  // logits per thread in a NORM item
+constexpr int kSampPer = kSampChunk / kThreads;  // logits per thread in a draw chunk
 constexpr int kMaxRows = 2 * 64 + 1;
-constexpr int kUncMax = 16;                      // uncertain tokens a NORM item records
-constexpr int kNormWords = 9 + kUncMax;          // Zt, Zd, A, B (2 words each), count, indices
-constexpr int kSeqWords = 4;
-constexpr double kSignBand = 1e-4;               // |log(et/ed) - log(rho)| below this is uncertain
-constexpr int kStageCap = 1024;                  // STAT partials DECIDE stages in LDS
+constexpr double kSignBand = 1e-4;  // |log(et/ed) - log(rho)| at or below this is uncertain
+constexpr int kStageCap = 1024;     // row partials the decision stages in LDS
 
 __device__ __forceinline__ bool temperature_valid(float t) {
   return t == 0.0f || (t >= kMinTemperature && t <= kFltMax);
@@ -111,144 +91,21 @@ struct Logit<uint16_t> {  // bfloat16 bits
   }
 };
 
-// ---------------------------------------------------------------------------
-// Epoch-tagged words.
-
-__device__ __forceinline__ void publish(uint64_t* p, uint64_t payload48, unsigned epoch) {
-  __hip_atomic_store(p, (payload48 << 16) | (epoch & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t fetch(uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool tagged(uint64_t w, unsigned epoch) { return (w & 0xffffu) == (epoch & 0xffffu); }
-__device__ __forceinline__ uint64_t payload(uint64_t w) { return w >> 16; }
-
-// STAT partial: (m, s, idx) in two words.
-__device__ __forceinline__ void publish_partial(uint64_t* w, float m, float s, int idx, unsigned epoch) {
-  const uint32_t mb = __float_as_uint(m), sb = __float_as_uint(s);
-  publish(w, (uint64_t(mb) << 16) | (sb >> 16), epoch);
-  publish(w + 1, (uint64_t(sb & 0xffffu) << 32) | uint32_t(idx), epoch);
-}
-__device__ __forceinline__ void unpack_partial(uint64_t w0, uint64_t w1, float& m, float& s, int& idx) {
-  const uint64_t p0 = payload(w0), p1 = payload(w1);
-  m = __uint_as_float(uint32_t(p0 >> 16));
-  s = __uint_as_float((uint32_t(p0 & 0xffffu) << 16) | uint32_t(p1 >> 32));
-  idx = int(uint32_t(p1 & 0xffffffffu));
-}
-
-// fp64 value in two words.
-__device__ __forceinline__ void publish_f64(uint64_t* w, double v, unsigned epoch) {
-  const uint64_t b = double_to_bits(v);
-  publish(w, b >> 32, epoch);
-  publish(w + 1, b & 0xffffffffu, epoch);
-}
-__device__ __forceinline__ double unpack_f64(uint64_t w0, uint64_t w1) {
-  return bits_to_double((payload(w0) << 32) | (payload(w1) & 0xffffffffu));
-}
-
-// What DECIDE leaves for the draw of one sequence.
-struct SeqInfo {
-  int mode;  // SeqMode
-  int j;
-  float m_target;  // largest logit of target row j
-  float m_draft;   // largest logit of draft row j (residual only)
-  double log_rho;  // log(Zt/Zd) from the fp32 row sums (residual only)
-};
-__device__ __forceinline__ void publish_seq(uint64_t* w, const SeqInfo& s, unsigned epoch) {
-  publish(w, (uint64_t(__float_as_uint(s.m_target)) << 16) | (uint64_t(s.j & 0xff) << 8) | uint64_t(s.mode & 0xff),
-          epoch);
-  publish(w + 1, uint64_t(__float_as_uint(s.m_draft)) << 16, epoch);
-  publish_f64(w + 2, s.log_rho, epoch);
-}
-__device__ __forceinline__ SeqInfo unpack_seq(uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3) {
-  SeqInfo s;
-  const uint64_t p0 = payload(w0);
-  s.m_target = __uint_as_float(uint32_t(p0 >> 16));
-  s.j = int((p0 >> 8) & 0xff);
-  s.mode = int(p0 & 0xff);
-  s.m_draft = __uint_as_float(uint32_t(payload(w1) >> 16));
-  s.log_rho = unpack_f64(w2, w3);
-  return s;
-}
-
-// ---------------------------------------------------------------------------
-// Kernel parameters and shared memory.
-
-struct Params {
-  const void* draft;
-  const void* target;
-  const int* tokens;
-  const float* accept_u;
-  const float* sample_u;
-  const float* temperature;
-  int* out_tokens;
-  int* out_n;
-  float* row_lse;
-  int* row_argmax;
-  uint64_t* stat_words;  // [B*R][nch][2]
-  uint64_t* seq_words;   // [B][kSeqWords]
-  uint64_t* norm_words;  // [B][nsch][kNormWords]
-  const double* exp_table;
-  int batch;
-  int n_draft;
-  int vocab;
-  int nch;
-  int nsch;
-  int spg;  // slots per group
-  long long total_slots;
-  int lag_decide;
-  int lag_norm;
-  int lag_draw;
-  unsigned epoch;
-  unsigned long long timeout_ticks;
-#ifdef SPECV_TRACE
-  unsigned long long* trace;  // [total_slots][4]: kind|block<<8, start, end, wait ticks|timeouts<<48
-  long long trace_slots;
-#endif
-};
-
-struct Shared {
-  double exp_table[kExpTableSize];
-  double red[kWaves * 2];
-  float row_m[kMaxRows];
-  double row_logz[kMaxRows];
-  int row_idx[kMaxRows];
-  int flag;
-  int pick[2];
-  int unc_base[kWaves];
-  // DECIDE stages STAT partials here; DRAW keeps chunk weights and flags here.
-  union {
-    struct {
-      float m[kStageCap];
-      float s[kStageCap];
-      int idx[kStageCap];
-    } part;
-    struct {
-      double w[kMaxSampChunks];
-      int dirty[kMaxSampChunks];
-    } draw;
-  } u;
-#ifdef SPECV_TRACE
-  unsigned long long wait_ticks;
-  unsigned long long timeouts;
-#endif
-};
-
-__device__ __forceinline__ double block_sum(double v, Shared& sh) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  double total = sh.red[0];
+  double total = red[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) total += sh.red[w];
+  for (int w = 1; w < kWaves; ++w) total += red[w];
   return total;
 }
 
 // Block-wide inclusive scan of one double per thread (fixed order); returns
 // the thread's inclusive prefix and sets total.
-__device__ __forceinline__ double block_scan(double v, double& total, Shared& sh) {
+__device__ __forceinline__ double block_scan(double v, double& total, double* red) {
   const int lane = threadIdx.x & 63;
   double incl = v;
 #pragma unroll
@@ -257,65 +114,25 @@ __device__ __forceinline__ double block_scan(double v, double& total, Shared& sh
     if (lane >= off) incl += up;
   }
   __syncthreads();
-  if (lane == 63) sh.red[threadIdx.x >> 6] = incl;
+  if (lane == 63) red[threadIdx.x >> 6] = incl;
   __syncthreads();
   double before = 0.0;
   total = 0.0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    if (w < (int(threadIdx.x) >> 6)) before += sh.red[w];
-    total += sh.red[w];
+    if (w < (int(threadIdx.x) >> 6)) before += red[w];
+    total += red[w];
   }
   return before + incl;
 }
 
-__device__ __forceinline__ void note_wait(Shared& sh, unsigned long long t0, bool timed_out) {
-#ifdef SPECV_TRACE
-  if (threadIdx.x == 0) {
-    sh.wait_ticks += wall_clock64() - t0;
-    sh.timeouts += timed_out ? 1 : 0;
-  }
-#endif
-}
-
-// True (in every thread) once all n words carry the epoch; false on timeout.
-__device__ bool block_wait(uint64_t* words, int n, const Params P, Shared& sh) {
-  const unsigned long long t0 = wall_clock64();
-  while (true) {
-    bool ok = true;
-    for (int i = threadIdx.x; i < n; i += kThreads) ok = ok && tagged(fetch(words + i), P.epoch);
-    if (__syncthreads_and(ok)) {
-      note_wait(sh, t0, false);
-      return true;
-    }
-    const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
-    if (__syncthreads_or(expired)) {
-      note_wait(sh, t0, true);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
-// True (in every thread) if the k words at p all carry the epoch.
-__device__ bool block_has(uint64_t* p, int k, const Params P, Shared& sh) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    bool ok = true;
-    for (int i = 0; i < k; ++i) ok = ok && tagged(fetch(p + i), P.epoch);
-    sh.flag = ok;
-  }
-  __syncthreads();
-  return sh.flag != 0;
-}
-
 // ---------------------------------------------------------------------------
-// STAT: fp32 row statistics of one chunk.
+// Row statistics.
 
 // Running state: m = largest logit seen, idx = its first index, s = sum of
 // 2^(z*c - k) with k = fl(m*c) once a finite logit was seen (0 before, while
 // s is 0 too). The exact product m*c differs from k by r = fma(m, c, -k); the
-// decision step removes it.
+// decision removes it.
 struct StatAcc {
   float m;
   float k;
@@ -394,7 +211,7 @@ __device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t r
   }
   // A chunk holds at most kMaxVec 16-byte vectors per thread: issue all loads
   // before any use so they are in flight together.
-  constexpr int kMaxVec = kStatsChunk / kVec / kThreads;
+  constexpr int kMaxVec = kStatsChunkBytes / 16 / kThreads;
   const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row + ea);
   uint4 x[kMaxVec];
 #pragma unroll
@@ -419,7 +236,9 @@ __device__ __forceinline__ void stats_chunk(const T* __restrict__ row, int64_t r
 }
 
 template <bool kSampled>
-__device__ __forceinline__ void block_merge(StatAcc& a, float c, Shared& sh) {
+__device__ __forceinline__ void block_merge(StatAcc& a, float c) {
+  __shared__ float sm[kWaves], ss[kWaves];
+  __shared__ int si[kWaves];
   float m = a.m, s = a.s;
   int idx = a.idx;
 #pragma unroll
@@ -429,10 +248,6 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c, Shared& sh) {
     const int i2 = __shfl_xor(idx, off);
     acc_merge<kSampled>(m, s, idx, m2, s2, i2, c);
   }
-  float* sm = reinterpret_cast<float*>(sh.red);  // 4 floats m, 4 floats s, 4 ints idx fit in red[8]
-  float* ss = sm + kWaves;
-  int* si = reinterpret_cast<int*>(ss + kWaves);
-  __syncthreads();
   if ((threadIdx.x & 63) == 0) {
     sm[threadIdx.x >> 6] = m;
     ss[threadIdx.x >> 6] = s;
@@ -450,90 +265,136 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c, Shared& sh) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ const T* row_ptr(const Params P, int b, int r, int64_t& row_flat) {
-  const int N = P.n_draft;
-  if (r < N) {
-    row_flat = (int64_t(b) * N + r) * P.vocab;
-    return static_cast<const T*>(P.draft) + row_flat;
-  }
-  row_flat = (int64_t(b) * (N + 1) + (r - N)) * P.vocab;
-  return static_cast<const T*>(P.target) + row_flat;
-}
+struct StatParams {
+  const void* draft;
+  const void* target;
+  const float* temperature;
+  RowPartial* partials;
+  int n_draft;
+  int vocab;
+  int nch;
+  int chunk;
+};
 
-// Computes and publishes STAT(b, r, chunk); t is sequence b's temperature.
-// Skips rows the sequence never needs.
+// One workgroup per (row, chunk) item: item = (b*(2N+1) + r)*nch + c. Rows a
+// sequence never needs (draft rows at T = 0, every row of an invalid
+// temperature) are skipped; their partials are never read.
 template <typename T>
-__device__ void stat_item(const Params P, Shared& sh, int b, int r, int chunk, float t) {
+__global__ __launch_bounds__(kThreads) void stat_kernel(StatParams P) {
+  const int R = 2 * P.n_draft + 1;
+  const int item = blockIdx.x;
+  const int row = item / P.nch;
+  const int chunk = item - row * P.nch;
+  const int b = row / R;
+  const int r = row - b * R;
+  const float t = P.temperature[b];
   if (!temperature_valid(t)) return;
   const bool greedy = (t == 0.0f);
   if (greedy && r < P.n_draft) return;
-  int64_t row_flat;
-  const T* rowp = row_ptr<T>(P, b, r, row_flat);
-  const int e0 = chunk * kStatsChunk;
-  const int e1 = min(P.vocab, e0 + kStatsChunk);
+  const int N = P.n_draft;
+  const int64_t row_flat = (r < N) ? (int64_t(b) * N + r) * P.vocab : (int64_t(b) * (N + 1) + (r - N)) * P.vocab;
+  const T* rowp = static_cast<const T*>(r < N ? P.draft : P.target) + row_flat;
+  const int e0 = chunk * P.chunk;
+  const int e1 = min(P.vocab, e0 + P.chunk);
   StatAcc a;
   acc_init(a);
   if (greedy) {
     stats_chunk<T, false>(rowp, row_flat, e0, e1, 0.0f, a);
-    block_merge<false>(a, 0.0f, sh);
+    block_merge<false>(a, 0.0f);
   } else {
     const float c = exp2_coef(t);
     stats_chunk<T, true>(rowp, row_flat, e0, e1, c, a);
-    block_merge<true>(a, c, sh);
+    block_merge<true>(a, c);
   }
   if (threadIdx.x == 0) {
-    const int R = 2 * P.n_draft + 1;
-    publish_partial(P.stat_words + ((int64_t(b) * R + r) * P.nch + chunk) * 2, a.m, a.s, a.idx, P.epoch);
+    RowPartial p;
+    p.m = a.m;
+    p.s = a.s;
+    p.idx = a.idx;
+    p.pad = 0;
+    P.partials[item] = p;
   }
 }
 
 // ---------------------------------------------------------------------------
-// DECIDE: log-normalisers, accept tests, first rejection, outputs.
+// Decision and draw chunks.
 
-// Waits for (or computes) the STAT partials of rows [r0, R); when they fit,
-// leaves them unpacked in shared memory (returns true).
+struct DrawParams {
+  const void* draft;
+  const void* target;
+  const int* tokens;
+  const float* accept_u;
+  const float* sample_u;
+  const float* temperature;
+  int* out_tokens;
+  int* out_n;
+  float* row_lse;
+  int* row_argmax;
+  const RowPartial* partials;
+  SeqRecord* seq;
+  NormRecord* norm;
+  const double* exp_table;
+  int n_draft;
+  int vocab;
+  int nch;
+  int nsch;
+};
+
 template <typename T>
-__device__ bool gather_stats(const Params P, Shared& sh, int b, int r0, float t) {
-  const int R = 2 * P.n_draft + 1;
-  const int n_part = (R - r0) * P.nch;
-  uint64_t* base = P.stat_words + (int64_t(b) * R + r0) * P.nch * 2;
-  const bool staged = n_part <= kStageCap;
-  const unsigned long long t0 = wall_clock64();
-  bool waited_out = false;
-  while (true) {
-    bool ok = true;
-    for (int i = threadIdx.x; i < n_part; i += kThreads) {
-      const uint64_t w0 = fetch(base + 2 * i), w1 = fetch(base + 2 * i + 1);
-      ok = ok && tagged(w0, P.epoch) && tagged(w1, P.epoch);
-      if (staged) unpack_partial(w0, w1, sh.u.part.m[i], sh.u.part.s[i], sh.u.part.idx[i]);
-    }
-    if (__syncthreads_and(ok)) break;
-    const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
-    if (__syncthreads_or(expired)) {
-      waited_out = true;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  note_wait(sh, t0, waited_out);
-  if (waited_out) {
-    for (int r = r0; r < R; ++r)
-      for (int c = 0; c < P.nch; ++c)
-        if (!block_has(P.stat_words + ((int64_t(b) * R + r) * P.nch + c) * 2, 2, P, sh)) stat_item<T>(P, sh, b, r, c, t);
-    __syncthreads();
-    if (staged) {
-      for (int i = threadIdx.x; i < n_part; i += kThreads)
-        unpack_partial(fetch(base + 2 * i), fetch(base + 2 * i + 1), sh.u.part.m[i], sh.u.part.s[i],
-                       sh.u.part.idx[i]);
-    }
-  }
-  __syncthreads();
-  return staged;
+struct DrawRows {
+  const T* trow;
+  const T* drow;
+  double mt, md, inv_t;
+  bool residual;
+};
+
+template <typename T>
+__device__ __forceinline__ DrawRows<T> draw_rows(const DrawParams& P, int b, const SeqRecord& s, float t) {
+  const int N = P.n_draft;
+  DrawRows<T> d;
+  d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
+  d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
+  d.mt = s.m_target;
+  d.md = s.m_draft;
+  d.inv_t = 1.0 / double(t);
+  d.residual = (s.mode == kModeResidual);
+  return d;
 }
 
+// Arguments (z - max)/T of token e's exps; -inf past the row end.
 template <typename T>
-__device__ void decide_item(const Params P, Shared& sh, int b) {
+__device__ __forceinline__ void draw_args(const DrawRows<T>& d, int e, int vocab, double& at, double& ad) {
+  at = -INFINITY;
+  ad = -INFINITY;
+  if (e < vocab) {
+    at = (double(Logit<T>::at(d.trow, e)) - d.mt) * d.inv_t;
+    if (d.residual) ad = (double(Logit<T>::at(d.drow, e)) - d.md) * d.inv_t;
+  }
+}
+
+// Residual weight of a token from its exps and the reciprocal normalisers.
+__device__ __forceinline__ double resid_weight(double et, double ed, double rt, double rd) {
+  return fmax(0.0, et * rt - ed * rd);
+}
+
+struct DecideShared {
+  double exp_table[kExpTableSize];
+  double red[kWaves];
+  float row_m[kMaxRows];
+  double row_logz[kMaxRows];
+  int row_idx[kMaxRows];
+  int unc_base[kWaves];
+  float part_m[kStageCap];
+  float part_s[kStageCap];
+  int part_idx[kStageCap];
+};
+
+// The decision for sequence b, computed identically by every workgroup that
+// asks: per-row log-normalisers and argmaxes from the row partials, the N
+// accept tests, the first rejection. The workgroup with `write` set also
+// writes the outputs, the row diagnostics and the sequence record.
+template <typename T>
+__device__ SeqRecord decide(const DrawParams& P, DecideShared& sh, int b, float t, bool write) {
   const int N = P.n_draft;
   const int R = 2 * N + 1;
   const int tid = threadIdx.x;
@@ -543,12 +404,10 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   float* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  uint64_t* seqw = P.seq_words + int64_t(b) * kSeqWords;
+  SeqRecord rec{kModeNone, 0, 0.0f, 0.0f, 0.0, 0.0};
 
-  // Issue the inputs of the accept tests before waiting for the row sums.
-  const float t = P.temperature[b];
   int d = 0;
-  float zt = 0.0f, zd = 0.0f, ua = 0.0f;
+  float ua = 0.0f;
   bool bad = !temperature_valid(t);
   if (tid < N) {
     d = tok[tid];
@@ -556,39 +415,44 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
     ua = P.accept_u[int64_t(b) * N + tid];
   }
   if (__syncthreads_or(bad)) {
-    for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
-    for (int r = tid; r < R; r += kThreads) {
-      lse[r] = NAN;
-      amax[r] = -1;
+    if (write) {
+      for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
+      for (int r = tid; r < R; r += kThreads) {
+        lse[r] = NAN;
+        amax[r] = -1;
+      }
+      if (tid == 0) {
+        P.out_n[b] = -1;
+        P.seq[b] = rec;
+      }
     }
-    if (tid == 0) {
-      P.out_n[b] = -1;
-      SeqInfo s{kModeNone, 0, 0.0f, 0.0f, 0.0};
-      publish_seq(seqw, s, P.epoch);
-    }
-    return;
+    return rec;
   }
   const bool greedy = (t == 0.0f);
+  float zt = 0.0f, zd = 0.0f;
   if (tid < N && !greedy) {
     zt = Logit<T>::at(static_cast<const T*>(P.target), (int64_t(b) * (N + 1) + tid) * P.vocab + d);
     zd = Logit<T>::at(static_cast<const T*>(P.draft), (int64_t(b) * N + tid) * P.vocab + d);
   }
   const int r_first = greedy ? N : 0;
-  const bool staged = gather_stats<T>(P, sh, b, r_first, t);
+  const int n_part = (R - r_first) * P.nch;
+  const RowPartial* parts = P.partials + (int64_t(b) * R + r_first) * P.nch;
+  const bool staged = n_part <= kStageCap;
+  if (staged) {
+    for (int i = tid; i < n_part; i += kThreads) {
+      const RowPartial p = parts[i];
+      sh.part_m[i] = p.m;
+      sh.part_s[i] = p.s;
+      sh.part_idx[i] = p.idx;
+    }
+    __syncthreads();
+  }
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
 
   // Merge each row's chunk partials: lanes take chunks lane, lane+64, ...,
   // then a butterfly; waves take rows wave, wave+4, ...
-  for (int r = wave; r < R; r += kWaves) {
-    if (r < r_first) {
-      if (lane == 0) {
-        lse[r] = NAN;
-        amax[r] = -1;
-      }
-      continue;
-    }
-    uint64_t* rw = P.stat_words + (int64_t(b) * R + r) * P.nch * 2;
+  for (int r = r_first + wave; r < R; r += kWaves) {
     const int pbase = (r - r_first) * P.nch;
     float m = -INFINITY, s = 0.0f;
     int idx = INT_MAX;
@@ -596,11 +460,14 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
       float m2, s2;
       int i2;
       if (staged) {
-        m2 = sh.u.part.m[pbase + k];
-        s2 = sh.u.part.s[pbase + k];
-        i2 = sh.u.part.idx[pbase + k];
+        m2 = sh.part_m[pbase + k];
+        s2 = sh.part_s[pbase + k];
+        i2 = sh.part_idx[pbase + k];
       } else {
-        unpack_partial(fetch(rw + 2 * k), fetch(rw + 2 * k + 1), m2, s2, i2);
+        const RowPartial p = parts[pbase + k];
+        m2 = p.m;
+        s2 = p.s;
+        i2 = p.idx;
       }
       if (greedy)
         acc_merge<false>(m, s, idx, m2, s2, i2, c);
@@ -624,30 +491,48 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
       sh.row_m[r] = m;
       sh.row_logz[r] = logz;
       sh.row_idx[r] = idx;
-      lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
-      amax[r] = idx;
+      if (write) {
+        lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
+        amax[r] = idx;
+      }
+    }
+  }
+  if (write && greedy) {
+    for (int r = tid; r < N; r += kThreads) {
+      lse[r] = NAN;
+      amax[r] = -1;
     }
   }
   __syncthreads();
 
-  if (wave == 0) {
-    bool accept = true;
-    if (lane < N) {
-      if (greedy) {
-        accept = (d == sh.row_idx[N + lane]);
-      } else if (zd == -INFINITY) {
-        accept = true;  // p(d) == 0: the ratio is infinite
-      } else {
-        const double log_q = (double(zt) - double(sh.row_m[N + lane])) * inv_t - sh.row_logz[N + lane];
-        const double log_p = (double(zd) - double(sh.row_m[lane])) * inv_t - sh.row_logz[lane];
-        accept = double(ua) < exp(log_q - log_p);
-      }
+  bool accept = true;
+  if (tid < N) {
+    if (greedy) {
+      accept = (d == sh.row_idx[N + tid]);
+    } else if (zd == -INFINITY) {
+      accept = true;  // p(d) == 0: the ratio is infinite
+    } else {
+      const double log_q = (double(zt) - double(sh.row_m[N + tid])) * inv_t - sh.row_logz[N + tid];
+      const double log_p = (double(zd) - double(sh.row_m[tid])) * inv_t - sh.row_logz[tid];
+      accept = double(ua) < exp(log_q - log_p);
     }
-    const unsigned long long rej = __ballot(lane < N && !accept);
-    const int j = rej ? (__ffsll(rej) - 1) : N;
-    // Position j of a sampled sequence is left to DRAW: a duplicate DECIDE
-    // running after it must not overwrite the drawn token.
-    for (int i = lane; i <= N; i += 64) {
+  }
+  // N <= 64: every decision lives in wave 0.
+  __shared__ unsigned long long rej_mask;
+  if (wave == 0) {
+    const unsigned long long rej = __ballot(tid < N && !accept);
+    if (lane == 0) rej_mask = rej;
+  }
+  __syncthreads();
+  const unsigned long long rej = rej_mask;
+  const int j = rej ? (__ffsll(rej) - 1) : N;
+  rec.mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
+  rec.j = j;
+  rec.m_target = sh.row_m[N + j];
+  rec.m_draft = (j < N && !greedy) ? sh.row_m[j] : 0.0f;
+  rec.log_rho = (j < N && !greedy) ? sh.row_logz[N + j] - sh.row_logz[j] : 0.0;
+  if (write) {
+    for (int i = tid; i <= N; i += kThreads) {
       if (i < j)
         otok[i] = tok[i];
       else if (i > j)
@@ -655,74 +540,22 @@ __device__ void decide_item(const Params P, Shared& sh, int b) {
       else if (greedy)
         otok[i] = sh.row_idx[N + j];
     }
-    if (lane == 0) {
+    if (tid == 0) {
       P.out_n[b] = j;
-      SeqInfo s;
-      s.mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
-      s.j = j;
-      s.m_target = sh.row_m[N + j];
-      s.m_draft = (j < N && !greedy) ? sh.row_m[j] : 0.0f;
-      s.log_rho = (j < N && !greedy) ? sh.row_logz[N + j] - sh.row_logz[j] : 0.0;
-      publish_seq(seqw, s, P.epoch);
+      P.seq[b] = rec;
     }
   }
   __syncthreads();
+  return rec;
 }
 
+// fp64 sums of one draw chunk (see NormRecord).
 template <typename T>
-__device__ SeqInfo ensure_decided(const Params P, Shared& sh, int b) {
-  uint64_t* w = P.seq_words + int64_t(b) * kSeqWords;
-  if (!block_wait(w, kSeqWords, P, sh)) decide_item<T>(P, sh, b);
-  return unpack_seq(fetch(w), fetch(w + 1), fetch(w + 2), fetch(w + 3));
-}
-
-// ---------------------------------------------------------------------------
-// Draw: fp64 exps, chunk sums, inverse CDF.
-
-template <typename T>
-struct DrawRows {
-  const T* trow;
-  const T* drow;
-  double mt, md, inv_t;
-  bool residual;
-};
-
-template <typename T>
-__device__ __forceinline__ DrawRows<T> draw_rows(const Params P, int b, const SeqInfo& s) {
-  const int N = P.n_draft;
-  DrawRows<T> d;
-  d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
-  d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
-  d.mt = s.m_target;
-  d.md = s.m_draft;
-  d.inv_t = 1.0 / double(P.temperature[b]);
-  d.residual = (s.mode == kModeResidual);
-  return d;
-}
-
-// Arguments (z - max)/T of token e's exps; -inf past the row end.
-template <typename T>
-__device__ __forceinline__ void draw_args(const DrawRows<T>& d, int e, int vocab, double& at, double& ad) {
-  at = -INFINITY;
-  ad = -INFINITY;
-  if (e < vocab) {
-    at = (double(Logit<T>::at(d.trow, e)) - d.mt) * d.inv_t;
-    if (d.residual) ad = (double(Logit<T>::at(d.drow, e)) - d.md) * d.inv_t;
-  }
-}
-
-// Residual weight of a token from its exps and the reciprocal normalisers.
-__device__ __forceinline__ double resid_weight(double et, double ed, double rt, double rd) {
-  return fmax(0.0, et * rt - ed * rd);
-}
-
-// NORM(b, c): publishes Zt, Zd, A, B and the uncertain tokens of one chunk
-// (bonus: only Zt, the chunk's weight).
-template <typename T>
-__device__ void norm_compute(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d, double log_rho) {
+__device__ void norm_chunk(const DrawParams& P, DecideShared& sh, int b, int c, const DrawRows<T>& d,
+                           double log_rho) {
   const int tid = threadIdx.x;
   double zt = 0.0, zd = 0.0, sa = 0.0, sb = 0.0;
-  uint32_t unc = 0;  // bit k: token c*kSampChunk + tid + k*kThreads is uncertain
+  uint32_t unc = 0;  // bit k: token c*kSampChunk + tid + k*kThreads has an uncertain sign
 #pragma unroll
   for (int k = 0; k < kSampPer; ++k) {
     double at, ad;
@@ -743,16 +576,15 @@ __device__ void norm_compute(const Params P, Shared& sh, int b, int c, const Dra
       }
     }
   }
-  zt = block_sum(zt, sh);
-  uint64_t* w = P.norm_words + (int64_t(b) * P.nsch + c) * kNormWords;
+  NormRecord* out = P.norm + int64_t(b) * P.nsch + c;
+  zt = block_sum(zt, sh.red);
   if (!d.residual) {
-    if (tid == 0) publish_f64(w, zt, P.epoch);
-    __syncthreads();
+    if (tid == 0) out->zt = zt;
     return;
   }
-  zd = block_sum(zd, sh);
-  sa = block_sum(sa, sh);
-  sb = block_sum(sb, sh);
+  zd = block_sum(zd, sh.red);
+  sa = block_sum(sa, sh.red);
+  sb = block_sum(sb, sh.red);
   // Uncertain tokens, listed in (thread, k) order.
   const int cnt = __popc(unc);
   int incl = cnt;
@@ -762,7 +594,6 @@ __device__ void norm_compute(const Params P, Shared& sh, int b, int c, const Dra
     const int up = __shfl_up(incl, off);
     if (lane >= off) incl += up;
   }
-  __syncthreads();
   if (lane == 63) sh.unc_base[tid >> 6] = incl;
   __syncthreads();
   int slot = incl - cnt, total = 0;
@@ -774,31 +605,43 @@ __device__ void norm_compute(const Params P, Shared& sh, int b, int c, const Dra
   if (total <= kUncMax) {
 #pragma unroll
     for (int k = 0; k < kSampPer; ++k)
-      if (unc & (1u << k)) publish(w + 9 + slot++, uint64_t(c * kSampChunk + tid + k * kThreads), P.epoch);
+      if (unc & (1u << k)) out->idx[slot++] = c * kSampChunk + tid + k * kThreads;
   }
   if (tid == 0) {
-    publish_f64(w, zt, P.epoch);
-    publish_f64(w + 2, zd, P.epoch);
-    publish_f64(w + 4, sa, P.epoch);
-    publish_f64(w + 6, sb, P.epoch);
-    publish(w + 8, uint64_t(total), P.epoch);
-    // Unused index words still need the epoch: a reader waits on all of them.
-    for (int k = min(total, kUncMax); k < kUncMax; ++k) publish(w + 9 + k, 0, P.epoch);
+    out->zt = zt;
+    out->zd = zd;
+    out->a = sa;
+    out->b = sb;
+    out->n_unc = total;
   }
-  __syncthreads();
 }
 
+// One workgroup per (sequence, draw chunk): the decision, then the chunk sums.
 template <typename T>
-__device__ void norm_item(const Params P, Shared& sh, int b, int c) {
-  const SeqInfo s = ensure_decided<T>(P, sh, b);
+__global__ __launch_bounds__(kThreads) void decide_norm_kernel(DrawParams P) {
+  __shared__ DecideShared sh;
+  const int b = blockIdx.x / P.nsch;
+  const int c = blockIdx.x - b * P.nsch;
+  if (threadIdx.x < kExpTableSize) sh.exp_table[threadIdx.x] = P.exp_table[threadIdx.x];
+  const float t = P.temperature[b];
+  const SeqRecord s = decide<T>(P, sh, b, t, c == 0);
   if (s.mode == kModeNone) return;
-  norm_compute<T>(P, sh, b, c, draw_rows<T>(P, b, s), s.log_rho);
+  norm_chunk<T>(P, sh, b, c, draw_rows<T>(P, b, s, t), s.log_rho);
 }
+
+struct DrawShared {
+  double exp_table[kExpTableSize];
+  double red[kWaves];
+  double w[kMaxSampChunks];
+  int dirty[kMaxSampChunks];
+  int pick[2];
+};
 
 // Weight sum of one chunk from its logits (after a rejection): used for
-// chunks with too many uncertain tokens.
+// chunks with more uncertain tokens than their record holds.
 template <typename T>
-__device__ double chunk_weight(const Params P, Shared& sh, int c, const DrawRows<T>& d, double rt, double rd) {
+__device__ double chunk_weight(const DrawParams& P, DrawShared& sh, int c, const DrawRows<T>& d, double rt,
+                               double rd) {
   double w = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampPer; ++k) {
@@ -806,86 +649,71 @@ __device__ double chunk_weight(const Params P, Shared& sh, int c, const DrawRows
     draw_args(d, c * kSampChunk + threadIdx.x + k * kThreads, P.vocab, at, ad);
     w += resid_weight(exp_nonpos(at, sh.exp_table), exp_nonpos(ad, sh.exp_table), rt, rd);
   }
-  return block_sum(w, sh);
+  return block_sum(w, sh.red);
 }
 
-// DRAW(b): chunk weights, the crossing chunk, an fp64 scan of it.
+// One workgroup per sequence: chunk weights, the crossing chunk, an fp64 scan of it.
 template <typename T>
-__device__ void draw_item(const Params P, Shared& sh, int b) {
-  const SeqInfo s = ensure_decided<T>(P, sh, b);
-  if (s.mode == kModeNone) return;
-  DrawRows<T> d = draw_rows<T>(P, b, s);
+__global__ __launch_bounds__(kThreads) void draw_kernel(DrawParams P) {
+  __shared__ DrawShared sh;
+  const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int nsch = P.nsch;
-  uint64_t* nw = P.norm_words + int64_t(b) * nsch * kNormWords;
-  const int words_per_chunk = d.residual ? kNormWords : 2;
-  // Wait for every chunk's NORM words (bonus: the first two of each chunk).
-  {
-    const unsigned long long t0 = wall_clock64();
-    bool waited_out = false;
-    while (true) {
-      bool ok = true;
-      for (int i = tid; i < nsch * words_per_chunk; i += kThreads) {
-        const int cc = i / words_per_chunk, k = i - cc * words_per_chunk;
-        ok = ok && tagged(fetch(nw + cc * kNormWords + k), P.epoch);
-      }
-      if (__syncthreads_and(ok)) break;
-      const bool expired = (wall_clock64() - t0) > P.timeout_ticks;
-      if (__syncthreads_or(expired)) {
-        waited_out = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    note_wait(sh, t0, waited_out);
-    if (waited_out) {
-      for (int cc = 0; cc < nsch; ++cc)
-        if (!block_has(nw + cc * kNormWords, words_per_chunk, P, sh)) norm_compute<T>(P, sh, b, cc, d, s.log_rho);
-      __syncthreads();
-    }
-  }
+  if (tid < kExpTableSize) sh.exp_table[tid] = P.exp_table[tid];
+  const SeqRecord s = P.seq[b];
+  if (s.mode == kModeNone) return;
+  const float t = P.temperature[b];
+  const DrawRows<T> d = draw_rows<T>(P, b, s, t);
+  const NormRecord* nr = P.norm + int64_t(b) * nsch;
+  __syncthreads();
+
   // Normalisers (fixed order) and the chunk weights.
   double rt = 0.0, rd = 0.0, rho = 0.0;
   if (d.residual) {
     double zt = 0.0, zd = 0.0;
     for (int cc = tid; cc < nsch; cc += kThreads) {
-      zt += unpack_f64(fetch(nw + cc * kNormWords), fetch(nw + cc * kNormWords + 1));
-      zd += unpack_f64(fetch(nw + cc * kNormWords + 2), fetch(nw + cc * kNormWords + 3));
+      zt += nr[cc].zt;
+      zd += nr[cc].zd;
     }
-    zt = block_sum(zt, sh);
-    zd = block_sum(zd, sh);
+    zt = block_sum(zt, sh.red);
+    zd = block_sum(zd, sh.red);
     rt = 1.0 / zt;
     rd = 1.0 / zd;
     rho = zt * rd;
   }
   for (int cc = tid; cc < nsch; cc += kThreads) {
-    uint64_t* w = nw + cc * kNormWords;
-    double wc = unpack_f64(fetch(w), fetch(w + 1));
+    double wc;
     int dirty = 0;
-    if (d.residual) {
-      const double sa = unpack_f64(fetch(w + 4), fetch(w + 5));
-      const double sb = unpack_f64(fetch(w + 6), fetch(w + 7));
-      const int nu = int(payload(fetch(w + 8)));
-      wc = rt * (sa - rho * sb);
+    if (!d.residual) {
+      wc = nr[cc].zt;
+    } else {
+      wc = rt * (nr[cc].a - rho * nr[cc].b);
+      const int nu = nr[cc].n_unc;
       if (nu > kUncMax) {
         dirty = 1;
       } else {
-        for (int k = 0; k < nu; ++k) {
-          const int e = int(payload(fetch(w + 9 + k)));
-          double at, ad;
-          draw_args(d, e, P.vocab, at, ad);
-          wc += resid_weight(exp_nonpos(at, sh.exp_table), exp_nonpos(ad, sh.exp_table), rt, rd);
+        double extra[kUncMax];
+#pragma unroll
+        for (int k = 0; k < kUncMax; ++k) {
+          extra[k] = 0.0;
+          if (k < nu) {
+            double at, ad;
+            draw_args(d, nr[cc].idx[k], P.vocab, at, ad);
+            extra[k] = resid_weight(exp_nonpos(at, sh.exp_table), exp_nonpos(ad, sh.exp_table), rt, rd);
+          }
         }
+#pragma unroll
+        for (int k = 0; k < kUncMax; ++k) wc += extra[k];
       }
     }
-    sh.u.draw.w[cc] = wc;
-    sh.u.draw.dirty[cc] = dirty;
+    sh.w[cc] = wc;
+    sh.dirty[cc] = dirty;
   }
   __syncthreads();
   for (int cc = 0; cc < nsch; ++cc) {
-    if (sh.u.draw.dirty[cc]) {
+    if (sh.dirty[cc]) {
       const double wc = chunk_weight<T>(P, sh, cc, d, rt, rd);
-      if (tid == 0) sh.u.draw.w[cc] = wc;
+      if (tid == 0) sh.w[cc] = wc;
       __syncthreads();
     }
   }
@@ -894,7 +722,7 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
   for (int g = 0; g < nsch; g += kThreads) {
     const int cc = g + tid;
     double tot;
-    block_scan(cc < nsch ? sh.u.draw.w[cc] : 0.0, tot, sh);
+    block_scan(cc < nsch ? sh.w[cc] : 0.0, tot, sh.red);
     S += tot;
   }
   bool fallback = false;
@@ -903,14 +731,13 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
     // chunk weights are the chunks' Zt scaled by 1/Zt.
     fallback = true;
     __syncthreads();
-    for (int cc = tid; cc < nsch; cc += kThreads)
-      sh.u.draw.w[cc] = rt * unpack_f64(fetch(nw + cc * kNormWords), fetch(nw + cc * kNormWords + 1));
+    for (int cc = tid; cc < nsch; cc += kThreads) sh.w[cc] = rt * nr[cc].zt;
     __syncthreads();
     S = 0.0;
     for (int g = 0; g < nsch; g += kThreads) {
       const int cc = g + tid;
       double tot;
-      block_scan(cc < nsch ? sh.u.draw.w[cc] : 0.0, tot, sh);
+      block_scan(cc < nsch ? sh.w[cc] : 0.0, tot, sh.red);
       S += tot;
     }
   }
@@ -920,9 +747,9 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
   int chunk = -1, last_pos = -1;
   for (int g = 0; g < nsch && chunk < 0; g += kThreads) {
     const int cc = g + tid;
-    const double w = cc < nsch ? sh.u.draw.w[cc] : 0.0;
+    const double w = cc < nsch ? sh.w[cc] : 0.0;
     double tot;
-    const double incl = before + block_scan(w, tot, sh);
+    const double incl = before + block_scan(w, tot, sh.red);
     if (tid == 0) {
       sh.pick[0] = INT_MAX;
       sh.pick[1] = -1;
@@ -942,7 +769,7 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
   for (int g = 0; g < chunk; g += kThreads) {
     const int cc = g + tid;
     double tot;
-    block_scan(cc < chunk ? sh.u.draw.w[cc] : 0.0, tot, sh);
+    block_scan(cc < chunk ? sh.w[cc] : 0.0, tot, sh.red);
     before += tot;
   }
   // Scan the chunk: thread t owns kSampPer consecutive tokens.
@@ -963,7 +790,7 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
     run += w[k];
   }
   double tot;
-  const double incl = block_scan(run, tot, sh);
+  const double incl = block_scan(run, tot, sh.red);
   double cum = before + (incl - run);
   if (tid == 0) {
     sh.pick[0] = INT_MAX;
@@ -985,141 +812,50 @@ __device__ void draw_item(const Params P, Shared& sh, int b) {
     if (token < 0) token = 0;
     P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = token;
   }
-  __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// The persistent kernel.
-
-enum ItemKind : int { kNoItem = 0, kStat = 1, kDecide = 2, kNorm = 3, kDraw = 4 };
-
-struct Slot {
-  int kind;
-  int b;
-  int r;  // STAT row
-  int c;  // STAT or NORM chunk
-};
-
-__device__ __forceinline__ Slot slot_item(const Params P, long long s) {
-  Slot it{kNoItem, 0, 0, 0};
-  const int n_stat = (2 * P.n_draft + 1) * P.nch;
-  const int g = int(s / P.spg);
-  const int o = int(s - (long long)g * P.spg);
-  if (o < n_stat) {
-    if (g < P.batch) it = Slot{kStat, g, o / P.nch, o % P.nch};
-  } else if (o == n_stat) {
-    const int b = g - P.lag_decide;
-    if (b >= 0 && b < P.batch) it = Slot{kDecide, b, 0, 0};
-  } else if (o < n_stat + 1 + P.nsch) {
-    const int b = g - P.lag_norm;
-    if (b >= 0 && b < P.batch) it = Slot{kNorm, b, 0, o - n_stat - 1};
-  } else {
-    const int b = g - P.lag_draw;
-    if (b >= 0 && b < P.batch) it = Slot{kDraw, b, 0, 0};
-  }
-  return it;
-}
+const char* const kStageNames[] = {"row_stats", "decide_norm", "draw"};
+constexpr int kNumStages = 3;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 4) void verify_kernel(Params P) {
-  __shared__ Shared sh;
-  if (threadIdx.x < kExpTableSize) sh.exp_table[threadIdx.x] = P.exp_table[threadIdx.x];
-  __syncthreads();
-  long long s = blockIdx.x;
-  Slot it = slot_item(P, s);
-  // The temperature of the next STAT item is loaded one item ahead.
-  float t_next = (it.kind == kStat) ? P.temperature[it.b] : 0.0f;
-  for (; s < P.total_slots; s += gridDim.x) {
-    const Slot cur = it;
-    const float t_cur = t_next;
-    it = slot_item(P, s + gridDim.x);
-    if (s + gridDim.x < P.total_slots && it.kind == kStat) t_next = P.temperature[it.b];
-#ifdef SPECV_TRACE
-    const unsigned long long t_start = wall_clock64();
-    if (threadIdx.x == 0) {
-      sh.wait_ticks = 0;
-      sh.timeouts = 0;
-    }
-#endif
-    switch (cur.kind) {
-      case kStat:
-        stat_item<T>(P, sh, cur.b, cur.r, cur.c, t_cur);
-        break;
-      case kDecide:
-        decide_item<T>(P, sh, cur.b);
-        break;
-      case kNorm:
-        norm_item<T>(P, sh, cur.b, cur.c);
-        break;
-      case kDraw:
-        draw_item<T>(P, sh, cur.b);
-        break;
-      default:
-        break;
-    }
-#ifdef SPECV_TRACE
-    __syncthreads();
-    if (threadIdx.x == 0 && cur.kind != kNoItem && s < P.trace_slots) {
-      unsigned long long* rec = P.trace + s * 4;
-      rec[0] = (unsigned long long)cur.kind | ((unsigned long long)blockIdx.x << 8);
-      rec[1] = t_start;
-      rec[2] = wall_clock64();
-      rec[3] = sh.wait_ticks | (sh.timeouts << 48);
-    }
-#endif
-  }
-}
-
-__global__ void clear_words_kernel(uint64_t* p, long long n) {
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
-const char* const kStageNames[] = {"verify"};
-constexpr int kNumStages = 1;
-
-template <typename T>
-hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, const LaunchConfig& cfg, hipStream_t stream,
-                        hipEvent_t* ev) {
-  Params P;
-  P.draft = a.draft;
-  P.target = a.target;
-  P.tokens = a.tokens;
-  P.accept_u = a.accept_u;
-  P.sample_u = a.sample_u;
-  P.temperature = a.temperature;
-  P.out_tokens = a.out_tokens;
-  P.out_n = a.out_n;
-  P.row_lse = w.row_lse;
-  P.row_argmax = w.row_argmax;
-  P.stat_words = w.stat_words;
-  P.seq_words = w.seq_words;
-  P.norm_words = w.norm_words;
-  P.exp_table = w.exp_table;
-  P.batch = a.batch;
-  P.n_draft = a.n_draft;
-  P.vocab = a.vocab;
-  P.nch = w.n_stats_chunks;
-  P.nsch = w.n_samp_chunks;
+hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* ev) {
   const int R = 2 * a.n_draft + 1;
-  P.spg = R * P.nch + 1 + P.nsch + 1;
-  P.lag_decide = cfg.lag_decide;
-  P.lag_norm = cfg.lag_norm;
-  P.lag_draw = cfg.lag_draw;
-  P.total_slots = (long long)(a.batch + cfg.lag_draw) * P.spg;
-  P.epoch = cfg.epoch;
-  P.timeout_ticks = cfg.timeout_ticks;
-#ifdef SPECV_TRACE
-  P.trace = w.trace;
-  P.trace_slots = w.trace_slots;
-#endif
-  // A grid size sharing a factor with the group size would give every
-  // workgroup the same item types (e.g. only DRAW items); keep them coprime.
-  long long grid = std::min<long long>(P.total_slots, cfg.max_blocks);
-  while (grid > 1 && std::gcd(grid, (long long)P.spg) != 1) --grid;
+  StatParams sp;
+  sp.draft = a.draft;
+  sp.target = a.target;
+  sp.temperature = a.temperature;
+  sp.partials = w.partials;
+  sp.n_draft = a.n_draft;
+  sp.vocab = a.vocab;
+  sp.nch = w.n_stats_chunks;
+  sp.chunk = w.stats_chunk;
+  DrawParams dp;
+  dp.draft = a.draft;
+  dp.target = a.target;
+  dp.tokens = a.tokens;
+  dp.accept_u = a.accept_u;
+  dp.sample_u = a.sample_u;
+  dp.temperature = a.temperature;
+  dp.out_tokens = a.out_tokens;
+  dp.out_n = a.out_n;
+  dp.row_lse = w.row_lse;
+  dp.row_argmax = w.row_argmax;
+  dp.partials = w.partials;
+  dp.seq = w.seq;
+  dp.norm = w.norm;
+  dp.exp_table = w.exp_table;
+  dp.n_draft = a.n_draft;
+  dp.vocab = a.vocab;
+  dp.nch = w.n_stats_chunks;
+  dp.nsch = w.n_samp_chunks;
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, P);
+  hipLaunchKernelGGL(stat_kernel<T>, dim3(unsigned(int64_t(a.batch) * R * sp.nch)), dim3(kThreads), 0, stream, sp);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
+  hipLaunchKernelGGL(decide_norm_kernel<T>, dim3(unsigned(int64_t(a.batch) * dp.nsch)), dim3(kThreads), 0, stream,
+                     dp);
+  if (ev != nullptr) (void)hipEventRecord(ev[2], stream);
+  hipLaunchKernelGGL(draw_kernel<T>, dim3(unsigned(a.batch)), dim3(kThreads), 0, stream, dp);
+  if (ev != nullptr) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError();
 }
 
@@ -1129,28 +865,11 @@ const char* stage_name(int stage) {
   return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
 }
 
-int max_blocks_per_cu(int dtype) {
-  int occ = 0;
-  if (dtype == 0)
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, verify_kernel<float>, kThreads, 0);
-  else
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, verify_kernel<uint16_t>, kThreads, 0);
-  return occ;
-}
-
-int norm_words_per_chunk() { return kNormWords; }
-int seq_words_per_sequence() { return kSeqWords; }
-
-hipError_t clear_words(uint64_t* p, long long n, hipStream_t stream) {
-  hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, const LaunchConfig& cfg, hipStream_t stream,
-                         hipEvent_t* events, int* n_stages) {
+hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* events,
+                         int* n_stages) {
   if (n_stages != nullptr) *n_stages = kNumStages;
-  if (a.dtype == 0) return launch_typed<float>(a, w, cfg, stream, events);
-  return launch_typed<uint16_t>(a, w, cfg, stream, events);
+  if (a.dtype == 0) return launch_typed<float>(a, w, stream, events);
+  return launch_typed<uint16_t>(a, w, stream, events);
 }
 
 }  // namespace specv

@@ -76,7 +76,7 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
     n = ctypes.c_int()
     assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
-    assert specv.specv_stage_name(0) == "verify"
+    assert specv.specv_stage_name(0) == "row_stats"
     assert specv.specv_stage_name(99) is None
 
 
