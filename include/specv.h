@@ -69,8 +69,8 @@ enum specv_status {
 /* Largest n_draft a handle accepts (one 64-lane wavefront holds a sequence's decisions). */
 #define SPECV_MAX_DRAFT 64
 
-/* Largest vocabulary a handle accepts (2^22 tokens). */
-#define SPECV_MAX_VOCAB 4194304
+/* Largest vocabulary a handle accepts (2^20 tokens). */
+#define SPECV_MAX_VOCAB 1048576
 
 /*
  * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,
@@ -130,6 +130,16 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
  * verify yet), SPECV_EHIP.
  */
 SPECV_API int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream);
+
+/*
+ * Bound on the in-kernel waits of later specv_verify calls on this handle, in
+ * microseconds (default 100). Workgroups of one call hand each other partial
+ * results; one that has waited this long for a result computes it itself,
+ * which gives the same bits, so the bound only trades time, never results.
+ * 0 makes every waiting workgroup compute what it waits for at once (used to
+ * test that path). Errors: SPECV_EINVAL (null handle, negative value).
+ */
+SPECV_API int specv_set_wait_limit(specv_handle h, int microseconds);
 
 /*
  * Kernel timing (diagnostic). With enable != 0, every later specv_verify on

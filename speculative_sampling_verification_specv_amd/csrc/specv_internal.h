@@ -7,12 +7,12 @@
 namespace specv {
 
 constexpr int kThreads = 256;            // threads per workgroup (4 wave64s)
-constexpr int kStatsChunkBytes = 32768;  // row-statistics item: 32 KB of logits of either dtype
+constexpr int kStatsChunkBytes = 65536;  // row-statistics item: 64 KB of logits of either dtype
 constexpr int kSampChunk = 4096;         // logits per draw-chunk item
 constexpr int kUncMax = 16;              // uncertain-sign tokens one draw chunk records
 
 // Largest vocabulary a handle accepts, so a sequence's draw chunks fit in LDS.
-constexpr int kMaxVocab = 1 << 22;
+constexpr int kMaxVocab = 1 << 20;
 constexpr int kMaxSampChunks = kMaxVocab / kSampChunk;
 
 // Smallest positive temperature accepted: keeps log2(e)/T and max|z|*log2(e)/T
@@ -23,43 +23,19 @@ inline int stats_chunk_elems(int dtype) { return kStatsChunkBytes / (dtype == 0 
 
 enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
-// Row statistics of one (row, chunk): m = largest logit, s = sum of
-// 2^(z*c - fl(m*c)) with c = log2(e)/T, idx = first index attaining m.
-struct RowPartial {
-  float m;
-  float s;
-  int idx;
-  int pad;
-};
-
-// What the decision leaves for the draw of one sequence.
-struct SeqRecord {
-  int mode;  // SeqMode
-  int j;     // first rejected position, or N when all were accepted
-  float m_target;
-  float m_draft;
-  double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
-  double pad;
-};
-
-// fp64 sums of one draw chunk. After a rejection: zt, zd = sums of
-// exp((z - max)/T) over target and draft row j; a, b = the same over the tokens
-// whose residual weight is certainly positive; n_unc tokens of uncertain sign
-// (listed in idx when n_unc <= kUncMax). For the bonus only zt is used.
-struct NormRecord {
-  double zt, zd, a, b;
-  int n_unc;
-  int idx[kUncMax];
-  int pad;
-};
+// Records passed between workgroups, in 64-bit words whose high half holds
+// the call's sequence number (see specv_kernels.hip).
+constexpr int kPartWords = 4;                        // one (row, chunk) partial
+constexpr int kSeqWords = 8;                         // one sequence's decision
+constexpr int kNormWords = 9 + 4 * kUncMax + 7;      // one draw chunk's sums (padded to 640 bytes)
 
 struct Workspace {
-  RowPartial* partials;  // [max_batch * (2*max_draft+1)][n_stats_chunks]
-  SeqRecord* seq;        // [max_batch]
-  NormRecord* norm;      // [max_batch][n_samp_chunks]
-  double* exp_table;     // [64]: 2^(j/64)
-  float* row_lse;        // [batch][2N+1] of the last call
-  int* row_argmax;       // [batch][2N+1] of the last call
+  uint64_t* partials;  // [max_batch * (2*max_draft+1)][n_stats_chunks][kPartWords]
+  uint64_t* seq;       // [max_batch][kSeqWords]
+  uint64_t* norm;      // [max_batch][n_samp_chunks][kNormWords]
+  double* exp_table;   // [64]: 2^(j/64)
+  float* row_lse;      // [batch][2N+1] of the last call
+  int* row_argmax;     // [batch][2N+1] of the last call
   int n_stats_chunks;
   int n_samp_chunks;
   int stats_chunk;  // logits per row-statistics item
@@ -78,6 +54,8 @@ struct VerifyArgs {
   const float* temperature;
   int* out_tokens;
   int* out_n;
+  uint32_t epoch;       // nonzero, different from the previous call's
+  uint64_t wait_ticks;  // bound on in-kernel waits (100 MHz ticks)
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -92,5 +70,8 @@ const char* stage_name(int stage);
 // events[*n_stages] after the last stage.
 hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* events,
                          int* n_stages);
+
+// Zero `bytes` (a multiple of 16) of device memory on `stream` with a kernel.
+hipError_t clear_records(void* mem, size_t bytes, hipStream_t stream);
 
 }  // namespace specv

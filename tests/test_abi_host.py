@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
-                                          "specv_stage_name"}
+                                          "specv_stage_name", "specv_set_wait_limit"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -65,7 +65,7 @@ def test_argument_errors_before_any_device_call():
     lib = specv.load_library()
     h = ctypes.c_void_p()
     assert lib.specv_create(None, 1, 1, 16, 0, 0) == _lib.SPECV_EINVAL
-    for args in ((0, 4, 16, 0), (1, 0, 16, 0), (1, 65, 16, 0), (1, 4, 0, 0), (1, 4, (1 << 22) + 1, 0),
+    for args in ((0, 4, 16, 0), (1, 0, 16, 0), (1, 65, 16, 0), (1, 4, 0, 0), (1, 4, _lib.SPECV_MAX_VOCAB + 1, 0),
                  (1, 4, 16, 2), (1, 4, 16, -1)):
         assert lib.specv_create(ctypes.byref(h), *args, 0) == _lib.SPECV_EINVAL, args
         assert h.value is None
@@ -74,9 +74,10 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
     lib.specv_destroy(None)  # no-op
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
+    assert lib.specv_set_wait_limit(None, 10) == _lib.SPECV_EINVAL
     n = ctypes.c_int()
     assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
-    assert specv.specv_stage_name(0) == "row_stats"
+    assert specv.specv_stage_name(0) == "verify"
     assert specv.specv_stage_name(99) is None
 
 

@@ -71,10 +71,11 @@ def _scaled(name, batch, vocab):
 
 
 SCALED = [
-    # several 8192-logit tiles plus a ragged tail in every case
-    ("b64_n5_v128256_bf16", 16, 3 * 8192 + 517),
-    ("b256_n7_v151936_bf16_mixed", 32, 2 * 8192 + 4099),
-    ("b32_n16_v128256_f32", 8, 3 * 8192 + 37),
+    # several row-statistics chunks (32768 bf16 / 16384 fp32 logits) plus a
+    # ragged tail in every case
+    ("b64_n5_v128256_bf16", 16, 3 * 32768 + 517),
+    ("b256_n7_v151936_bf16_mixed", 32, 2 * 32768 + 4099),
+    ("b32_n16_v128256_f32", 8, 3 * 16384 + 37),
     ("b1_n5_v32000_f32", 1, 32000),
 ]
 
@@ -158,7 +159,8 @@ def test_masked_logits(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 15, 1001, 4095, 4096, 4097, 8191, 8192, 8193, 12289])
+@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 15, 1001, 4095, 4096, 4097, 8191, 8192, 8193, 12289,
+                                   16383, 16384, 16385, 32767, 32768, 32769])
 def test_vocab_shapes(dtype, vocab):
     """Row starts misaligned for 16-byte loads, single tokens, chunk and tile edges."""
     require_gpu()
@@ -207,13 +209,38 @@ def test_greedy_ties():
 
 def test_determinism():
     require_gpu()
-    wl = _scaled("b64_n5_v128256_bf16", 16, 3 * 8192 + 517)
+    wl = _scaled("b64_n5_v128256_bf16", 16, 3 * 32768 + 517)
     b = synth.make_batch(wl, seed=42)
     with Verifier(wl.batch, wl.n_draft, wl.vocab, wl.dtype) as v:
         a = run_gpu(b, v)
         c = run_gpu(b, v)
     assert np.array_equal(a.tokens, c.tokens) and np.array_equal(a.n_accepted, c.n_accepted)
     assert np.array_equal(a.lse.view(np.uint32), c.lse.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,batch,vocab", [("b256_n7_v151936_bf16_mixed", 24, 2 * 32768 + 4099),
+                                               ("b32_n16_v128256_f32", 6, 3 * 16384 + 37)])
+def test_zero_wait_limit_recomputes_the_same_bits(name, batch, vocab):
+    """With no waiting allowed, workgroups compute the records they need themselves.
+
+    Forces every recompute path from the host (missing row partials, a
+    missing decision, missing chunk sums, stale uncertain-token entries); the
+    results must be bit-identical to the default run and match the oracle.
+    """
+    require_gpu()
+    wl = _scaled(name, batch, vocab)
+    b = synth.make_batch(wl, seed=77)
+    with Verifier(wl.batch, wl.n_draft, wl.vocab, wl.dtype) as v:
+        ref = run_gpu(b, v)
+        v.set_wait_limit(0)
+        for _ in range(2):
+            got = run_gpu(b, v)
+            assert np.array_equal(got.tokens, ref.tokens) and np.array_equal(got.n_accepted, ref.n_accepted)
+            assert np.array_equal(got.lse.view(np.uint32), ref.lse.view(np.uint32))
+            assert np.array_equal(got.argmax, ref.argmax)
+    tally = compare(b, got, run_oracle(b))
+    _say(f"[parity] zero wait {name}: cases={tally.cases} exact={tally.exact} excused={tally.excused}")
+    tally.check(f"zero wait {name}")
 
 
 def test_reuse_with_smaller_batch_and_draft():
