@@ -92,6 +92,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const int chunk = specv::stats_chunk_elems(dtype);
   const int nch = specv::ceil_div(vocab, chunk);
   const int nsch = specv::ceil_div(vocab, specv::kSampChunk);
+  if (specv::grid_blocks(max_batch, max_draft, nch, nsch) >= (int64_t(1) << 31)) return SPECV_EINVAL;
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
   size_t off = 0;
   const size_t off_partials = off;

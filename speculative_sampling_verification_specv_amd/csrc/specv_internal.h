@@ -8,11 +8,11 @@ namespace specv {
 
 constexpr int kThreads = 256;            // threads per workgroup (4 wave64s)
 constexpr int kStatsChunkBytes = 65536;  // row-statistics item: 64 KB of logits of either dtype
-constexpr int kSampChunk = 4096;         // logits per draw-chunk item
-constexpr int kUncMax = 16;              // uncertain-sign tokens one draw chunk records
+constexpr int kSampChunk = 2048;         // logits per draw-chunk item
+constexpr int kUncMax = 4;               // uncertain-sign tokens one draw chunk records
 
 // Largest vocabulary a handle accepts, so a sequence's draw chunks fit in LDS.
-constexpr int kMaxVocab = 1 << 20;
+constexpr int kMaxVocab = 1 << 19;
 constexpr int kMaxSampChunks = kMaxVocab / kSampChunk;
 
 // Smallest positive temperature accepted: keeps log2(e)/T and max|z|*log2(e)/T
@@ -27,7 +27,7 @@ enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 // the call's sequence number (see specv_kernels.hip).
 constexpr int kPartWords = 4;                        // one (row, chunk) partial
 constexpr int kSeqWords = 8;                         // one sequence's decision
-constexpr int kNormWords = 9 + 4 * kUncMax + 7;      // one draw chunk's sums (padded to 640 bytes)
+constexpr int kNormWords = 32;                       // one draw chunk's sums (256 bytes)
 
 struct Workspace {
   uint64_t* partials;  // [max_batch * (2*max_draft+1)][n_stats_chunks][kPartWords]
@@ -70,6 +70,9 @@ const char* stage_name(int stage);
 // events[*n_stages] after the last stage.
 hipError_t launch_verify(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* events,
                          int* n_stages);
+
+// Workgroups one launch uses (the grid must stay below 2^31).
+int64_t grid_blocks(int batch, int n_draft, int n_stats_chunks, int n_samp_chunks);
 
 // Zero `bytes` (a multiple of 16) of device memory on `stream` with a kernel.
 hipError_t clear_records(void* mem, size_t bytes, hipStream_t stream);

@@ -6,29 +6,29 @@
 // (Speculative Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
 // verification loop.
 //
-// One launch per call. B sequences, N drafts, 2N+1 rows of V logits each; the
-// grid is B*(2N+1)*nch row-statistics workgroups followed by B*nsch draw-chunk
-// workgroups, both in sequence order:
-//   row statistics  one workgroup per (row, 32 KB chunk): fp32 max, sum of
+// One launch per call. B sequences, N drafts, 2N+1 rows of V logits each.
+// Two kinds of workgroups share the grid:
+//   row statistics  one per (row, 64 KB chunk): fp32 max, sum of
 //                   2^(z*c - fl(max*c)) with c = log2(e)/T, first argmax, and
 //                   the logit at the row's draft token if the chunk holds it.
 //                   Streaming and HBM-bound; greedy sequences skip draft rows.
-//                   The sequence's last workgroup (its last chunk of target
-//                   row N) then collects the sequence's row partials, merges
-//                   them into log-normalisers, runs the N accept tests in fp64
-//                   and writes the accepted prefix and a sequence record.
-//   draw chunks     one workgroup per (sequence, 4096-logit chunk): waits for
-//                   the sequence record, sums fp64 exps over its chunk of the
-//                   row(s) the draw needs; the sequence's last chunk
-//                   workgroup then collects the chunk sums, finds the chunk
-//                   where the inverse CDF crosses u*S and rescans it in fp64.
-// Draw-chunk workgroups come after every row-statistics workgroup in the
-// grid, so those of early sequences run while the stream is still going.
+//                   The sequence's last one (last chunk of target row N) then
+//                   collects the sequence's row partials, merges them into
+//                   log-normalisers, runs the N accept tests and writes the
+//                   accepted prefix and a sequence record.
+//   draw chunks     one per (sequence, 2048-logit chunk): waits for the
+//                   sequence record, sums fp64 exps over its chunk of the
+//                   row(s) the draw needs; the sequence's last one then
+//                   collects the chunk sums, finds the chunk where the inverse
+//                   CDF crosses u*S and rescans it in fp64.
+// The grid holds every row-statistics workgroup first, then every draw-chunk
+// workgroup; draw chunks of sequences decided early run while the last rows
+// still stream.
 //
 // The residual weight of token x is w_x = max(0, et_x/Zt - ed_x/Zd)
 // = max(0, et_x - rho*ed_x)/Zt with rho = Zt/Zd, so its sign only depends on
 // whether log(et_x/ed_x) exceeds log(rho). The decision knows log(rho) from the
-// fp32 row sums to ~1e-6; a draw chunk treats tokens more than 1e-4 away from it
+// fp32 row sums to a few 1e-6; a draw chunk treats tokens more than 1e-4 away from it
 // as certain and sums their exps into A and B, so the chunk's weight is
 // (A - rho*B)/Zt plus the exact terms of its few uncertain tokens, whose exps
 // the chunk records. One pass over the rows gives the normalisers and every
@@ -60,10 +60,11 @@ constexpr double kLn2 = 0.69314718055994530942;
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRun = kSampChunk / kThreads;            // consecutive logits a thread owns in a draw chunk
-static_assert(kMaxSampChunks <= kThreads, "the draw gives each thread at most one chunk");
 constexpr int kMaxRows = 2 * 64 + 1;
-constexpr double kSignBand = 1e-4;  // |log(et/ed) - log(rho)| at or below this is uncertain
+constexpr double kSignBand = 1e-4;      // |log(et/ed) - log(rho)| at or below this is uncertain
+constexpr int kUncPerThread = 2;        // uncertain tokens a thread stages; more overflow the chunk
 constexpr int kMaxRecomputeRounds = 3;  // a waiter's own recomputation always completes in one
+static_assert(kMaxSampChunks <= kThreads, "the draw gives each thread at most one chunk");
 
 __device__ __forceinline__ bool temperature_valid(float t) {
   return t == 0.0f || (t >= kMinTemperature && t <= kFltMax);
@@ -391,13 +392,13 @@ struct Params {
   const double* exp_table;
   uint64_t wait_ticks;  // bound on a wait, in 100 MHz wall-clock ticks
   uint32_t epoch;       // this call's sequence number, never 0
+  int batch;
   int n_draft;
   int vocab;
   int nch;     // row-statistics chunks per row
   int chunk;   // logits per row-statistics chunk
   int nsch;    // draw chunks per row
   int vec_ok;  // rows start 16-byte aligned
-  int n_stat_items;
 };
 
 // Record layouts (64-bit tagged words).
@@ -405,6 +406,7 @@ struct Params {
 //   sequence:     mode | j << 8, m_target, m_draft, log_rho (2 words)
 //   draw chunk:   zt, zd, a, b (2 words each), n_unc, then per uncertain token et, ed (2 words each)
 constexpr int kNormHead = 9;
+static_assert(kNormHead + 4 * kUncMax <= kNormWords, "draw-chunk record layout");
 
 __device__ __forceinline__ uint64_t* partial_at(const Params P, int b, int r, int c) {
   return P.partials + ((int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c) * kPartWords;
@@ -418,26 +420,29 @@ __device__ __forceinline__ bool wait_expired(const Params P, uint64_t t0) {
   return __syncthreads_or(wall_clock64() - t0 > P.wait_ticks);
 }
 
+constexpr int kStageParts = 1024;  // row partials the decision holds in LDS at once
+
 struct DecideShared {
   float row_m[kMaxRows];
   double row_logz[kMaxRows];
   int row_idx[kMaxRows];
   float row_zg[kMaxRows];
-  int row_done[kMaxRows];
-  int bad_part;
+  float part_m[kStageParts];
+  float part_s[kStageParts];
+  int part_idx[kStageParts];  // -1: the partial is not current yet
+  float part_zg[kStageParts];
   unsigned long long rej_mask;
 };
 
-constexpr int kUncPerThread = 2;  // uncertain tokens a thread stages; more overflow the chunk
-
 struct DrawShared {
-  double red[kWaves];
+  double red[4 * kWaves];
   int unc_base[kWaves];
   double unc_et[kUncPerThread][kThreads];
   double unc_ed[kUncPerThread][kThreads];
-  double w[kMaxSampChunks];
-  int flag[kMaxSampChunks];  // while collecting: chunk still missing; then: its uncertain-token count
-  int pick[2];
+  int flag[kMaxSampChunks];  // chunk record still missing (collecting), or overflowed (recompute)
+  double w[kThreads];        // chunk weights, then the rescanned chunk's per-thread sums
+  int pick;
+  double before;
 };
 
 struct Shared {
@@ -448,6 +453,37 @@ struct Shared {
     DrawShared drw;
   } u;
 };
+
+// Sums four doubles over the workgroup in a fixed order.
+__device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off);
+    b += __shfl_xor(b, off);
+    c += __shfl_xor(c, off);
+    d += __shfl_xor(d, off);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    const int w = threadIdx.x >> 6;
+    red[w] = a;
+    red[kWaves + w] = b;
+    red[2 * kWaves + w] = c;
+    red[3 * kWaves + w] = d;
+  }
+  __syncthreads();
+  a = red[0];
+  b = red[kWaves];
+  c = red[2 * kWaves];
+  d = red[3 * kWaves];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    a += red[w];
+    b += red[kWaves + w];
+    c += red[2 * kWaves + w];
+    d += red[3 * kWaves + w];
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Row statistics.
@@ -515,6 +551,11 @@ __device__ __forceinline__ void write_seq(const Params P, int b, const SeqInfo& 
 // prefix (and the token itself when greedy), the row diagnostics and the
 // sequence record. Every workgroup that runs it for a call computes and
 // writes the same values.
+//
+// The normalisers come from fp32 row sums (relative error ~1e-6); logs and
+// the ratio are taken in fp64, so log(rho) is good to a few 1e-6 (well inside
+// the draw's sign band) and a decision can only differ from exact arithmetic
+// when u is within a few 1e-6 of the ratio.
 template <typename T>
 __device__ __forceinline__ SeqInfo decide_seq(const Params P, Shared& sh, int b) {
   DecideShared& ds = sh.u.dec;
@@ -554,41 +595,72 @@ __device__ __forceinline__ SeqInfo decide_seq(const Params P, Shared& sh, int b)
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
-  for (int r = tid; r < R; r += kThreads) ds.row_done[r] = (r < r_first);
-  __syncthreads();
-
-  // Merge each row's chunk partials once they are all current: waves take
-  // rows wave, wave+4, ...; lanes take chunks lane, lane+64, ..., then a
-  // fixed butterfly. Past the wait bound the workgroup computes the missing
-  // partials itself.
-  const uint64_t t0 = wall_clock64();
-  int rounds = 0;
-  while (true) {
-    for (int r = r_first + wave; r < R; r += kWaves) {
-      if (ds.row_done[r]) continue;
-      const int gchunk = (r < 2 * N) ? tok[r < N ? r : r - N] / P.chunk : -1;
-      float m = -INFINITY, s = 0.0f, zg = 0.0f;
-      int idx = INT_MAX;
+  // The row partials, a group of rows at a time: every thread loads partials
+  // tid, tid + kThreads, ... of the group (one round trip per pass) until all
+  // are current; past the wait bound the workgroup computes the missing ones
+  // itself. Then waves merge rows wave, wave+4, ... of the group: lanes take
+  // chunks lane, lane+64, ..., then a fixed butterfly.
+  const int rows_per_group = max(1, kStageParts / P.nch);
+  for (int rg = r_first; rg < R; rg += rows_per_group) {
+    const int nr = min(rows_per_group, R - rg);
+    const int np = nr * P.nch;
+    const uint64_t t0 = wall_clock64();
+    int rounds = 0;
+    while (true) {
       bool ok = true;
-      for (int k = lane; k < P.nch; k += 64) {
-        const uint64_t* w = partial_at(P, b, r, k);
-        const float m2 = get_word_f(w, P.epoch, ok);
-        const float s2 = get_word_f(w + 1, P.epoch, ok);
-        const int i2 = int(get_word(w + 2, P.epoch, ok));
-        const float z2 = get_word_f(w + 3, P.epoch, ok);
-        if (greedy)
-          acc_merge<false>(m, s, idx, m2, s2, i2, c);
-        else
-          acc_merge<true>(m, s, idx, m2, s2, i2, c);
-        if (k == gchunk) zg = z2;
+      for (int i = tid; i < np; i += kThreads) {
+        const int rr = i / P.nch;
+        const uint64_t* w = partial_at(P, b, rg + rr, i - rr * P.nch);
+        bool okp = true;
+        ds.part_m[i] = get_word_f(w, P.epoch, okp);
+        ds.part_s[i] = get_word_f(w + 1, P.epoch, okp);
+        const int idx = int(get_word(w + 2, P.epoch, okp));
+        ds.part_zg[i] = get_word_f(w + 3, P.epoch, okp);
+        ds.part_idx[i] = okp ? idx : -1;
+        ok = ok && okp;
       }
-      if (__ballot(!ok) != 0) continue;  // wave-uniform
+      if (__syncthreads_and(ok)) break;
+      trace(5);
+      if (!wait_expired(P, t0)) {
+        __builtin_amdgcn_s_sleep(2);
+        continue;
+      }
+      if (++rounds > kMaxRecomputeRounds) {
+        // Unreachable unless the records are broken: fail the sequence
+        // rather than wait forever.
+        for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
+        if (tid == 0) {
+          P.out_n[b] = -1;
+          write_seq(P, b, rec);
+        }
+        __syncthreads();
+        return rec;
+      }
+      for (int i = 0; i < np; ++i) {
+        if (ds.part_idx[i] < 0) {
+          const int rr = i / P.nch;
+          stat_item<T, 2>(P, sh, b, rg + rr, i - rr * P.nch, t);
+        }
+      }
+      stores_done();
+      __syncthreads();
+    }
+    for (int rr = wave; rr < nr; rr += kWaves) {
+      const int r = rg + rr;
+      float m = -INFINITY, s = 0.0f;
+      int idx = INT_MAX;
+      for (int k = lane; k < P.nch; k += 64) {
+        const int i = rr * P.nch + k;
+        if (greedy)
+          acc_merge<false>(m, s, idx, ds.part_m[i], ds.part_s[i], ds.part_idx[i], c);
+        else
+          acc_merge<true>(m, s, idx, ds.part_m[i], ds.part_s[i], ds.part_idx[i], c);
+      }
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) {
         const float m2 = __shfl_xor(m, off);
         const float s2 = __shfl_xor(s, off);
         const int i2 = __shfl_xor(idx, off);
-        zg += __shfl_xor(zg, off);  // one lane holds the token's logit, the others 0: exact
         if (greedy)
           acc_merge<false>(m, s, idx, m2, s2, i2, c);
         else
@@ -601,46 +673,14 @@ __device__ __forceinline__ SeqInfo decide_seq(const Params P, Shared& sh, int b)
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        ds.row_zg[r] = zg;
-        ds.row_done[r] = 1;
+        ds.row_zg[r] = (r < 2 * N) ? ds.part_zg[rr * P.nch + tok[r < N ? r : r - N] / P.chunk] : 0.0f;
         lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
         amax[r] = idx;
       }
     }
-    if (__syncthreads_and(tid >= R || ds.row_done[tid] != 0)) break;
-    if (wait_expired(P, t0)) {
-      if (++rounds > kMaxRecomputeRounds) {
-        // Unreachable unless the records are broken: fail the sequence
-        // rather than wait forever.
-        for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
-        if (tid == 0) {
-          P.out_n[b] = -1;
-          write_seq(P, b, rec);
-        }
-        __syncthreads();
-        return rec;
-      }
-      for (int r = r_first; r < R; ++r) {
-        if (ds.row_done[r]) continue;
-        for (int k = 0; k < P.nch; ++k) {
-          if (tid == 0) {
-            bool ok = true;
-            const uint64_t* w = partial_at(P, b, r, k);
-            for (int q = 0; q < kPartWords; ++q) (void)get_word(w + q, P.epoch, ok);
-            ds.bad_part = ok ? 0 : 1;
-          }
-          __syncthreads();
-          const bool missing = ds.bad_part != 0;
-          __syncthreads();
-          if (missing) stat_item<T, 2>(P, sh, b, r, k, t);
-        }
-      }
-      stores_done();
-      __syncthreads();
-    } else {
-      __builtin_amdgcn_s_sleep(2);
-    }
+    __syncthreads();
   }
+  trace(3);
   if (greedy) {
     for (int r = tid; r < N; r += kThreads) {
       lse[r] = NAN;
@@ -657,9 +697,10 @@ __device__ __forceinline__ SeqInfo decide_seq(const Params P, Shared& sh, int b)
     } else if (zd == -INFINITY) {
       accept = true;  // p(d) == 0: the ratio is infinite
     } else {
-      const double log_q = (double(zt) - double(ds.row_m[N + tid])) * inv_t - ds.row_logz[N + tid];
-      const double log_p = (double(zd) - double(ds.row_m[tid])) * inv_t - ds.row_logz[tid];
-      accept = double(ua) < exp(log_q - log_p);
+      // log(q(d)/p(d)); the test is u < exp of it.
+      const double lr = ((double(zt) - double(ds.row_m[N + tid])) - (double(zd) - double(ds.row_m[tid]))) * inv_t -
+                        (ds.row_logz[N + tid] - ds.row_logz[tid]);
+      accept = double(ua) < exp(lr);
     }
   }
   // N <= 64: every decision lives in wave 0.
@@ -719,7 +760,8 @@ template <typename T>
 struct DrawRows {
   const T* trow;
   const T* drow;
-  double mt, md, inv_t;
+  double nmt, nmd;  // -max/T of the target and draft rows
+  double inv_t;
   bool residual;
 };
 
@@ -729,15 +771,15 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params P, int b, const Se
   DrawRows<T> d;
   d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
   d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
-  d.mt = s.m_target;
-  d.md = s.m_draft;
   d.inv_t = 1.0 / double(P.temperature[b]);
+  d.nmt = -double(s.m_target) * d.inv_t;
+  d.nmd = -double(s.m_draft) * d.inv_t;
   d.residual = (s.mode == kModeResidual);
   return d;
 }
 
-// Argument (z - max)/T of a token's exp; every step forms it the same way.
-__device__ __forceinline__ double exp_arg(float z, double m, double inv_t) { return (double(z) - m) * inv_t; }
+// Argument z/T - max/T of a token's exp; every step forms it the same way.
+__device__ __forceinline__ double exp_arg(float z, double nm, double inv_t) { return fma(double(z), inv_t, nm); }
 
 // Keeps the scheduler from interleaving the fp64 work of many tokens, which
 // would hold their temporaries live at once and cost occupancy.
@@ -750,28 +792,33 @@ __device__ __forceinline__ double resid_weight(double et, double ed, double rt, 
 
 // fp64 sums of draw chunk c of sequence b, written as a tagged record.
 template <typename T>
-__device__ __forceinline__ void norm_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d, double log_rho) {
+__device__ __forceinline__ void norm_item(const Params P, Shared& sh, int b, int c, const DrawRows<T>& d,
+                                          double log_rho) {
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int e0 = c * kSampChunk + tid * kRun;
   float zt[kRun], zd[kRun];
   load_run(d.trow, e0, P.vocab, P.vec_ok != 0, zt);
   if (d.residual) load_run(d.drow, e0, P.vocab, P.vec_ok != 0, zd);
+  // The sign of w_x follows (zt - zd)/T - (mt - md)/T against log(rho); fp32
+  // gets it to ~1e-6 here, well inside the band.
+  const float inv_tf = float(d.inv_t);
+  const float dmf = float(d.nmt - d.nmd);  // -(mt - md)/T
+  const float hi = float(log_rho + kSignBand), lo = float(log_rho - kSignBand);
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;
   int n_unc = 0;  // uncertain-sign tokens of this thread; the first kUncPerThread are staged
 #pragma unroll
   for (int k = 0; k < kRun; ++k) {
-    const double at = exp_arg(zt[k], d.mt, d.inv_t);
-    const double et = exp_nonpos(at, sh.exp_table);
+    const double et = exp_nonpos(exp_arg(zt[k], d.nmt, d.inv_t), sh.exp_table);
     st += et;
     if (d.residual) {
-      const double ad = exp_arg(zd[k], d.md, d.inv_t);
-      const double ed = exp_nonpos(ad, sh.exp_table);
+      const double ed = exp_nonpos(exp_arg(zd[k], d.nmd, d.inv_t), sh.exp_table);
       sd += ed;
-      // at - ad is +inf when the draft gives the token zero mass.
-      const double lr = at - ad;
-      const bool pos = et > 0.0 && (ed == 0.0 || lr > log_rho + kSignBand);
-      const bool band = et > 0.0 && !pos && lr >= log_rho - kSignBand;
+      // +inf when the draft gives the token zero mass, NaN (neither side)
+      // when both rows do: such a token adds nothing wherever it goes.
+      const float lr = fmaf(zt[k] - zd[k], inv_tf, dmf);
+      const bool pos = lr > hi;
+      const bool band = !pos && lr >= lo;
       sa += pos ? et : 0.0;
       sb += pos ? ed : 0.0;
       if (band && n_unc < kUncPerThread) {
@@ -783,12 +830,9 @@ __device__ __forceinline__ void norm_item(const Params P, Shared& sh, int b, int
     fp64_step_fence();
   }
   uint64_t* out = norm_at(P, b, c);
-  st = block_sum(st, ws.red);
+  block_sum4(st, sd, sa, sb, ws.red);
   int total = 0;
   if (d.residual) {
-    sd = block_sum(sd, ws.red);
-    sa = block_sum(sa, ws.red);
-    sb = block_sum(sb, ws.red);
     // Uncertain tokens in ascending token order (threads own ascending runs),
     // with their exps; a thread past its staging capacity overflows the chunk.
     const int cnt = (n_unc <= kUncPerThread) ? n_unc : kUncMax + 1;
@@ -828,7 +872,8 @@ __device__ __forceinline__ void norm_item(const Params P, Shared& sh, int b, int
 // Weight sum of one chunk from its logits (after a rejection): used for
 // chunks whose uncertain tokens overflowed their record.
 template <typename T>
-__device__ __forceinline__ double chunk_weight(const Params P, Shared& sh, int c, const DrawRows<T>& d, double rt, double rd) {
+__device__ __forceinline__ double chunk_weight(const Params P, Shared& sh, int c, const DrawRows<T>& d, double rt,
+                                               double rd) {
   const int e0 = c * kSampChunk + threadIdx.x * kRun;
   float zt[kRun], zd[kRun];
   load_run(d.trow, e0, P.vocab, P.vec_ok != 0, zt);
@@ -836,24 +881,83 @@ __device__ __forceinline__ double chunk_weight(const Params P, Shared& sh, int c
   double w = 0.0;
 #pragma unroll
   for (int k = 0; k < kRun; ++k) {
-    w += resid_weight(exp_nonpos(exp_arg(zt[k], d.mt, d.inv_t), sh.exp_table),
-                      exp_nonpos(exp_arg(zd[k], d.md, d.inv_t), sh.exp_table), rt, rd);
+    w += resid_weight(exp_nonpos(exp_arg(zt[k], d.nmt, d.inv_t), sh.exp_table),
+                      exp_nonpos(exp_arg(zd[k], d.nmd, d.inv_t), sh.exp_table), rt, rd);
     fp64_step_fence();
   }
   return block_sum(w, sh.u.drw.red);
 }
 
-// Sum of the chunk weights over all chunks, as a scan in groups of kThreads
-// chunks (the order the crossing search uses).
-__device__ __forceinline__ double weight_total(DrawShared& ws, int nsch) {
-  double S = 0.0;
-  for (int g = 0; g < nsch; g += kThreads) {
-    const int cc = g + threadIdx.x;
-    double tot;
-    block_scan(cc < nsch ? ws.w[cc] : 0.0, tot, ws.red);
-    S += tot;
+// Crossing searches run by wave 0 over kThreads values v[0..kThreads): lane l
+// owns v[4l..4l+3]. Lane sums (in order), a wave inclusive scan, then each
+// lane walks its four values from its exclusive prefix.
+
+// Inclusive wave scan of one double per lane (Hillis-Steele, fixed order).
+__device__ __forceinline__ double wave_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double up = __shfl_up(x, off);
+    if (lane >= off) x += up;
   }
-  return S;
+  return x;
+}
+
+// First index i with positive v[i] whose inclusive prefix exceeds target,
+// else the last index with positive v[i], else 0; returns target - prefix
+// before i through `rem` and the total through S. Uniform over wave 0.
+__device__ __forceinline__ int find_crossing_abs(const double* v, int lane, double target, double& S, double& rem) {
+  constexpr int kPer = kThreads / 64;
+  double own = 0.0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) own += v[kPer * lane + q];
+  const double incl = wave_scan(own, lane);
+  S = __shfl(incl, 63);
+  double pre = incl - own;  // exclusive prefix of this lane's values
+  int cross = INT_MAX, lastpos = -1;
+  double cross_pre = 0.0, last_pre = 0.0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = kPer * lane + q;
+    const double x = v[i];
+    if (x > 0.0) {
+      if (cross == INT_MAX && pre + x > target) {
+        cross = i;
+        cross_pre = pre;
+      }
+      lastpos = i;
+      last_pre = pre;
+    }
+    pre += x;
+  }
+  const unsigned long long has = __ballot(cross != INT_MAX);
+  if (has) {
+    const int src = __ffsll(has) - 1;
+    const int i = __shfl(cross, src);
+    rem = target - __shfl(cross_pre, src);
+    return i;
+  }
+  const unsigned long long pos = __ballot(lastpos >= 0);
+  if (pos) {
+    const int src = 63 - __clzll(pos);
+    const int i = __shfl(lastpos, src);
+    rem = target - __shfl(last_pre, src);
+    return i;
+  }
+  rem = target;
+  return 0;
+}
+
+// The chunk search: target = u * S over the chunk weights.
+__device__ __forceinline__ int find_crossing(const double* v, int lane, double u, double& S, double& rem) {
+  constexpr int kPer = kThreads / 64;
+  double own = 0.0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) own += v[kPer * lane + q];
+  S = __shfl(wave_scan(own, lane), 63);
+  double r;
+  const int i = find_crossing_abs(v, lane, u * S, S, r);
+  if (lane == 0) rem = r;
+  return i;
 }
 
 // The draw for sequence b, by the workgroup of its last draw chunk.
@@ -863,9 +967,12 @@ __device__ __forceinline__ void draw_seq(const Params P, Shared& sh, int b, cons
   const int tid = threadIdx.x;
   const int nsch = P.nsch;
 
-  // Collect the chunk records: thread tid owns chunk tid. Every pass reads
-  // them all afresh; past the wait bound the missing ones are computed here.
+  // Collect the chunk records with their uncertain-token entries: thread tid
+  // owns chunk tid. Every pass reads them afresh; past the wait bound the
+  // missing ones are computed here.
+  const bool mine = tid < nsch;
   double rz, rzd, ra, rb;
+  double uet[kUncMax], ued[kUncMax];
   int rn;
   const uint64_t t0 = wall_clock64();
   int rounds = 0;
@@ -873,16 +980,25 @@ __device__ __forceinline__ void draw_seq(const Params P, Shared& sh, int b, cons
     bool ok = true;
     rz = rzd = ra = rb = 0.0;
     rn = 0;
-    if (tid < nsch) {
+    if (mine) {
       const uint64_t* w = norm_at(P, b, tid);
       rz = get_word_d(w, P.epoch, ok);
       rzd = get_word_d(w + 2, P.epoch, ok);
       ra = get_word_d(w + 4, P.epoch, ok);
       rb = get_word_d(w + 6, P.epoch, ok);
       rn = int(get_word(w + 8, P.epoch, ok));
+#pragma unroll
+      for (int k = 0; k < kUncMax; ++k) {
+        bool okk = true;
+        uet[k] = get_word_d(w + kNormHead + 4 * k, P.epoch, okk);
+        ued[k] = get_word_d(w + kNormHead + 4 * k + 2, P.epoch, okk);
+        // Only entries the record holds must be current (none when it overflowed).
+        ok = ok && (okk || k >= rn || rn > kUncMax);
+      }
       ws.flag[tid] = ok ? 0 : 1;
     }
     if (__syncthreads_and(ok)) break;
+    trace(7);
     if (!wait_expired(P, t0)) {
       __builtin_amdgcn_s_sleep(2);
       continue;
@@ -897,195 +1013,172 @@ __device__ __forceinline__ void draw_seq(const Params P, Shared& sh, int b, cons
     stores_done();
     __syncthreads();
   }
+  trace(4);
   double rt = 0.0, rd = 0.0;
+  double wc = rz;  // bonus: the chunk's sum of exps
   if (d.residual) {
-    const double zt = block_sum(rz, ws.red);
-    const double zd = block_sum(rzd, ws.red);
+    double zt = rz, zd = rzd, unused0 = 0.0, unused1 = 0.0;
+    block_sum4(zt, zd, unused0, unused1, ws.red);
     rt = 1.0 / zt;
     rd = 1.0 / zd;
     const double rho = zt * rd;
-    if (tid < nsch) {
-      ws.w[tid] = rt * (ra - rho * rb);
-      ws.flag[tid] = rn;
-    }
-    __syncthreads();
-    // Exact terms of the uncertain tokens from their recorded exps: lane
-    // group g of 16 takes chunk c0 + g, lane k its k-th token; a fixed
-    // butterfly sums the group. A chunk whose entries are not all current
-    // yet is retried, and past the wait bound recomputed from its logits.
-    const int g = tid >> 4, k = tid & 15;
-    const uint64_t t1 = wall_clock64();
-    bool pending = true;
-    while (pending) {
-      bool stale = false;
-      for (int c0 = 0; c0 < nsch; c0 += kThreads / 16) {
-        const int cc = c0 + g;
-        const int n = (cc < nsch) ? ws.flag[cc] : 0;
-        double x = 0.0;
-        bool ok = true;
-        if (k < n && n <= kUncMax) {
-          const uint64_t* e = norm_at(P, b, cc) + kNormHead + 4 * k;
-          const double et = get_word_d(e, P.epoch, ok);
-          const double ed = get_word_d(e + 2, P.epoch, ok);
-          x = resid_weight(et, ed, rt, rd);
-        }
+    wc = rt * (ra - rho * rb);
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          x += __shfl_xor(x, off, 16);
-          ok = ok && __shfl_xor(int(ok), off, 16);
-        }
-        stale = stale || !ok;
-        if (k == 0 && n > 0 && n <= kUncMax && ok) {
-          ws.w[cc] += x;
-          ws.flag[cc] = 0;  // done
-        }
-      }
-      pending = __syncthreads_or(stale);
-      if (pending && wait_expired(P, t1)) {
-        for (int cc = tid; cc < nsch; cc += kThreads)
-          if (ws.flag[cc] > 0 && ws.flag[cc] <= kUncMax) ws.flag[cc] = kUncMax + 1;
-        __syncthreads();
-        pending = false;
-      } else if (pending) {
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
+    for (int k = 0; k < kUncMax; ++k)
+      if (k < rn) wc += resid_weight(uet[k], ued[k], rt, rd);
     // Chunks whose uncertain tokens overflowed their record: recompute.
-    for (int cc = 0; cc < nsch; ++cc) {
-      if (ws.flag[cc] > kUncMax) {
-        const double wc = chunk_weight<T>(P, sh, cc, d, rt, rd);
-        if (tid == 0) ws.w[cc] = wc;
+    if (__syncthreads_or(mine && rn > kUncMax)) {
+      if (mine) ws.flag[tid] = rn > kUncMax ? 1 : 0;
+      __syncthreads();
+      for (int cc = 0; cc < nsch; ++cc) {
+        if (ws.flag[cc]) {
+          const double w2 = chunk_weight<T>(P, sh, cc, d, rt, rd);
+          if (tid == cc) wc = w2;
+        }
       }
     }
-  } else if (tid < nsch) {
-    ws.w[tid] = rz;
+  }
+  if (!mine) wc = 0.0;
+  trace(5);
+  // Chunk search by wave 0: lane l sums chunks 4l..4l+3 in order, a wave scan
+  // gives S and each lane's prefix, and the first chunk with positive weight
+  // whose inclusive prefix exceeds u*S is the crossing.
+  ws.w[tid] = wc;
+  __syncthreads();
+  bool fallback = false;
+  if (tid < 64) {
+    double S;
+    int chunk = find_crossing(ws.w, tid, double(P.sample_u[b]), S, ws.before);
+    // Every residual weight rounded to zero (S <= 0): flag the fallback.
+    if (d.residual && !(S > 0.0)) chunk = -1;
+    if (tid == 0) ws.pick = chunk;
   }
   __syncthreads();
-  double S = weight_total(ws, nsch);
-  bool fallback = false;
-  if (d.residual && !(S > 0.0)) {
-    // Every residual weight rounded to zero: draw from q_j itself, whose
-    // chunk weights are the chunks' Zt scaled by 1/Zt.
+  if (ws.pick < 0) {
+    // Draw from q_j itself, whose chunk weights are the chunks' Zt scaled by 1/Zt.
     fallback = true;
+    ws.w[tid] = mine ? rt * rz : 0.0;
     __syncthreads();
-    if (tid < nsch) ws.w[tid] = rt * rz;
-    __syncthreads();
-    S = weight_total(ws, nsch);
-  }
-  const double target_mass = double(P.sample_u[b]) * S;
-  // First chunk with positive weight whose inclusive prefix exceeds target_mass.
-  double before = 0.0;
-  int chunk = -1, last_pos = -1;
-  for (int g = 0; g < nsch && chunk < 0; g += kThreads) {
-    const int cc = g + tid;
-    const double w = cc < nsch ? ws.w[cc] : 0.0;
-    double tot;
-    const double incl = before + block_scan(w, tot, ws.red);
-    if (tid == 0) {
-      ws.pick[0] = INT_MAX;
-      ws.pick[1] = -1;
+    if (tid < 64) {
+      double S;
+      const int chunk = find_crossing(ws.w, tid, double(P.sample_u[b]), S, ws.before);
+      if (tid == 0) ws.pick = chunk;
     }
     __syncthreads();
-    if (cc < nsch && incl > target_mass && w > 0.0) atomicMin(&ws.pick[0], cc);
-    if (cc < nsch && w > 0.0) atomicMax(&ws.pick[1], cc);
-    __syncthreads();
-    if (ws.pick[1] >= 0) last_pos = ws.pick[1];
-    if (ws.pick[0] != INT_MAX) chunk = ws.pick[0];
-    before += tot;
-    __syncthreads();
   }
-  if (chunk < 0) chunk = max(last_pos, 0);  // rounding left u*S at or past the total
-  // Exclusive prefix of the chosen chunk, in the same group-scan order.
-  before = 0.0;
-  for (int g = 0; g < chunk; g += kThreads) {
-    const int cc = g + tid;
-    double tot;
-    block_scan(cc < chunk ? ws.w[cc] : 0.0, tot, ws.red);
-    before += tot;
-  }
-  // Rescan the chunk: thread tid owns kRun consecutive tokens; their weights
-  // are formed twice (for the thread's sum, then for the walk) rather than kept.
+  const int chunk = ws.pick;
+  const double target_mass = ws.before;  // mass still to cover inside the chunk
+  __syncthreads();
+  trace(6);
+  // Rescan the chunk: thread tid owns kRun consecutive tokens; wave 0 finds
+  // the thread whose run crosses, that thread the token.
   const int e_base = chunk * kSampChunk + tid * kRun;
-  float zt[kRun], zd[kRun];
-  load_run(d.trow, e_base, P.vocab, P.vec_ok != 0, zt);
-  if (d.residual) load_run(d.drow, e_base, P.vocab, P.vec_ok != 0, zd);
-  auto weight = [&](int k) {
-    const double et = exp_nonpos(exp_arg(zt[k], d.mt, d.inv_t), sh.exp_table);
-    if (!d.residual) return et;
-    if (fallback) return et * rt;
-    return resid_weight(et, exp_nonpos(exp_arg(zd[k], d.md, d.inv_t), sh.exp_table), rt, rd);
-  };
+  double w[kRun];
   double run = 0.0;
+  {
+    float zt[kRun], zd[kRun];
+    load_run(d.trow, e_base, P.vocab, P.vec_ok != 0, zt);
+    if (d.residual) load_run(d.drow, e_base, P.vocab, P.vec_ok != 0, zd);
 #pragma unroll
-  for (int k = 0; k < kRun; ++k) {
-    run += weight(k);
-    fp64_step_fence();
+    for (int k = 0; k < kRun; ++k) {
+      const double et = exp_nonpos(exp_arg(zt[k], d.nmt, d.inv_t), sh.exp_table);
+      if (!d.residual)
+        w[k] = et;
+      else if (fallback)
+        w[k] = et * rt;
+      else
+        w[k] = resid_weight(et, exp_nonpos(exp_arg(zd[k], d.nmd, d.inv_t), sh.exp_table), rt, rd);
+      run += w[k];
+      fp64_step_fence();
+    }
   }
-  // Hide the logits' values from the optimiser so the walk recomputes the
-  // weights instead of keeping all of them live from the first pass.
-#pragma unroll
-  for (int k = 0; k < kRun; ++k) {
-    asm volatile("" : "+v"(zt[k]));
-    if (d.residual) asm volatile("" : "+v"(zd[k]));
-  }
-  double tot;
-  const double incl = block_scan(run, tot, ws.red);
-  double cum = before + (incl - run);
-  if (tid == 0) {
-    ws.pick[0] = INT_MAX;
-    ws.pick[1] = -1;
+  ws.w[tid] = run;
+  __syncthreads();
+  if (tid < 64) {
+    double S, rem;
+    const int thr = find_crossing_abs(ws.w, tid, target_mass, S, rem);
+    if (tid == 0) {
+      ws.pick = thr;
+      ws.before = rem;
+    }
   }
   __syncthreads();
-  int first = INT_MAX, last = -1;
+  if (tid == ws.pick) {
+    // Walk this thread's run: first token with positive weight whose running
+    // sum exceeds the remaining mass, else (rounding) the last positive one.
+    const double rem = ws.before;
+    double cum = 0.0;
+    int token = -1, last = -1;
 #pragma unroll
-  for (int k = 0; k < kRun; ++k) {
-    const double wk = weight(k);
-    cum += wk;
-    if (first == INT_MAX && cum > target_mass && wk > 0.0) first = k;
-    if (wk > 0.0) last = k;
-    fp64_step_fence();
-  }
-  if (first != INT_MAX) atomicMin(&ws.pick[0], e_base + first);
-  if (last >= 0) atomicMax(&ws.pick[1], e_base + last);
-  __syncthreads();
-  if (tid == 0) {
-    int token = (ws.pick[0] != INT_MAX) ? ws.pick[0] : ws.pick[1];
-    if (token < 0) token = 0;
-    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = token;
+    for (int k = 0; k < kRun; ++k) {
+      cum += w[k];
+      if (token < 0 && cum > rem && w[k] > 0.0) token = k;
+      if (w[k] > 0.0) last = k;
+    }
+    const int k = token >= 0 ? token : last;
+    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? e_base + k : 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // The launch.
 
+// What workgroup x does: the row statistics of every sequence come first in
+// the grid, then the draw chunks of every sequence, both in sequence order.
+// (Draw chunks dispatched while rows still stream would take issue slots from
+// the stream, whose ALU is already close to busy.)
+struct Work {
+  bool stat;
+  int b;
+  int idx;  // row-statistics item within the sequence (r * nch + chunk), or draw chunk
+};
+
+__device__ __forceinline__ Work work_of(const Params P, int x) {
+  const int A = (2 * P.n_draft + 1) * P.nch;
+  Work w;
+  w.stat = x < P.batch * A;
+  if (w.stat) {
+    w.b = x / A;
+    w.idx = x - w.b * A;
+  } else {
+    x -= P.batch * A;
+    w.b = x / P.nsch;
+    w.idx = x - w.b * P.nsch;
+  }
+  return w;
+}
+
+// Decisions and draws sit on the critical path of the sequences that finish
+// last, while the CU is busy with other workgroups' streaming and fp64
+// sums: their waves take issue priority.
+__device__ __forceinline__ void critical_path() { __builtin_amdgcn_s_setprio(3); }
+
+// At most 128 VGPRs (four waves per SIMD): row-statistics workgroups keep
+// 64 KB each in flight, enough to keep HBM busy at this occupancy.
 template <typename T>
-// At most 128 VGPRs (four waves per SIMD): the row-statistics workgroups
-// stream with 32 KB each in flight, enough to keep HBM busy at this occupancy.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(Params P) {
   __shared__ Shared sh;
   trace(0);
-  if (int(blockIdx.x) < P.n_stat_items) {
+  const Work wk = work_of(P, int(blockIdx.x));
+  const int b = wk.b;
+  if (wk.stat) {
     const int R = 2 * P.n_draft + 1;
-    const int item = blockIdx.x;
-    const int row = item / P.nch;
-    const int chunk = item - row * P.nch;
-    const int b = row / R;
-    const int r = row - b * R;
+    const int r = wk.idx / P.nch;
+    const int chunk = wk.idx - r * P.nch;
     const float t = P.temperature[b];
     if (temperature_valid(t) && !(t == 0.0f && r < P.n_draft))
       stat_item<T, kStatsChunkBytes / 16 / kThreads>(P, sh, b, r, chunk, t);
     trace(1);
     if (r == R - 1 && chunk == P.nch - 1) {
+      critical_path();
       __syncthreads();
       decide_seq<T>(P, sh, b);
       trace(2);
     }
     return;
   }
-  const int k = int(blockIdx.x) - P.n_stat_items;
-  const int b = k / P.nsch;
-  const int c = k - b * P.nsch;
-  if (threadIdx.x < kExpTableSize) sh.exp_table[threadIdx.x] = P.exp_table[threadIdx.x];
+  const int c = wk.idx;
+  for (int i = threadIdx.x; i < kExpTableSize; i += kThreads) sh.exp_table[i] = P.exp_table[i];
   const SeqInfo s = wait_seq<T>(P, sh, b);
   trace(1);
   if (s.mode == kModeNone) return;
@@ -1093,6 +1186,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   norm_item<T>(P, sh, b, c, d, s.log_rho);
   trace(2);
   if (c != P.nsch - 1) return;
+  critical_path();
   __syncthreads();
   draw_seq<T>(P, sh, b, s, d);
   trace(3);
@@ -1103,7 +1197,6 @@ constexpr int kNumStages = 1;
 
 template <typename T>
 hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* ev) {
-  const int R = 2 * a.n_draft + 1;
   Params p;
   p.draft = a.draft;
   p.target = a.target;
@@ -1121,14 +1214,14 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.exp_table = w.exp_table;
   p.wait_ticks = a.wait_ticks;
   p.epoch = a.epoch;
+  p.batch = a.batch;
   p.n_draft = a.n_draft;
   p.vocab = a.vocab;
   p.nch = w.n_stats_chunks;
   p.chunk = w.stats_chunk;
   p.nsch = w.n_samp_chunks;
   p.vec_ok = (int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0;
-  p.n_stat_items = a.batch * R * p.nch;
-  const int64_t blocks = int64_t(p.n_stat_items) + int64_t(a.batch) * p.nsch;
+  const int64_t blocks = grid_blocks(a.batch, a.n_draft, p.nch, p.nsch);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
@@ -1145,6 +1238,10 @@ __global__ void clear_kernel(uint4* p, int64_t n) {
 
 const char* stage_name(int stage) {
   return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
+}
+
+int64_t grid_blocks(int batch, int n_draft, int n_stats_chunks, int n_samp_chunks) {
+  return int64_t(batch) * (int64_t(2 * n_draft + 1) * n_stats_chunks + n_samp_chunks);
 }
 
 hipError_t clear_records(void* mem, size_t bytes, hipStream_t stream) {

@@ -118,6 +118,9 @@ def compare(batch: synth.Batch, gpu: GpuResult, results: list, seqs=None) -> Tal
         if r.n_accepted < 0 or g_n < 0 or T == 0.0:
             t.hard.append(info)
             continue
+        if not (0 <= g_n <= batch.n_draft) or not (0 <= g_t[g_n] < batch.vocab):
+            t.hard.append(info)  # a token that is not a vocabulary index is never excused
+            continue
         if g_n != r.n_accepted:
             i = min(g_n, r.n_accepted)
             m = r.decision_margins[i]

@@ -1,0 +1,37 @@
+"""Host check of the kernels' fp64 exponential (specv_math.h), built with g++.
+
+The draw sums fp64 exps of (z - max)/T; its parity with the oracle needs them
+to ~1e-10 relative. The header states 3e-13.
+"""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_specv_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def exp_report(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    out = tmp_path_factory.mktemp("exp") / "exp_check"
+    subprocess.run([gxx, "-O2", "-std=c++17", "-I", CSRC, os.path.join(ROOT, "tests", "native", "exp_check.cpp"),
+                    "-o", str(out), "-lm"], check=True)
+    text = subprocess.run([str(out)], check=True, capture_output=True, text=True).stdout
+    return dict(line.split(None, 1) for line in text.strip().splitlines())
+
+
+def test_relative_error_bound(exp_report):
+    assert float(exp_report["max_rel_err"].split()[0]) < 3e-13
+
+
+def test_special_values(exp_report):
+    assert float(exp_report["exp0"]) == 1.0
+    assert float(exp_report["exp_minus_inf"]) == 0.0
+    assert float(exp_report["exp_nan"]) == 0.0
+    assert float(exp_report["exp_below"]) == 0.0

@@ -159,7 +159,7 @@ def test_masked_logits(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 15, 1001, 4095, 4096, 4097, 8191, 8192, 8193, 12289,
+@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 9, 15, 1001, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192, 8193, 12289,
                                    16383, 16384, 16385, 32767, 32768, 32769])
 def test_vocab_shapes(dtype, vocab):
     """Row starts misaligned for 16-byte loads, single tokens, chunk and tile edges."""
