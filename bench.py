@@ -44,6 +44,14 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="logit copies rotated per step (0: enough for 512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="b256_n7_v151936_bf16_mixed",
+                    help="comma-separated workloads also timed (reported under 'also'); empty for none")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MB (8 times) so that a "
+                         "rocprofv3 --pmc run of this command also measures a copy of known size")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "OUT"),
+                    help="write the HBM traffic summary of the verify kernel from rocprofv3 --pmc "
+                         "output (FETCH_SIZE and WRITE_SIZE runs under PMC_DIR) to OUT, then exit")
     return ap.parse_args()
 
 
@@ -103,44 +111,115 @@ def traffic_record(kernel: str, workload: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 rec[k.strip()] = v.strip()
-    with open(KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
         return None
     return float(rec["hbm_bytes_per_dispatch"])
 
 
-def main() -> int:
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange but the outputs); run with --gpus 1",
-              file=sys.stderr)
-        return 2
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
-    import torch
 
+def _pmc_rows(pmc_dir: str):
+    """(dispatch id, kernel name, counter, value) of every dispatch in rocprofv3 counter CSVs under pmc_dir."""
+    import csv
+
+    for dirpath, _, files in os.walk(pmc_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, fn), newline="") as f:
+                    for row in csv.DictReader(f):
+                        yield (os.path.join(dirpath, fn), int(row["Dispatch_Id"])), row["Kernel_Name"], \
+                            row["Counter_Name"], float(row["Counter_Value"])
+
+
+def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int) -> int:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the verify kernel, scaled by a plain copy's.
+
+    The calibration copies are the first 8 __amd_rocclr_copyBuffer dispatches of
+    each run (bench.py --calibrate-copy-mb makes them before anything else is
+    copied); each moves copy_mb * 10^6 bytes each way. The ratio of that to what
+    the same counter reads for them is the factor applied to the verify kernel.
+    """
+    verify: dict = {}
+    copies: dict = {}
+    for key, name, ctr, val in sorted(_pmc_rows(pmc_dir)):
+        if "verify_kernel" in name:
+            verify.setdefault(ctr, []).append(val)
+        elif "copyBuffer" in name:
+            seen = copies.setdefault((key[0], ctr), [])
+            if len(seen) < 8:
+                seen.append(val)
+    copy_vals: dict = {}
+    for (_, ctr), vals in copies.items():
+        copy_vals.setdefault(ctr, []).extend(vals)
+    need = ["FETCH_SIZE", "WRITE_SIZE"]
+    missing = [c for c in need if c not in verify or len(copy_vals.get(c, [])) < 8]
+    if missing:
+        print(f"counters missing in {pmc_dir}: {missing}", file=sys.stderr)
+        return 1
+    mean = {("verify", c): float(np.mean(verify[c])) for c in need}
+    mean.update({("copy", c): float(np.mean(copy_vals[c])) for c in need})
+    copy_bytes = copy_mb * 1e6
+    f_fetch = copy_bytes / (mean[("copy", "FETCH_SIZE")] * 1024.0)
+    f_write = copy_bytes / (mean[("copy", "WRITE_SIZE")] * 1024.0)
+    fetch = mean[("verify", "FETCH_SIZE")] * 1024.0 * f_fetch
+    write = mean[("verify", "WRITE_SIZE")] * 1024.0 * f_write
+    text = "".join([
+        f"# HBM traffic of verify_kernel, workload {workload}, from two rocprofv3 --pmc runs\n",
+        "# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the dispatches of the run),\n",
+        f"# each scaled by the factor that maps the same counter on a plain {copy_mb} MB device copy\n",
+        "# (__amd_rocclr_copyBuffer, the run's first 8 copies) to its known size.\n",
+        f"verify_dispatches = {len(verify['FETCH_SIZE'])}\n",
+        f"verify_fetch_kib_per_dispatch = {mean[('verify', 'FETCH_SIZE')]:.1f}\n",
+        f"verify_write_kib_per_dispatch = {mean[('verify', 'WRITE_SIZE')]:.1f}\n",
+        f"copy_fetch_kib_per_dispatch = {mean[('copy', 'FETCH_SIZE')]:.1f}\n",
+        f"copy_write_kib_per_dispatch = {mean[('copy', 'WRITE_SIZE')]:.1f}\n",
+        f"copy_bytes_per_dispatch = {copy_bytes:.0f}\n",
+        f"fetch_scale = {f_fetch:.4f}\n",
+        f"write_scale = {f_write:.4f}\n",
+        f"hbm_fetch_bytes_per_dispatch = {fetch:.0f}\n",
+        f"hbm_write_bytes_per_dispatch = {write:.0f}\n",
+        f"hbm_bytes_per_dispatch = {fetch + write:.0f}\n",
+        f"kernel_source_sha256 = {kernel_source_sha()}\n",
+    ])
+    with open(out, "w") as f:
+        f.write(text)
+    print(text, end="")
+    return 0
+
+
+def calibration_copy(torch, dev, mb: int) -> None:
+    """A plain device-to-device copy of mb * 10^6 bytes, 8 times (the counters' scale reference)."""
+    n = mb * 1000 * 1000
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def device_logits(torch, a, dtype, dev):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(a)
+    return t.to(dev)
+
+
+def measure(torch, dev, name: str, args) -> dict:
+    """Time K calls of workload `name`; returns the numbers the JSON line reports."""
     import synth
     from speculative_sampling_verification_specv_amd import Verifier
 
-    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    dev = torch.device("cuda", 0)
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[name]
     batch = synth.make_batch(wl, args.seed)
     B, N, V = batch.batch, batch.n_draft, batch.vocab
-    e = wl.elem_bytes
-    copy_bytes = B * (2 * N + 1) * V * e
+    copy_bytes = B * (2 * N + 1) * V * wl.elem_bytes
     copies = args.copies or max(3, math.ceil(512e6 / copy_bytes))
-
-    def logits(a):
-        a = np.ascontiguousarray(a)
-        if batch.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
-        return torch.from_numpy(a)
-
-    d_host, t_host = logits(batch.draft_logits), logits(batch.target_logits)
-    sets = [(d_host.to(dev), t_host.to(dev)) for _ in range(copies)]
+    d0 = device_logits(torch, batch.draft_logits, batch.dtype, dev)
+    t0_ = device_logits(torch, batch.target_logits, batch.dtype, dev)
+    sets = [(d0, t0_)] + [(d0.clone(), t0_.clone()) for _ in range(copies - 1)]
     small = dict(draft_tokens=torch.from_numpy(batch.draft_tokens).to(dev),
                  accept_uniforms=torch.from_numpy(batch.accept_uniforms).to(dev),
                  sample_uniforms=torch.from_numpy(batch.sample_uniforms).to(dev),
@@ -160,42 +239,70 @@ def main() -> int:
     nbytes = algorithmic_bytes(batch, n_acc)
 
     # Timed region: K whole calls, bracketed by device synchronisation.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
     for k in range(args.steps):
         step(k)
-    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
-    ms_events = start.elapsed_time(end) / args.steps
 
-    # Per-kernel durations: HIP events the library records around each kernel
-    # on the launch stream (a separate pass; recording adds a little overhead).
+    # Per-kernel durations: HIP events the library records around its launch
+    # on the launch stream (a separate pass of K calls).
     v.set_timing(True)
-    sums = {}
+    per_call = {}
     for k in range(args.steps):
         step(k)
-        for name, ms in v.last_timings().items():
-            sums[name] = sums.get(name, 0.0) + ms
+        for st, ms in v.last_timings().items():
+            per_call.setdefault(st, []).append(ms)
     v.set_timing(False)
-    stage_ms = {k: s / args.steps for k, s in sums.items()}
+    v.close()
+    stage_ms = {k: float(np.mean(x)) for k, x in per_call.items()}
     dominant = max(stage_ms, key=stage_ms.get)
-    kernel_bytes = {"row_stats": nbytes["stats"]}.get(dominant, nbytes["reread"])
-    achieved = kernel_bytes / (stage_ms[dominant] * 1e-3) / 1e9
-    traffic = traffic_record(dominant, args.workload)
+    # The one launch does the whole call: its algorithmic bytes are the call's.
+    kernel_bytes = {"verify": nbytes["total"]}[dominant]
+    dom = np.asarray(per_call[dominant])
+    return dict(
+        workload=name, batch=batch, copies=copies, ms_per_step=ms_per_step, nbytes=nbytes,
+        stage_ms=stage_ms, dominant=dominant, kernel_bytes=kernel_bytes,
+        kernel_ms_p10=float(np.percentile(dom, 10)), kernel_ms_p50=float(np.percentile(dom, 50)),
+        kernel_ms_p90=float(np.percentile(dom, 90)),
+        achieved=kernel_bytes / (stage_ms[dominant] * 1e-3) / 1e9,
+        positions=B * N, n_accepted_mean=float(np.mean(n_acc)),
+    )
 
-    positions = B * N
+
+def main() -> int:
+    args = parse()
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                             args.calibrate_copy_mb or 256)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange but the outputs); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda", 0)
+    if args.calibrate_copy_mb:
+        calibration_copy(torch, dev, args.calibrate_copy_mb)
+
+    m = measure(torch, dev, args.workload, args)
+    batch, nbytes = m["batch"], m["nbytes"]
+    B, N, V = batch.batch, batch.n_draft, batch.vocab
+    ms = m["ms_per_step"]
     line = {
         "metric": METRIC,
-        "value": positions / (ms_per_step * 1e-3),
+        "value": m["positions"] / (ms * 1e-3),
         "unit": "verified draft positions/sec",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -203,24 +310,40 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_draft": N, "vocab": V, "logits": batch.dtype,
                    "temperature": sorted(set(float(x) for x in batch.temperature)), "seed": args.seed,
-                   "rotated_copies": copies},
+                   "rotated_copies": m["copies"]},
         "path": {
-            "hbm_gbs": nbytes["total"] / (ms_per_step * 1e-3) / 1e9,
-            "hbm_frac": nbytes["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "hbm_gbs": nbytes["total"] / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bytes_per_call": nbytes["total"],
             "formula_bytes_per_call": nbytes["formula"],
-            "ms_per_step_events": ms_events,
             "residual_seqs": nbytes["resid_seqs"],
             "bonus_seqs": nbytes["bonus_seqs"],
-            "stage_ms": stage_ms,
+            "mean_n_accepted": m["n_accepted_mean"],
+            "stage_ms": m["stage_ms"],
+            "kernel_ms_p10_p50_p90": [m["kernel_ms_p10"], m["kernel_ms_p50"], m["kernel_ms_p90"]],
         },
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": m["dominant"], "achieved": m["achieved"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": m["achieved"] / HBM_PEAK_GBS,
+                     "traffic": traffic_record(m["dominant"], args.workload)},
     }
+    also = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        a = measure(torch, dev, name, args)
+        also[name] = {
+            "positions_per_sec": a["positions"] / (a["ms_per_step"] * 1e-3),
+            "ms_per_step": a["ms_per_step"],
+            "bytes_per_call": a["nbytes"]["total"],
+            "formula_bytes_per_call": a["nbytes"]["formula"],
+            "hbm_gbs": a["nbytes"]["total"] / (a["ms_per_step"] * 1e-3) / 1e9,
+            "kernel_ms": a["stage_ms"][a["dominant"]],
+            "kernel_achieved_gbs": a["achieved"],
+            "kernel_frac": a["achieved"] / HBM_PEAK_GBS,
+            "traffic": traffic_record(a["dominant"], name),
+        }
+    if also:
+        line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
-    v.close()
     print(json.dumps(line), flush=True)
     return 0
 
