@@ -50,7 +50,7 @@ def parse():
                     help="first run a plain device-to-device copy of this many MB (8 times) so that a "
                          "rocprofv3 --pmc run of this command also measures a copy of known size")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "OUT"),
-                    help="write the HBM traffic summary of the verify kernel from rocprofv3 --pmc "
+                    help="write the HBM traffic summary of the row-statistics kernel from rocprofv3 --pmc "
                          "output (FETCH_SIZE and WRITE_SIZE runs under PMC_DIR) to OUT, then exit")
     return ap.parse_args()
 
@@ -134,8 +134,8 @@ def _pmc_rows(pmc_dir: str):
                             row["Counter_Name"], float(row["Counter_Value"])
 
 
-def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int) -> int:
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the verify kernel, scaled by a plain copy's.
+def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int, kernel: str = "row_stats") -> int:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of one kernel, scaled by a plain copy's.
 
     The calibration copies are the first 8 __amd_rocclr_copyBuffer dispatches of
     each run (bench.py --calibrate-copy-mb makes them before anything else is
@@ -145,7 +145,7 @@ def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int) -> int:
     verify: dict = {}
     copies: dict = {}
     for key, name, ctr, val in sorted(_pmc_rows(pmc_dir)):
-        if "verify_kernel" in name:
+        if f"{kernel}_kernel" in name:
             verify.setdefault(ctr, []).append(val)
         elif "copyBuffer" in name:
             seen = copies.setdefault((key[0], ctr), [])
@@ -167,13 +167,13 @@ def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int) -> int:
     fetch = mean[("verify", "FETCH_SIZE")] * 1024.0 * f_fetch
     write = mean[("verify", "WRITE_SIZE")] * 1024.0 * f_write
     text = "".join([
-        f"# HBM traffic of verify_kernel, workload {workload}, from two rocprofv3 --pmc runs\n",
+        f"# HBM traffic of {kernel}_kernel, workload {workload}, from two rocprofv3 --pmc runs\n",
         "# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the dispatches of the run),\n",
         f"# each scaled by the factor that maps the same counter on a plain {copy_mb} MB device copy\n",
         "# (__amd_rocclr_copyBuffer, the run's first 8 copies) to its known size.\n",
-        f"verify_dispatches = {len(verify['FETCH_SIZE'])}\n",
-        f"verify_fetch_kib_per_dispatch = {mean[('verify', 'FETCH_SIZE')]:.1f}\n",
-        f"verify_write_kib_per_dispatch = {mean[('verify', 'WRITE_SIZE')]:.1f}\n",
+        f"kernel_dispatches = {len(verify['FETCH_SIZE'])}\n",
+        f"kernel_fetch_kib_per_dispatch = {mean[('verify', 'FETCH_SIZE')]:.1f}\n",
+        f"kernel_write_kib_per_dispatch = {mean[('verify', 'WRITE_SIZE')]:.1f}\n",
         f"copy_fetch_kib_per_dispatch = {mean[('copy', 'FETCH_SIZE')]:.1f}\n",
         f"copy_write_kib_per_dispatch = {mean[('copy', 'WRITE_SIZE')]:.1f}\n",
         f"copy_bytes_per_dispatch = {copy_bytes:.0f}\n",
@@ -259,8 +259,10 @@ def measure(torch, dev, name: str, args) -> dict:
     v.close()
     stage_ms = {k: float(np.mean(x)) for k, x in per_call.items()}
     dominant = max(stage_ms, key=stage_ms.get)
-    # The one launch does the whole call: its algorithmic bytes are the call's.
-    kernel_bytes = {"verify": nbytes["total"]}[dominant]
+    # Algorithmic bytes of each launch: the row statistics read every row the
+    # method needs; the members re-read the draw's row(s); the finisher re-reads
+    # one sub-chunk (counted with the members' rows).
+    kernel_bytes = {"row_stats": nbytes["stats"], "members": nbytes["reread"], "finish": 0}[dominant]
     dom = np.asarray(per_call[dominant])
     return dict(
         workload=name, batch=batch, copies=copies, ms_per_step=ms_per_step, nbytes=nbytes,

@@ -76,7 +76,8 @@ enum specv_status {
  * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,
  * vocabulary size `vocab` (V >= 1) and logits stored as `dtype`, on HIP device
  * `device`. Allocates the scratch workspace on that device (size grows with
- * max_batch * (2*max_draft+1) * ceil(V/8192)). On success *out is set and
+ * max_batch * (2*max_draft+1) * ceil(V*dtype_bytes/32768) row partials plus
+ * max_batch * ceil(V*dtype_bytes/16384) draw records). On success *out is set and
  * SPECV_OK returned; on failure *out is NULL.
  * Errors: SPECV_EINVAL (out NULL, max_batch < 1, max_draft outside
  * [1, SPECV_MAX_DRAFT], vocab < 1 or > SPECV_MAX_VOCAB, unknown dtype, bad device),
@@ -130,16 +131,6 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
  * verify yet), SPECV_EHIP.
  */
 SPECV_API int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream);
-
-/*
- * Bound on the in-kernel waits of later specv_verify calls on this handle, in
- * microseconds (default 100). Workgroups of one call hand each other partial
- * results; one that has waited this long for a result computes it itself,
- * which gives the same bits, so the bound only trades time, never results.
- * 0 makes every waiting workgroup compute what it waits for at once (used to
- * test that path). Errors: SPECV_EINVAL (null handle, negative value).
- */
-SPECV_API int specv_set_wait_limit(specv_handle h, int microseconds);
 
 /*
  * Kernel timing (diagnostic). With enable != 0, every later specv_verify on

@@ -32,7 +32,6 @@ _SIGNATURES = {
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "specv_destroy": (None, [ctypes.c_void_p]),
     "specv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
-    "specv_set_wait_limit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
     "specv_set_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
     "specv_last_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int)]),
@@ -109,10 +108,6 @@ def specv_verify(handle: int, draft_logits, target_logits, draft_tokens, accept_
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:
     _check(load_library().specv_row_stats(handle, _ptr(out_lse), _ptr(out_argmax),
                                           _stream_ptr(stream, out_lse.device)), "specv_row_stats")
-
-
-def specv_set_wait_limit(handle: int, microseconds: int) -> None:
-    _check(load_library().specv_set_wait_limit(handle, int(microseconds)), "specv_set_wait_limit")
 
 
 def specv_set_timing(handle: int, enable: bool) -> None:
@@ -196,9 +191,6 @@ class Verifier:
                      temperature, out_tokens, out_n_accepted, stream)
         self._last = (B, N)
         return out_tokens, out_n_accepted
-
-    def set_wait_limit(self, microseconds: int) -> None:
-        specv_set_wait_limit(self.handle, microseconds)
 
     def set_timing(self, enable: bool) -> None:
         specv_set_timing(self.handle, enable)

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 #include "specv.h"
 #include "specv_internal.h"
@@ -22,9 +23,6 @@ struct specv_ctx {
   void* mem;  // one device allocation holding the whole workspace
   size_t mem_bytes;
   specv::Workspace ws;
-  size_t records_bytes;  // leading part of mem holding the inter-workgroup records
-  uint32_t epoch;        // sequence number of the last call (records carry it)
-  uint64_t wait_ticks;   // bound on in-kernel waits, 100 MHz ticks
   int last_batch;        // -1 until a verify succeeds
   int last_n_draft;
   bool timing;                               // record stage events on every verify
@@ -56,11 +54,6 @@ class DeviceGuard {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// In-kernel waits give up after 100 us (then the waiting workgroup computes
-// what it waited for itself).
-constexpr uint64_t kTicksPerMicrosecond = 100;  // the 100 MHz wall clock the kernels read
-constexpr uint64_t kDefaultWaitTicks = 100 * kTicksPerMicrosecond;
-
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
@@ -89,21 +82,21 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
   if (device < 0 || device >= n_dev) return SPECV_EINVAL;
 
-  const int chunk = specv::stats_chunk_elems(dtype);
+  const int chunk = specv::stat_chunk_elems(dtype);
   const int nch = specv::ceil_div(vocab, chunk);
-  const int nsch = specv::ceil_div(vocab, specv::kSampChunk);
-  if (specv::grid_blocks(max_batch, max_draft, nch, nsch) >= (int64_t(1) << 31)) return SPECV_EINVAL;
+  const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
+  // Grids: one workgroup per row-statistics item, per draw member.
+  if (int64_t(rows) * nch >= (int64_t(1) << 31) || int64_t(max_batch) * nm >= (int64_t(1) << 31))
+    return SPECV_EINVAL;
+
   size_t off = 0;
   const size_t off_partials = off;
-  off = align_up(off + rows * nch * specv::kPartWords * sizeof(uint64_t), 256);
+  off = align_up(off + rows * nch * specv::partial_bytes(), 256);
   const size_t off_seq = off;
-  off = align_up(off + size_t(max_batch) * specv::kSeqWords * sizeof(uint64_t), 256);
-  const size_t off_norm = off;
-  off = align_up(off + size_t(max_batch) * nsch * specv::kNormWords * sizeof(uint64_t), 256);
-  const size_t records_bytes = off;
-  const size_t off_table = off;
-  off = align_up(off + specv::kExpTableSize * sizeof(double), 256);
+  off = align_up(off + size_t(max_batch) * specv::seq_bytes(), 256);
+  const size_t off_records = off;
+  off = align_up(off + size_t(max_batch) * nm * specv::member_bytes(), 256);
   const size_t off_lse = off;
   off = align_up(off + rows * sizeof(float), 256);
   const size_t off_argmax = off;
@@ -125,27 +118,19 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->vocab = vocab;
   h->dtype = dtype;
   h->mem_bytes = off;
-  h->records_bytes = records_bytes;
-  h->ws.partials = reinterpret_cast<uint64_t*>(base + off_partials);
-  h->ws.seq = reinterpret_cast<uint64_t*>(base + off_seq);
-  h->ws.norm = reinterpret_cast<uint64_t*>(base + off_norm);
-  h->ws.exp_table = reinterpret_cast<double*>(base + off_table);
+  h->ws.partials = base + off_partials;
+  h->ws.seq = base + off_seq;
+  h->ws.records = base + off_records;
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
   h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
-  h->ws.n_stats_chunks = nch;
-  h->ws.n_samp_chunks = nsch;
-  h->ws.stats_chunk = chunk;
-  double table[specv::kExpTableSize];
-  for (int j = 0; j < specv::kExpTableSize; ++j) table[j] = double(exp2l((long double)j / specv::kExpTableSize));
-  // Records start with sequence number 0, which no call uses.
-  if (hipMemset(h->mem, 0, off) != hipSuccess ||
-      hipMemcpy(h->ws.exp_table, table, sizeof table, hipMemcpyHostToDevice) != hipSuccess) {
+  h->ws.n_stat_chunks = nch;
+  h->ws.n_members = nm;
+  h->ws.stat_chunk = chunk;
+  if (hipMemset(h->mem, 0, off) != hipSuccess) {
     (void)hipFree(h->mem);
     delete h;
     return SPECV_EHIP;
   }
-  h->epoch = 0;
-  h->wait_ticks = kDefaultWaitTicks;
   h->last_batch = -1;
   h->last_n_draft = 0;
   h->timing = false;
@@ -174,13 +159,6 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   DeviceGuard guard(h->device);
   if (!guard.ok()) return SPECV_EHIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t epoch = h->epoch + 1;
-  if (epoch == 0) {
-    // The sequence number wrapped: clear the records so no stale word can
-    // carry a number that comes round again.
-    if (specv::clear_records(h->mem, h->records_bytes, s) != hipSuccess) return SPECV_EHIP;
-    epoch = 1;
-  }
   specv::VerifyArgs a;
   a.batch = batch;
   a.n_draft = n_draft;
@@ -194,11 +172,8 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
-  a.epoch = epoch;
-  a.wait_ticks = h->wait_ticks;
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, h->timing ? h->events : nullptr, &stages) != hipSuccess) return SPECV_EHIP;
-  h->epoch = epoch;
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;
@@ -218,12 +193,6 @@ int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* s
     return SPECV_EHIP;
   if (hipMemcpyAsync(out_argmax, h->ws.row_argmax, n * sizeof(int), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return SPECV_EHIP;
-  return SPECV_OK;
-}
-
-int specv_set_wait_limit(specv_handle h, int microseconds) {
-  if (h == nullptr || microseconds < 0) return SPECV_EINVAL;
-  h->wait_ticks = uint64_t(microseconds) * kTicksPerMicrosecond;
   return SPECV_OK;
 }
 
@@ -259,6 +228,8 @@ int specv_last_timings(specv_handle h, float* ms, int capacity, int* count) {
 }
 
 const char* specv_stage_name(int stage) { return specv::stage_name(stage); }
+
+
 
 void specv_destroy(specv_handle h) {
   if (h == nullptr) return;

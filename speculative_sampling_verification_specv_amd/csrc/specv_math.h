@@ -1,4 +1,4 @@
-// fp64 exponential shared by the kernels; also compiled by a plain host
+// fp64 exponential used by the draw kernels; also compiled by a plain host
 // compiler for its unit test.
 #pragma once
 
@@ -8,13 +8,11 @@
 #define __host__
 #define __device__
 #endif
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
 namespace specv {
-
-// 2^(j/256), j = 0..255, rounded to double (filled by the host).
-constexpr int kExpTableSize = 256;
 
 __host__ __device__ inline double bits_to_double(uint64_t u) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -36,28 +34,41 @@ __host__ __device__ inline uint64_t double_to_bits(double d) {
 #endif
 }
 
-// exp(a) for a <= 0 in fp64, table-driven (Tang's method): a = (256n + j) ln2/256 + r
-// with |r| <= ln2/512, exp(a) = 2^n * 2^(j/256) * exp(r), and exp(r) - 1 by its
-// degree-3 Taylor polynomial (truncation below 1.5e-13 relative). Rounding
-// a*256/ln2 to an integer uses the 1.5*2^52 shifter, whose low word then holds
-// it; one fma reduces with ln2/256 rounded to double (error below 1e-13 for
-// a >= -708). The power of two is applied by adding n to the exponent field,
-// valid because results stay normal for a >= -708; below that (including
-// -inf) the result is 0, which only drops terms under 3.3e-308 of the row
-// maximum. NaN gives 0. Relative error below 3e-13.
-__host__ __device__ inline double exp_nonpos(double a, const double* __restrict__ table) {
-  const double kShift = 6755399441055744.0;      // 1.5 * 2^52
-  const double kInvStep = 369.3299304675746;     // 256 / ln 2
-  const double kStep = 0x1.62e42fefa39efp-9;     // ln2 / 256
-  const double t = fma(a, kInvStep, kShift);
+// exp(a) for a <= 0 in fp64, without tables (registers only, so independent
+// calls overlap freely): a = n ln2 + r with n = rint(a / ln2) and
+// |r| <= ln2/2, exp(a) = 2^n exp(r). n comes from the 1.5*2^52 shifter (the
+// low word of the shifted value holds it); r from a two-part ln2 (Cody and
+// Waite: n * ln2_hi is exact for |n| < 2^11, the low part adds 1e-16
+// relative); exp(r) from its degree-11 Taylor polynomial evaluated by
+// Estrin's scheme (truncation below 1e-14 relative on |r| <= ln2/2); 2^n by
+// ldexp. Below a = -708 (and for -inf or NaN) the result is 0, which drops
+// only terms under 3.3e-308 of the row maximum. Relative error below 1e-13.
+__host__ __device__ inline double exp_nonpos(double a) {
+  const double kShift = 6755399441055744.0;         // 1.5 * 2^52
+  const double kInvLn2 = 1.4426950408889634;        // 1 / ln 2
+  const double kLn2Hi = 6.93147180369123816490e-01;  // ln 2, upper bits (low 32 bits zero)
+  const double kLn2Lo = 1.90821492927058770002e-10;  // ln 2 - kLn2Hi
+  const double t = fma(a, kInvLn2, kShift);
   const double kd = t - kShift;
-  const int32_t k = static_cast<int32_t>(static_cast<uint32_t>(double_to_bits(t)));
-  const double r = fma(kd, -kStep, a);
-  const double q = fma(fma(r, 1.0 / 6.0, 0.5), r, 1.0) * r;  // exp(r) - 1
-  const double base = table[k & (kExpTableSize - 1)];
-  const double res = fma(base, q, base);
-  const uint64_t scaled = double_to_bits(res) + (static_cast<uint64_t>(static_cast<int64_t>(k >> 8)) << 52);
-  return (a >= -708.0) ? bits_to_double(scaled) : 0.0;
+  const int32_t n = static_cast<int32_t>(static_cast<uint32_t>(double_to_bits(t)));
+  double r = fma(kd, -kLn2Hi, a);
+  r = fma(kd, -kLn2Lo, r);
+  // Estrin's scheme: pairs, then pairs of pairs (a short dependency chain).
+  const double r2 = r * r;
+  const double r4 = r2 * r2;
+  const double r8 = r4 * r4;
+  const double q0 = fma(r, 1.0, 1.0);                      // 1 + r
+  const double q1 = fma(r, 1.0 / 6.0, 0.5);                // 1/2! + r/3!
+  const double q2 = fma(r, 1.0 / 120.0, 1.0 / 24.0);       // 1/4! + r/5!
+  const double q3 = fma(r, 1.0 / 5040.0, 1.0 / 720.0);     // 1/6! + r/7!
+  const double q4 = fma(r, 1.0 / 362880.0, 1.0 / 40320.0);  // 1/8! + r/9!
+  const double q5 = fma(r, 1.0 / 39916800.0, 1.0 / 3628800.0);  // 1/10! + r/11!
+  const double s0 = fma(q1, r2, q0);
+  const double s1 = fma(q3, r2, q2);
+  const double s2 = fma(q5, r2, q4);
+  const double p = fma(s2, r8, fma(s1, r4, s0));
+  const double res = ldexp(p, n);
+  return (a >= -708.0) ? res : 0.0;
 }
 
 }  // namespace specv
