@@ -50,7 +50,7 @@ def parse():
                     help="first run a plain device-to-device copy of this many MB (8 times) so that a "
                          "rocprofv3 --pmc run of this command also measures a copy of known size")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "OUT"),
-                    help="write the HBM traffic summary of the row-statistics kernel from rocprofv3 --pmc "
+                    help="write the HBM traffic summary of the verification kernel from rocprofv3 --pmc "
                          "output (FETCH_SIZE and WRITE_SIZE runs under PMC_DIR) to OUT, then exit")
     return ap.parse_args()
 
@@ -134,7 +134,7 @@ def _pmc_rows(pmc_dir: str):
                             row["Counter_Name"], float(row["Counter_Value"])
 
 
-def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int, kernel: str = "row_stats") -> int:
+def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int, kernel: str = "verify") -> int:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of one kernel, scaled by a plain copy's.
 
     The calibration copies are the first 8 __amd_rocclr_copyBuffer dispatches of
@@ -259,10 +259,10 @@ def measure(torch, dev, name: str, args) -> dict:
     v.close()
     stage_ms = {k: float(np.mean(x)) for k, x in per_call.items()}
     dominant = max(stage_ms, key=stage_ms.get)
-    # Algorithmic bytes of each launch: the row statistics read every row the
-    # method needs; the members re-read the draw's row(s); the finisher re-reads
-    # one sub-chunk (counted with the members' rows).
-    kernel_bytes = {"row_stats": nbytes["stats"], "members": nbytes["reread"], "finish": 0}[dominant]
+    # Algorithmic bytes of the launch: every row the method needs once, plus
+    # the draw's re-read of the drawn row(s) (the finishers' rescan of one
+    # sub-chunk per sequence is counted with them).
+    kernel_bytes = {"verify": nbytes["stats"] + nbytes["reread"]}[dominant]
     dom = np.asarray(per_call[dominant])
     return dict(
         workload=name, batch=batch, copies=copies, ms_per_step=ms_per_step, nbytes=nbytes,

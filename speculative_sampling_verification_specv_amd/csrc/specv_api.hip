@@ -86,9 +86,8 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const int nch = specv::ceil_div(vocab, chunk);
   const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
-  // Grids: one workgroup per row-statistics item, per draw member.
-  if (int64_t(rows) * nch >= (int64_t(1) << 31) || int64_t(max_batch) * nm >= (int64_t(1) << 31))
-    return SPECV_EINVAL;
+  // Grid: one workgroup per row-statistics item and per draw member.
+  if (int64_t(rows) * nch + int64_t(max_batch) * nm >= (int64_t(1) << 31)) return SPECV_EINVAL;
 
   size_t off = 0;
   const size_t off_partials = off;
@@ -101,6 +100,8 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   off = align_up(off + rows * sizeof(float), 256);
   const size_t off_argmax = off;
   off = align_up(off + rows * sizeof(int), 256);
+  const size_t off_counters = off;
+  off = align_up(off + 2 * size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
 
   DeviceGuard guard(device);
   if (!guard.ok()) return SPECV_EHIP;
@@ -123,10 +124,13 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->ws.records = base + off_records;
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
   h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
+  h->ws.stat_done = reinterpret_cast<int*>(base + off_counters);
+  h->ws.draw_done = h->ws.stat_done + size_t(max_batch) * specv::kCounterStride;
   h->ws.n_stat_chunks = nch;
   h->ws.n_members = nm;
   h->ws.stat_chunk = chunk;
-  if (hipMemset(h->mem, 0, off) != hipSuccess) {
+  h->ws.resident_blocks = specv::max_resident_blocks(dtype);
+  if (h->ws.resident_blocks < 1 || hipMemset(h->mem, 0, off) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->mem);
     delete h;
     return SPECV_EHIP;

@@ -10,9 +10,9 @@ namespace specv {
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64s)
 constexpr int kStatBytes = 32768;  // row-statistics item: 32 KB of one row, either dtype
 
-// A draw member covers 16 KB of each row it reads: 8192 bfloat16 or 4096
+// A draw member covers 8 KB of each row it reads: 4096 bfloat16 or 2048
 // float32 logits, split into kSubs sub-chunks of 32 consecutive threads.
-constexpr int kMemberBytes = 16384;
+constexpr int kMemberBytes = 8192;
 inline int member_elems(int dtype) { return kMemberBytes / (dtype == 0 ? 4 : 2); }
 constexpr int kMinMemberElems = kMemberBytes / 4;
 constexpr int kSubs = 8;
@@ -29,6 +29,8 @@ constexpr float kMinTemperature = 0x1p-60f;
 
 inline int stat_chunk_elems(int dtype) { return kStatBytes / (dtype == 0 ? 4 : 2); }
 
+constexpr int kCounterStride = 64;
+
 enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
 // Device workspace: records one launch writes and the next reads.
@@ -38,7 +40,14 @@ struct Workspace {
   void* records;     // [max_batch][n_members] draw-member records
   float* row_lse;    // [batch][2N+1] of the last call
   int* row_argmax;   // [batch][2N+1] of the last call
+  // Per sequence, how many workgroups of a launch are done with it; the last
+  // one resets its count to zero. Zero between calls. One counter per
+  // kCounterStride ints (its own 256-byte line), so that atomics on different
+  // sequences' counters never contend for a line.
+  int* stat_done;    // [max_batch * kCounterStride] row-statistics items
+  int* draw_done;    // [max_batch * kCounterStride] draw members
   int n_stat_chunks;
+  int resident_blocks;  // workgroups of the verification kernel the device holds at once
   int n_members;     // draw members per sequence
   int stat_chunk;    // logits per row-statistics item
 };
@@ -61,6 +70,11 @@ struct VerifyArgs {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kMaxStages = 8;
+
+
+// Workgroups of the verification kernel for `dtype` the current device holds
+// at once (-1 on a HIP error).
+int max_resident_blocks(int dtype);
 
 // Names of the kernel stages launch_verify enqueues, in order.
 const char* stage_name(int stage);

@@ -6,21 +6,22 @@
 // (Speculative Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
 // verification loop.
 //
-// Three launches per call, in order on the caller's stream; each one's
-// results are complete and visible when the next starts, so workgroups never
-// wait for each other:
+// Two launches per call, in order on the caller's stream; the second starts
+// when the first's results are complete and visible. Within a launch no
+// workgroup waits for another: per sequence, the workgroup that reports last
+// on an atomic counter carries on with what needs all of them.
 //
 //   row_stats  one workgroup per row-statistics item (32 KB of one row):
 //              fp32 max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T, first
 //              argmax, and the logit at the row's draft token. Pure streaming,
-//              HBM-bound; greedy sequences skip their draft rows.
-//   members    one workgroup per (sequence, 16 KB chunk of a row): merges the
-//              sequence's row partials into log-normalisers, takes the N
-//              accept decisions (member 0 writes them out, and the token
-//              itself when greedy), then sums fp64 exps of its chunk of the
-//              draw's row(s) into a member record.
-//   finish     one workgroup per sequence: from the member records, the fp64
-//              normalisers and sub-chunk weights, the sub-chunk where the
+//              HBM-bound; greedy sequences skip their draft rows. The last
+//              item of a sequence merges its row partials into
+//              log-normalisers, takes the N accept decisions and writes them
+//              out (the token itself when greedy) with the draw's record.
+//   draw       one workgroup per (sequence, 8 KB chunk of the draw's row(s)):
+//              fp64 exps of the chunk summed into a member record. The last
+//              member of a sequence is its finisher: the fp64 normalisers and
+//              sub-chunk weights from the records, the sub-chunk where the
 //              inverse CDF crosses u*S, an exact rescan of it, the token.
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
@@ -57,16 +58,26 @@ __device__ __forceinline__ float scaled_max(float m, float c) { return __fmul_rn
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Diagnostic builds (-DSPECV_TRACE) stamp the wall clock (100 MHz) at fixed
-// points of each members / finish workgroup.
+// points of each workgroup's work: kernel 0 the draw members (sequence * nm +
+// member), 1 the finishers (sequence), 2 the row-statistics items (sequence *
+// items per sequence + item).
 #if defined(SPECV_TRACE)
 constexpr int kTraceSlots = 8;
 constexpr int kTraceBlocks = 1 << 16;
-__device__ uint64_t g_trace[2][kTraceBlocks * kTraceSlots];
+__device__ uint64_t g_trace[3][kTraceBlocks * kTraceSlots];
+__shared__ unsigned g_trace_idx;
+__device__ __forceinline__ void trace_at(int kernel, unsigned idx, int slot) {
+  if (threadIdx.x == 0 && idx < kTraceBlocks) g_trace[kernel][idx * kTraceSlots + slot] = wall_clock64();
+}
+__device__ __forceinline__ void trace_set(unsigned idx) {
+  if (threadIdx.x == 0) g_trace_idx = idx;
+}
 __device__ __forceinline__ void trace(int kernel, int slot) {
-  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)
-    g_trace[kernel][blockIdx.x * kTraceSlots + slot] = wall_clock64();
+  if (threadIdx.x == 0) trace_at(kernel, g_trace_idx, slot);
 }
 #else
+__device__ __forceinline__ void trace_at(int, unsigned, int) {}
+__device__ __forceinline__ void trace_set(unsigned) {}
 __device__ __forceinline__ void trace(int, int) {}
 #endif
 
@@ -120,7 +131,7 @@ struct Logit;
 template <>
 struct Logit<float> {
   static constexpr int kVec = 4;   // logits per 16-byte load
-  static constexpr int kPer = 16;  // logits of one row per draw-member thread (64 bytes)
+  static constexpr int kPer = 8;  // logits of one row per draw-member thread (32 bytes)
   __device__ static float at(const float* p, int64_t i) { return p[i]; }
   __device__ static uint32_t bits(const float* p, int64_t i) { return __float_as_uint(p[i]); }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b); }
@@ -144,7 +155,7 @@ struct Logit<float> {
 template <>
 struct Logit<uint16_t> {  // bfloat16 bits
   static constexpr int kVec = 8;
-  static constexpr int kPer = 32;
+  static constexpr int kPer = 16;
   __device__ static float at(const uint16_t* p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
   __device__ static uint32_t bits(const uint16_t* p, int64_t i) { return p[i]; }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
@@ -363,17 +374,45 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c, StatShared& sh)
   }
 }
 
-// Records written by one launch and read by the next.
-struct PartialRec {  // one (row, chunk) of row statistics
+// ---------------------------------------------------------------------------
+// Device-coherent words. Records that one workgroup hands to another within a
+// launch are written and read only as agent-scope relaxed atomics: these
+// bypass the per-XCD L2s' stale or dirty copies, so no L2 write-back or
+// invalidation (what an agent-scope release or acquire fence costs) is ever
+// needed. A writer waits for its record stores to complete before it reports
+// on the unit's counter (last_arrival), and a reader loads a record only
+// after the counter told it that every writer has reported.
+
+__device__ __forceinline__ void put_u64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_u64(const void* p) {
+  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_d(double* p, double v) { put_u64(p, double_to_bits(v)); }
+__device__ __forceinline__ double get_d(const double* p) { return bits_to_double(get_u64(p)); }
+__device__ __forceinline__ void put_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int get_i(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+  return uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
+}
+
+// Records written by one workgroup and read by another (or the next launch).
+struct alignas(16) PartialRec {  // one (row, chunk) of row statistics
   float m, s;        // max logit, sum of 2^(z*c - fl(m*c))
   int idx;           // first argmax
   float zg;          // logit at the row's draft token (0 if not in the chunk)
 };
-struct SeqRec {  // one sequence's decision
-  int mode, j;
-  float mt, md;    // maxima of target row j and draft row j
-  double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums
+struct SeqRec {     // one sequence's decision, published for its draw members
+  uint64_t flag;    // kPublished | j << 8 | mode, written after the other words; 0 between calls
+  uint64_t maxima;  // maxima of target row j (low half) and draft row j
+  double log_rho;   // log(Zt/Zd) of row j from the fp32 row sums
 };
+constexpr uint64_t kPublished = uint64_t(1) << 63;
 struct MemberRec {  // one draw member's fp64 sums
   double zt, zd;                  // sums of the target and draft exps
   double a[kSubs], bs[kSubs];     // per sub-chunk: sums of et and ed of certainly positive weight
@@ -397,7 +436,10 @@ struct Params {
   PartialRec* partials;  // [batch][2N+1][nch]
   SeqRec* seq;           // [batch]
   MemberRec* records;    // [batch][nm]
-  int64_t n_items;       // row-statistics items: batch * (2N+1) * nch
+  int* stat_done;        // [batch * kCounterStride] row-statistics items done (zero between launches)
+  int* draw_done;        // [batch * kCounterStride] draw members done (zero between launches)
+  int items_per_seq;     // row-statistics items per sequence: (2N+1) * nch
+  int lag;               // draw members of sequence b follow the row statistics of sequence b + lag
   int batch;
   int n_draft;
   int vocab;
@@ -436,7 +478,6 @@ __device__ __forceinline__ Item item_at(const Params& P, int64_t t) {
   constexpr int kVec = Logit<T>::kVec;
   Item it;
   it.live = false;
-  if (t >= P.n_items) return it;
   const int N = P.n_draft;
   const int R = 2 * N + 1;
   const int64_t rc = t / P.nch;
@@ -547,23 +588,58 @@ __device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g
 
 // Thread 0 stores an item's partial.
 __device__ __forceinline__ void item_write(const Params& P, const Item& it, const Partial& q) {
-  if (threadIdx.x == 0) *partial_at(P, it.b, it.r, it.c) = PartialRec{q.m, q.s, q.idx, q.zg};
+  if (threadIdx.x == 0) {
+    PartialRec* r = partial_at(P, it.b, it.r, it.c);
+    put_u64(&r->m, pack2(q.m, q.s));
+    put_u64(&r->idx, pack2(__int_as_float(q.idx), q.zg));
+  }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(Params P) {
-  __shared__ StatShared sh;
-  const Item it = item_at<T>(P, int64_t(blockIdx.x));
-  if (!it.live) return;
-  ItemRegs g;
-  item_load<T>(P, it, g);
-  item_write(P, it, item_reduce<T>(it, g, sh));
+
+// ---------------------------------------------------------------------------
+// Hand-over between the workgroups of one launch.
+
+__shared__ int g_last;
+
+// Counts this workgroup as done with a unit that `total` workgroups of the
+// launch each report once. Returns true, in every thread, in the workgroup that
+// reports last, which resets the count to zero for the next launch. Each
+// thread's record stores (device-coherent words) have completed before the
+// workgroup reports, so the last one reads every record complete. No
+// workgroup ever waits for another.
+__device__ __forceinline__ bool last_arrival(int* count, int total) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g_last = (prev == total - 1);
+    if (prev == total - 1) put_i(count, 0);
+  }
+  __syncthreads();
+  return g_last != 0;
 }
 
 // ---------------------------------------------------------------------------
 // Decision.
 
-constexpr int kStageParts = 1024;  // row partials the decision holds in LDS at once
+// Publishes sequence b's decision for its draw members: the data words, then
+// (once they are complete) the flag word. Only sampled sequences (T > 0) have
+// draw members waiting; the last of them clears the flag again, so it reads
+// zero at every call's start (also when a captured launch is replayed).
+__device__ __forceinline__ void publish(const Params& P, int b, int mode, int j, float mt, float md,
+                                        double log_rho) {
+  SeqRec* q = P.seq + b;
+  put_u64(&q->maxima, pack2(mt, md));
+  put_d(&q->log_rho, log_rho);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  put_u64(&q->flag, kPublished | (uint32_t(j) << 8) | uint32_t(mode));
+}
+
+// Whether sequence b's draw members wait for its decision: a positive valid
+// temperature (invalid tokens still give it a decision, with no draw).
+__device__ __forceinline__ bool has_draw_members(float t) { return t > 0.0f && temperature_valid(t); }
+
+constexpr int kStageParts = 256;  // row partials the decision holds in LDS at once
 
 struct DecideShared {
   float row_m[kMaxRows];
@@ -571,16 +647,19 @@ struct DecideShared {
   int row_idx[kMaxRows];
   float row_zg[kMaxRows];
   PartialRec part[kStageParts];
+  int tok[kMaxRows / 2];
   unsigned long long rej_mask;
 };
+static_assert(kStageParts == kThreads, "one staged row partial per thread");
+static_assert(int64_t(kMaxVocab) * 4 / kStatBytes <= kStageParts, "a row's partials fit one group");
 
 struct DrawShared {
   double red[4 * kWaves];
   double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
   double unc_ed[2][kThreads];
   int unc_base[kWaves];
-  int nunc[kMaxMembers];        // finisher: per member its uncertain count
-  double w[kMaxMembers * kSubs];  // finisher: per sub-chunk its weight
+  int nunc[kMaxMembers];  // finisher: per member its uncertain count
+  int slots[kWaves];
   int pick;
   double rem;
 };
@@ -593,6 +672,8 @@ struct Shared {
   } u;
 };
 
+__shared__ Shared g_shared;
+
 struct SeqInfo {
   int mode;
   int j;
@@ -601,17 +682,17 @@ struct SeqInfo {
   double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
 };
 
-// The decision for sequence b: per-row log-normalisers and argmaxes from the
-// row partials, the N accept tests, the first rejection. Every member of the
-// sequence computes it; with `write` (member 0) it writes the accepted prefix
-// (and the token itself when greedy), n_accepted, the row diagnostics and the
-// sequence record the finisher reads.
+// The decision for sequence b (whole workgroup, once per sequence): per-row
+// log-normalisers and argmaxes from the row partials, the N accept tests, the
+// first rejection. Writes the accepted prefix (and the token itself when
+// greedy), n_accepted, the row diagnostics and the sequence record the draw
+// reads.
 //
 // The normalisers come from fp32 row sums (relative error ~1e-6); logs and
 // the ratio are taken in fp64, so a decision can only differ from exact
 // arithmetic when u is within a few 1e-6 of the ratio.
 template <typename T>
-__device__ __forceinline__ SeqInfo decide(const Params& P, Shared& sh, int b, bool write) {
+__device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   DecideShared& ds = sh.u.dec;
   const int N = P.n_draft;
   const int R = 2 * N + 1;
@@ -622,60 +703,71 @@ __device__ __forceinline__ SeqInfo decide(const Params& P, Shared& sh, int b, bo
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   float* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  const float t = P.temperature[b];
-  SeqInfo rec{kModeNone, 0, 0.0f, 0.0f, 0.0};
-
-  int d = 0;
-  float ua = 0.0f;
-  bool bad = !temperature_valid(t);
-  if (tid < N) {
-    d = tok[tid];
-    bad = bad || d < 0 || d >= P.vocab;
-    ua = P.accept_u[int64_t(b) * N + tid];
-  }
-  if (block_any(bad)) {
-    if (write) {
-      for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
-      for (int r = tid; r < R; r += kThreads) {
-        lse[r] = NAN;
-        amax[r] = -1;
-      }
-      if (tid == 0) {
-        P.out_n[b] = -1;
-        P.seq[b] = SeqRec{kModeNone, 0, 0.0f, 0.0f, 0.0};
-      }
+  // Everything the decision reads is requested at once (unconditional loads
+  // at clamped addresses): the first group of row partials, the draft tokens,
+  // the accept uniforms, the temperature.
+  const int rows_per_group = max(1, kStageParts / P.nch);
+  const PartialRec* part_b = P.partials + int64_t(b) * R * P.nch;
+  const PartialRec* q0 = part_b + min(tid, min(rows_per_group, R) * P.nch - 1);
+  uint64_t pw0 = get_u64(&q0->m), pw1 = get_u64(&q0->idx);
+  const int ti = min(tid, N - 1);
+  const int d = tok[ti];
+  const float ua = P.accept_u[int64_t(b) * N + ti];
+  const float t = load_uniform(P.temperature + b);
+  if (tid < N) ds.tok[tid] = d;
+  if (block_any(!temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab)))) {
+    for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
+    for (int r = tid; r < R; r += kThreads) {
+      lse[r] = NAN;
+      amax[r] = -1;
     }
-    barrier();
-    return rec;
+    if (tid == 0) {
+      P.out_n[b] = -1;
+      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0);
+    }
+    return;
   }
+  trace(2, 4);
   const bool greedy = (t == 0.0f);
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
 
-  // The row partials, a group of rows at a time: every thread loads partials
-  // tid, tid + kThreads, ... of the group; then waves merge rows wave,
-  // wave+4, ... of the group: lanes take chunks lane, lane+64, ..., then a
-  // fixed butterfly.
-  const int rows_per_group = max(1, kStageParts / P.nch);
-  for (int rg = r_first; rg < R; rg += rows_per_group) {
+  // The row partials, a group of rows at a time: thread i holds partial i of
+  // the group; then the group's rows are merged (greedy sequences only their
+  // target rows) in a fixed order.
+  int cs = 1;
+  while (cs < P.nch) cs <<= 1;
+  const int rows_per_wave = 64 / cs;
+  const int seg = lane / cs, k_in_seg = lane - seg * cs;
+  for (int rg = 0; rg < R; rg += rows_per_group) {
     const int nr = min(rows_per_group, R - rg);
     const int np = nr * P.nch;
-    for (int i = tid; i < np; i += kThreads) ds.part[i] = P.partials[(int64_t(b) * R + rg) * P.nch + i];
+    if (rg > 0) {
+      const PartialRec* q = part_b + int64_t(rg) * P.nch + min(tid, np - 1);
+      pw0 = get_u64(&q->m);
+      pw1 = get_u64(&q->idx);
+    }
+    if (tid < np)
+      ds.part[tid] = PartialRec{__uint_as_float(uint32_t(pw0)), __uint_as_float(uint32_t(pw0 >> 32)),
+                                int(uint32_t(pw1)), __uint_as_float(uint32_t(pw1 >> 32))};
     barrier();
-    for (int rr = wave; rr < nr; rr += kWaves) {
+    // Segments of cs lanes (nch rounded up to a power of two) each merge one
+    // row: lane k of a segment holds chunk k, then a butterfly within the
+    // segment. A wave takes 64 / cs rows at a time.
+    for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
+      const int rr = r0 + seg;
       const int r = rg + rr;
+      const bool row_ok = rr < nr && r >= r_first;
       float m = -INFINITY, s = 0.0f;
       int idx = INT_MAX;
-      for (int k = lane; k < P.nch; k += 64) {
-        const PartialRec& q = ds.part[rr * P.nch + k];
-        if (greedy)
-          acc_merge<false>(m, s, idx, q.m, q.s, q.idx, c);
-        else
-          acc_merge<true>(m, s, idx, q.m, q.s, q.idx, c);
+      if (row_ok && k_in_seg < P.nch) {
+        const PartialRec& q = ds.part[rr * P.nch + k_in_seg];
+        m = q.m;
+        s = q.s;
+        idx = q.idx;
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
+      for (int off = 1; off < cs; off <<= 1) {
         const float m2 = __shfl_xor(m, off);
         const float s2 = __shfl_xor(s, off);
         const int i2 = __shfl_xor(idx, off);
@@ -684,23 +776,22 @@ __device__ __forceinline__ SeqInfo decide(const Params& P, Shared& sh, int b, bo
         else
           acc_merge<true>(m, s, idx, m2, s2, i2, c);
       }
-      if (lane == 0) {
+      if (row_ok && k_in_seg == 0) {
         if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
         // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c) exactly.
         const double logz = greedy ? 0.0 : kLn2 * (log2(double(s)) - double(fmaf(m, c, -scaled_max(m, c))));
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * P.nch + tok[r < N ? r : r - N] / P.chunk].zg : 0.0f;
-        if (write) {
-          lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
-          amax[r] = idx;
-        }
+        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * P.nch + ds.tok[r < N ? r : r - N] / P.chunk].zg : 0.0f;
+        lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
+        amax[r] = idx;
       }
     }
     barrier();
   }
-  if (greedy && write) {
+  trace(2, 5);
+  if (greedy) {
     for (int r = tid; r < N; r += kThreads) {
       lse[r] = NAN;
       amax[r] = -1;
@@ -728,29 +819,24 @@ __device__ __forceinline__ SeqInfo decide(const Params& P, Shared& sh, int b, bo
     if (lane == 0) ds.rej_mask = rej;
   }
   barrier();
+  trace(2, 6);
   const unsigned long long rej = ds.rej_mask;
   const int j = rej ? (__ffsll(rej) - 1) : N;
-  rec.mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
-  rec.j = j;
-  rec.m_target = ds.row_m[N + j];
-  rec.m_draft = (j < N && !greedy) ? ds.row_m[j] : 0.0f;
-  rec.log_rho = (j < N && !greedy) ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-  if (write) {
-    for (int i = tid; i <= N; i += kThreads) {
-      if (i < j)
-        otok[i] = tok[i];
-      else if (i > j)
-        otok[i] = -1;
-      else if (greedy)
-        otok[i] = ds.row_idx[N + j];
-    }
-    if (tid == 0) {
-      P.out_n[b] = j;
-      P.seq[b] = SeqRec{rec.mode, rec.j, rec.m_target, rec.m_draft, rec.log_rho};
-    }
+  const int mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
+  for (int i = tid; i <= N; i += kThreads) {
+    if (i < j)
+      otok[i] = ds.tok[i];
+    else if (i > j)
+      otok[i] = -1;
+    else if (greedy)
+      otok[i] = ds.row_idx[N + j];
   }
-  barrier();
-  return rec;
+  if (tid == 0) {
+    P.out_n[b] = j;
+    const float md = (j < N && !greedy) ? ds.row_m[j] : 0.0f;
+    const double log_rho = (j < N && !greedy) ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
+    if (!greedy) publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +856,7 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params& P, int b, const S
   DrawRows<T> d;
   d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
   d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
-  d.inv_t = 1.0 / double(P.temperature[b]);
+  d.inv_t = 1.0 / double(load_uniform(P.temperature + b));
   d.nmt = -double(s.m_target) * d.inv_t;
   d.nmd = -double(s.m_draft) * d.inv_t;
   return d;
@@ -785,84 +871,90 @@ __device__ __forceinline__ double resid_weight(double et, double ed, double rt, 
   return fmax(0.0, fma(et, rt, -__dmul_rn(ed, rd)));
 }
 
-// Crossing search by wave 0 over n = 64 * kPer values v[0..n): lane l owns
-// v[kPer*l .. kPer*l + kPer). Lane sums (in order), a wave inclusive scan,
-// then each lane walks its values from its exclusive prefix. Returns the first
-// index i with positive v[i] whose inclusive prefix exceeds target, else the
-// last index with positive v[i], else 0; `rem` = target - prefix before i,
-// S = the total. Uniform over wave 0.
-template <int kPer>
-__device__ __forceinline__ int find_crossing(const double* v, int lane, double target, double& S, double& rem) {
-  double own = 0.0;
-#pragma unroll 1
-  for (int q = 0; q < kPer; ++q) own += v[kPer * lane + q];
-  double incl = own;
+// Exclusive prefix (fixed order) of one value per thread over the workgroup,
+// in thread order; `total` gets the sum of all of them.
+__device__ __forceinline__ double block_excl_scan(double v, double& total, double* red) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  double incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double up = __shfl_up(incl, off);
     if (lane >= off) incl += up;
   }
-  S = __shfl(incl, 63);
-  double pre = incl - own;  // exclusive prefix of this lane's values
-  int cross = INT_MAX, lastpos = -1;
-  double cross_pre = 0.0, last_pre = 0.0;
-#pragma unroll 1
-  for (int q = 0; q < kPer; ++q) {
-    const int i = kPer * lane + q;
-    const double x = v[i];
-    if (x > 0.0) {
-      if (cross == INT_MAX && pre + x > target) {
-        cross = i;
-        cross_pre = pre;
-      }
-      lastpos = i;
-      last_pre = pre;
-    }
-    pre += x;
+  double excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = 0.0;
+  barrier();
+  if (lane == 63) red[wave] = incl;
+  barrier();
+  double base = 0.0, sum = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) base += red[w];
+    sum += red[w];
   }
-  const unsigned long long has = __ballot(cross != INT_MAX);
-  if (has) {
-    const int src = __ffsll(has) - 1;
-    rem = target - __shfl(cross_pre, src);
-    return __shfl(cross, src);
-  }
-  const unsigned long long pos = __ballot(lastpos >= 0);
-  if (pos) {
-    const int src = 63 - __clzll(pos);
-    rem = target - __shfl(last_pre, src);
-    return __shfl(lastpos, src);
-  }
-  rem = target;
-  return 0;
+  total = sum;
+  return base + excl;
 }
 
-// Whole-workgroup crossing search over v[0..64*kPer) in LDS; result in ws.pick, ws.rem.
-template <int kPer>
-__device__ __forceinline__ void block_crossing(DrawShared& ws, const double* v, double target, bool scale_by_total,
-                                               double u) {
+// Lowest (kFirst) or highest thread index whose flag is set, kThreads or -1
+// if none; the same in every thread.
+template <bool kFirst>
+__device__ __forceinline__ int block_pick(bool flag, int* slots) {
+  const unsigned long long m = __ballot(flag);
+  const int wave = threadIdx.x >> 6;
   barrier();
-  if (threadIdx.x < 64) {
-    double S, rem;
-    int pick;
-    if (scale_by_total) {
-      double own = 0.0;
-#pragma unroll 1
-      for (int q = 0; q < kPer; ++q) own += v[kPer * threadIdx.x + q];
-      double incl = own;
+  if ((threadIdx.x & 63) == 0) {
+    if (kFirst)
+      slots[wave] = m ? wave * 64 + __ffsll(m) - 1 : kThreads;
+    else
+      slots[wave] = m ? wave * 64 + 63 - __clzll(m) : -1;
+  }
+  barrier();
+  int r = slots[0];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double up = __shfl_up(incl, off);
-        if (int(threadIdx.x) >= off) incl += up;
+  for (int w = 1; w < kWaves; ++w) r = kFirst ? min(r, slots[w]) : max(r, slots[w]);
+  return r;
+}
+
+// Inverse-CDF step over n values per thread, in thread order then value
+// order: thread `pre` is its exclusive prefix. Picks the first value with
+// positive weight whose inclusive prefix exceeds `target`, else the last
+// positive one; ws.pick = thread * n + index and ws.rem = target minus the
+// prefix before it (-1 and target if no value is positive).
+template <int n>
+__device__ __forceinline__ void block_inverse_cdf(DrawShared& ws, const double (&w)[n], double pre, double target) {
+  double cum = pre, hit_pre = 0.0, last_pre = 0.0;
+  int hit = -1, lastp = -1;
+#pragma unroll
+  for (int k = 0; k < n; ++k) {
+    const double x = w[k];
+    if (x > 0.0) {
+      if (hit < 0 && cum + x > target) {
+        hit = k;
+        hit_pre = cum;
       }
-      const double tot = __shfl(incl, 63);
-      pick = find_crossing<kPer>(v, threadIdx.x, u * tot, S, rem);
-      if (!(tot > 0.0)) pick = -1;
-    } else {
-      pick = find_crossing<kPer>(v, threadIdx.x, target, S, rem);
+      lastp = k;
+      last_pre = cum;
     }
-    if (threadIdx.x == 0) {
-      ws.pick = pick;
-      ws.rem = rem;
+    cum += x;
+  }
+  const int tid = threadIdx.x;
+  const int first = block_pick<true>(hit >= 0, ws.slots);
+  if (first < kThreads) {
+    if (tid == first) {
+      ws.pick = tid * n + hit;
+      ws.rem = target - hit_pre;
+    }
+  } else {
+    const int last = block_pick<false>(lastp >= 0, ws.slots);
+    if (tid == last) {
+      ws.pick = tid * n + lastp;
+      ws.rem = target - last_pre;
+    }
+    if (last < 0 && tid == 0) {
+      ws.pick = -1;
+      ws.rem = target;
     }
   }
   barrier();
@@ -885,83 +977,56 @@ constexpr double kSignBand = 1e-4;
 
 // Member c of sequence b: fp64 exps of its kPer logits per thread of the
 // draw's row(s) (target row j and draft row j after a rejection, target row N
-// for the bonus), summed and classified; writes the member's record. The
-// same bits whoever computes it.
+// for the bonus), summed and classified; writes the member's record.
 template <typename T>
 __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b, int c, const SeqInfo& s) {
   const bool residual = s.mode == kModeResidual;
   constexpr int kPer = Logit<T>::kPer;
+  constexpr int kG = kPer / Logit<T>::kVec;  // 16-byte groups per row
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const DrawRows<T> d = draw_rows<T>(P, b, s);
   const int e = (c * kThreads + tid) * kPer;
-  constexpr int kVec = Logit<T>::kVec;
-  constexpr int kG = kPer / kVec;  // 16-byte groups per row
   uint4 xt[kG], xd[kG];
   load_packed(d.trow, e, P.vocab, P.vec_ok != 0, xt);
   if (residual) load_packed(d.drow, e, P.vocab, P.vec_ok != 0, xd);
-  trace(0, 2);
-    // The sign of w_x follows (zt - zd)/T - (mt - md)/T against log(rho).
-  const float inv_tf = float(d.inv_t);
-  const float dmf = float(d.nmt - d.nmd);  // -(mt - md)/T
-  const float hi = float(s.log_rho + kSignBand), lo = float(s.log_rho - kSignBand);
+  trace(0, 1);
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;
   uint32_t unc = 0;  // bit k: token k of this thread has an uncertain sign
-  // A rolled loop over the 16-byte groups (the code stays small enough to
-  // remain in the instruction cache); each pass selects its group. The two
-  // kinds of draw have separate loops without branches inside, so the tokens
-  // of a group are one basic block and their exps overlap.
   if (residual) {
-#pragma unroll 1
-    for (int g = 0; g < kG; ++g) {
-      uint4 gt = xt[0], gd = xd[0];
+    // The sign of w_x follows (zt - zd)/T - (mt - md)/T against log(rho).
+    const float inv_tf = float(d.inv_t);
+    const float dmf = float(d.nmt - d.nmd);  // -(mt - md)/T
+    const float hi = float(s.log_rho + kSignBand), lo = float(s.log_rho - kSignBand);
 #pragma unroll
-      for (int q = 1; q < kG; ++q) {
-        gt = (g == q) ? xt[q] : gt;
-        gd = (g == q) ? xd[q] : gd;
-      }
-      const uint4 one_t[1] = {gt};
-      const uint4 one_d[1] = {gd};
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) {
-        const float ztk = Logit<T>::element(one_t, v);
-        const float zdk = Logit<T>::element(one_d, v);
-        const double et = exp_nonpos(exp_arg(ztk, d.nmt, d.inv_t));
-        const double ed = exp_nonpos(exp_arg(zdk, d.nmd, d.inv_t));
-        st += et;
-        sd += ed;
-        // +inf when the draft gives the token zero mass, NaN (neither class)
-        // when both rows do: such a token adds nothing wherever it goes.
-        const float lr = fmaf(ztk - zdk, inv_tf, dmf);
-        const bool pos = lr > hi;
-        const bool band = !pos && lr >= lo;
-        sa += pos ? et : 0.0;
-        sb += pos ? ed : 0.0;
-        unc |= band ? (1u << (g * kVec + v)) : 0u;
-      }
+    for (int k = 0; k < kPer; ++k) {
+      const float ztk = Logit<T>::element(xt, k);
+      const float zdk = Logit<T>::element(xd, k);
+      const double et = exp_nonpos(exp_arg(ztk, d.nmt, d.inv_t));
+      const double ed = exp_nonpos(exp_arg(zdk, d.nmd, d.inv_t));
+      st += et;
+      sd += ed;
+      // +inf when the draft gives the token zero mass, NaN (neither class)
+      // when both rows do: such a token adds nothing wherever it goes.
+      const float lr = fmaf(ztk - zdk, inv_tf, dmf);
+      const bool pos = lr > hi;
+      const bool band = !pos && lr >= lo;
+      sa += pos ? et : 0.0;
+      sb += pos ? ed : 0.0;
+      unc |= band ? (1u << k) : 0u;
     }
   } else {
-#pragma unroll 1
-    for (int g = 0; g < kG; ++g) {
-      uint4 gt = xt[0];
 #pragma unroll
-      for (int q = 1; q < kG; ++q) gt = (g == q) ? xt[q] : gt;
-      const uint4 one_t[1] = {gt};
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) {
-        const double et = exp_nonpos(exp_arg(Logit<T>::element(one_t, v), d.nmt, d.inv_t));
-        st += et;
-        sa += et;
-      }
-    }
+    for (int k = 0; k < kPer; ++k) st += exp_nonpos(exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t));
+    sa = st;
   }
-  trace(0, 3);
+  trace(0, 2);
   // The first two uncertain tokens of this thread: their exps again (the same
   // bits), staged in LDS; more overflow the record.
   const int n_unc = __popc(unc);
   int unc_k0 = 0, unc_k1 = 0;
-  if (residual && n_unc > 0) {
+  if (n_unc > 0) {
     unc_k0 = __ffs(int(unc)) - 1;
     unc_k1 = n_unc > 1 ? __ffs(int(unc & (unc - 1))) - 1 : 0;
     for (int i = 0; i < min(n_unc, 2); ++i) {
@@ -979,8 +1044,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     sb += __shfl_xor(sb, off);
   }
   if ((lane & 31) == 0) {
-    rec->a[tid >> 5] = sa;
-    rec->bs[tid >> 5] = sb;
+    put_d(&rec->a[tid >> 5], sa);
+    put_d(&rec->bs[tid >> 5], sb);
   }
   block_sum2(st, sd, ws.red);
   int total = 0;
@@ -1004,27 +1069,26 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     }
     if (total <= kUncMax) {
       for (int i = 0; i < cnt; ++i) {
-        rec->pos[slot + i] = e + (i == 0 ? unc_k0 : unc_k1);
-        rec->uet[slot + i] = ws.unc_et[i][tid];
-        rec->ued[slot + i] = ws.unc_ed[i][tid];
+        put_i(&rec->pos[slot + i], e + (i == 0 ? unc_k0 : unc_k1));
+        put_d(&rec->uet[slot + i], ws.unc_et[i][tid]);
+        put_d(&rec->ued[slot + i], ws.unc_ed[i][tid]);
       }
     }
   }
   if (tid == 0) {
-    rec->zt = st;
-    rec->zd = sd;
-    rec->n_unc = min(total, kUncMax + 1);
+    put_d(&rec->zt, st);
+    put_d(&rec->zd, sd);
+    put_i(&rec->n_unc, min(total, kUncMax + 1));
   }
-  barrier();
 }
 
 // Exact weights of sub-chunk `sub` of member c (whole workgroup): each thread
 // takes kPer/8 consecutive tokens; returns this thread's weights' sum and its
-// weights through w.
+// weights through w. rd = 0 after a rejection gives et/Zt instead of the
+// residual.
 template <typename T>
-__device__ __forceinline__ double sub_weights(const Params& P, const Shared& sh, const DrawRows<T>& d, int c,
-                                              int sub, bool residual, double rt, double rd,
-                                              double (&w)[Logit<T>::kPer / 8], int& e0) {
+__device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>& d, int c, int sub, bool residual,
+                                              double rt, double rd, double (&w)[Logit<T>::kPer / 8], int& e0) {
   constexpr int kQ = Logit<T>::kPer / 8;  // a sub-chunk holds 32*kPer tokens: kQ per thread
   e0 = c * kThreads * Logit<T>::kPer + sub * 32 * Logit<T>::kPer + int(threadIdx.x) * kQ;
   double sum = 0.0;
@@ -1045,25 +1109,27 @@ __device__ __forceinline__ double sub_weights(const Params& P, const Shared& sh,
   return sum;
 }
 
-// A member's record computed by another workgroup (a rare path, out of line).
-// Exact weights of every sub-chunk of member c into ws.w (rd = 0 gives the
-// target probabilities et/Zt instead).
+// Exact weights of the kSubs sub-chunks of member c (whole workgroup, a rare
+// path); thread c receives them in w.
 template <typename T>
-__device__ __forceinline__ void exact_sub_weights(const Params& P, Shared& sh, const DrawRows<T>& d, int c, double rt,
-                                                  double rd) {
+__device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared& ws, const DrawRows<T>& d, int c,
+                                                     double rt, double rd, double (&w)[kSubs]) {
+#pragma unroll 1
   for (int sub = 0; sub < kSubs; ++sub) {
-    double w[Logit<T>::kPer / 8];
+    double wq[Logit<T>::kPer / 8];
     int e0;
-    const double sum = block_sum(sub_weights<T>(P, sh, d, c, sub, true, rt, rd, w, e0), sh.u.drw.red);
-    if (threadIdx.x == 0) sh.u.drw.w[c * kSubs + sub] = sum;
-    barrier();
+    const double v = block_sum(sub_weights<T>(P, d, c, sub, true, rt, rd, wq, e0), ws.red);
+#pragma unroll
+    for (int k = 0; k < kSubs; ++k)
+      if (k == sub && int(threadIdx.x) == c) w[k] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// The finisher: from the member records, the normalisers and sub-chunk
-// weights, the sub-chunk where the inverse CDF crosses u*S, an exact rescan of
-// it, the token.
+// The finisher (the last member of a sequence): from the member records, the
+// normalisers and sub-chunk weights (thread c holds member c's), the
+// sub-chunk where the inverse CDF crosses u*S, an exact rescan of it, the
+// token.
 
 template <typename T>
 __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s) {
@@ -1073,128 +1139,234 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int nm = P.nm;
-  const int nw = nm * kSubs;
-  const MemberRec* recs = P.records + int64_t(b) * nm;
-  // Normalisers (fixed order: thread c holds member c's sums).
+  const bool mine = tid < nm;
+  const MemberRec* rec = P.records + int64_t(b) * nm + (mine ? tid : 0);
   double zt = 0.0, zd = 0.0;
-  if (tid < nm) {
-    zt = recs[tid].zt;
-    zd = recs[tid].zd;
-    ws.nunc[tid] = recs[tid].n_unc;
+  double a[kSubs], bs[kSubs], w[kSubs];
+  int nunc = 0;
+#pragma unroll
+  for (int k = 0; k < kSubs; ++k) a[k] = bs[k] = 0.0;
+  if (mine) {
+    zt = get_d(&rec->zt);
+    zd = get_d(&rec->zd);
+    nunc = get_i(&rec->n_unc);
+#pragma unroll
+    for (int k = 0; k < kSubs; ++k) {
+      a[k] = get_d(&rec->a[k]);
+      bs[k] = get_d(&rec->bs[k]);
+    }
+    ws.nunc[tid] = nunc;
   }
+  // Normalisers (fixed order: thread c holds member c's sums).
   block_sum2(zt, zd, ws.red);
-  trace(1, 1);
+  trace_at(1, b, 1);
   const double rt = 1.0 / zt;
   const double rd = residual ? 1.0 / zd : 0.0;
-  // Sub-chunk weights: A/Zt - B/Zd of the certain tokens.
-  for (int i = tid; i < kMaxMembers * kSubs; i += kThreads) {
-    double w = 0.0;
-    if (i < nw) {
-      const MemberRec& r = recs[i / kSubs];
-      const double a = r.a[i % kSubs];
-      w = residual ? fma(a, rt, -__dmul_rn(r.bs[i % kSubs], rd)) : a;
-    }
-    ws.w[i] = w;
-  }
-  barrier();
   const DrawRows<T> d = draw_rows<T>(P, b, s);
-  if (residual) {
-    // Listed uncertain tokens, member by member in order (one thread per
-    // member, entries in token order).
-    if (tid < nm && ws.nunc[tid] <= kUncMax) {
-      const MemberRec& r = recs[tid];
-      for (int k = 0; k < ws.nunc[tid]; ++k) {
-        const int sub = (r.pos[k] - tid * kThreads * kPer) / (32 * kPer);
-        ws.w[tid * kSubs + sub] += resid_weight(r.uet[k], r.ued[k], rt, rd);
+  // Sub-chunk weights A/Zt - B/Zd of the certain tokens, then the listed
+  // uncertain tokens in token order.
+#pragma unroll
+  for (int k = 0; k < kSubs; ++k) w[k] = !mine ? 0.0 : residual ? fma(a[k], rt, -__dmul_rn(bs[k], rd)) : a[k];
+  if (residual && mine && nunc > 0 && nunc <= kUncMax) {
+    // The whole list at once, then its first nunc entries in order.
+    int upos[kUncMax];
+    double uet[kUncMax], ued[kUncMax];
+#pragma unroll
+    for (int i = 0; i < kUncMax; ++i) {
+      upos[i] = get_i(&rec->pos[i]);
+      uet[i] = get_d(&rec->uet[i]);
+      ued[i] = get_d(&rec->ued[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kUncMax; ++i) {
+      if (i < nunc) {
+        const int sub = (upos[i] - tid * kThreads * kPer) / (32 * kPer);
+        const double v = resid_weight(uet[i], ued[i], rt, rd);
+#pragma unroll
+        for (int k = 0; k < kSubs; ++k) w[k] += (k == sub) ? v : 0.0;
       }
     }
-    barrier();
-    // Members whose uncertain tokens overflowed their record: exact weights.
-    for (int c = 0; c < nm; ++c)
-      if (ws.nunc[c] > kUncMax) exact_sub_weights<T>(P, sh, d, c, rt, rd);
   }
-  const double us = double(P.sample_u[b]);
-  block_crossing<kMaxMembers * kSubs / 64>(ws, ws.w, 0.0, true, us);
-  int pick = ws.pick;
-  double rem = ws.rem;
+  // Members whose uncertain tokens overflowed their record: exact weights.
+  if (residual)
+    for (int c = 0; c < nm; ++c)
+      if (ws.nunc[c] > kUncMax) exact_member_weights<T>(P, ws, d, c, rt, rd, w);
+  double run = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSubs; ++k) run += w[k];
+  double S;
+  double pre = block_excl_scan(run, S, ws.red);
   bool from_q = false;
-  if (residual && pick < 0) {
+  if (residual && !(S > 0.0)) {
     // Every residual weight rounded to zero: draw from q_j itself, sub-chunk
     // by sub-chunk exactly.
     from_q = true;
-    barrier();
-    for (int i = tid; i < kMaxMembers * kSubs; i += kThreads) ws.w[i] = 0.0;
-    barrier();
-    for (int c = 0; c < nm; ++c) exact_sub_weights<T>(P, sh, d, c, rt, 0.0);
-    block_crossing<kMaxMembers * kSubs / 64>(ws, ws.w, 0.0, true, us);
-    pick = ws.pick < 0 ? 0 : ws.pick;
-    rem = ws.rem;
-  }
-  trace(1, 2);
-  // Rescan the crossing sub-chunk: exact weights, thread sums, the crossing
-  // thread, its token.
-  const int c = pick / kSubs, sub = pick % kSubs;
-  double w[kQ];
-  int e0;
-  const double run = sub_weights<T>(P, sh, d, c, sub, residual, rt, from_q ? 0.0 : rd, w, e0);
-  trace(1, 3);
-  barrier();
-  ws.w[tid] = run;
-  block_crossing<kThreads / 64>(ws, ws.w, rem, false, 0.0);
-  if (tid == ws.pick) {
-    // First token with positive weight whose running sum exceeds the
-    // remaining mass, else (rounding) the last positive one.
-    const double r = ws.rem;
-    double cum = 0.0;
-    int token = -1, last = -1;
+    for (int c = 0; c < nm; ++c) exact_member_weights<T>(P, ws, d, c, rt, 0.0, w);
+    run = 0.0;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      cum += w[q];
-      if (token < 0 && cum > r && w[q] > 0.0) token = q;
-      if (w[q] > 0.0) last = q;
-    }
-    const int q = token >= 0 ? token : last;
-    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = q >= 0 ? e0 + q : 0;
+    for (int k = 0; k < kSubs; ++k) run += w[k];
+    pre = block_excl_scan(run, S, ws.red);
+  }
+  const double us = double(load_uniform(P.sample_u + b));
+  block_inverse_cdf<kSubs>(ws, w, pre, us * S);
+  const int pick = max(ws.pick, 0);
+  const double rem = ws.rem;
+  trace_at(1, b, 2);
+  // Rescan the crossing sub-chunk: exact weights, the token.
+  double wq[kQ];
+  int e0;
+  const double own = sub_weights<T>(P, d, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
+  trace_at(1, b, 3);
+  double tot;
+  const double pre2 = block_excl_scan(own, tot, ws.red);
+  block_inverse_cdf<kQ>(ws, wq, pre2, rem);
+  if (tid == 0) {
+    const int k = ws.pick;
+    const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
+    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Kernels after the row statistics.
+// Kernels.
 
-__shared__ Shared g_shared;
+// A sequence's decision and its finisher lie on the path of the sequences
+// that end last, while their CU is busy with other workgroups' streaming or
+// fp64 sums: their waves take issue priority.
+__device__ __forceinline__ void critical_path() { __builtin_amdgcn_s_setprio(3); }
 
-// Member c of sequence b (grid: batch * nm). Greedy and invalid sequences
-// need no draw: their member 0 does all.
+// Row-statistics item `idx` of sequence b; the last item of a sequence to
+// finish takes the sequence's decision.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void members_kernel(Params P) {
-  Shared& sh = g_shared;
-  const int b = int(blockIdx.x / unsigned(P.nm));
-  const int c = int(blockIdx.x - unsigned(b) * unsigned(P.nm));
-  const float t = P.temperature[b];
-  if (c != 0 && !(t > 0.0f && temperature_valid(t))) return;
+__device__ __forceinline__ void stat_role(const Params& P, Shared& sh, int b, int idx) {
+  trace_set(unsigned(b) * unsigned(P.items_per_seq) + unsigned(idx));
+  trace(2, 0);
+  const Item it = item_at<T>(P, int64_t(b) * P.items_per_seq + idx);
+  if (it.live) {
+    ItemRegs g;
+    item_load<T>(P, it, g);
+    const Partial q = item_reduce<T>(it, g, sh.st);
+    trace(2, 1);
+    item_write(P, it, q);
+  }
+  const bool last = last_arrival(P.stat_done + b * kCounterStride, P.items_per_seq);
+  trace(2, 2);
+  if (last) {
+    critical_path();
+    decide<T>(P, sh, b);
+    trace(2, 3);
+  }
+}
+
+// Waits (bounded) for sequence b's decision. A draw member only waits for
+// row-statistics workgroups that precede it in the launch order and never
+// wait themselves, so the wait ends. Returns false if it timed out.
+constexpr int kWaitPolls = 1 << 20;
+
+__shared__ SeqInfo g_seq;
+__shared__ int g_seq_ok;
+
+__device__ __forceinline__ bool wait_decision(const Params& P, int b, SeqInfo& s) {
+  if (threadIdx.x == 0) {
+    const SeqRec* q = P.seq + b;
+    uint64_t f = get_u64(&q->flag);
+    for (int i = 0; !(f & kPublished) && i < kWaitPolls; ++i) {
+      __builtin_amdgcn_s_sleep(8);
+      f = get_u64(&q->flag);
+    }
+    const bool ok = (f & kPublished) != 0;
+    g_seq_ok = ok;
+    g_seq = SeqInfo{kModeNone, 0, 0.0f, 0.0f, 0.0};
+    if (ok) {
+      const uint64_t mx = get_u64(&q->maxima);
+      g_seq = SeqInfo{int(f & 0xff), int((f >> 8) & 0xffffff), __uint_as_float(uint32_t(mx)),
+                      __uint_as_float(uint32_t(mx >> 32)), get_d(&q->log_rho)};
+    }
+  }
+  barrier();
+  s = g_seq;
+  return g_seq_ok != 0;
+}
+
+// Draw member c of sequence b. Every member of a sampled sequence reports
+// when done; the last one clears the decision's flag and, if there is a draw,
+// draws the token.
+template <typename T>
+__device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
+  if (!has_draw_members(load_uniform(P.temperature + b))) return;
+  trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
-  const SeqInfo s = decide<T>(P, sh, b, c == 0);
-  trace(0, 1);
-  if (s.mode == kModeNone) return;
-  member_record<T>(P, sh, b, c, s);
+  SeqInfo s;
+  if (!wait_decision(P, b, s)) {
+    // Not expected: the decision did not come within the bound. The sequence
+    // is reported as failed rather than the device left waiting.
+    if (threadIdx.x == 0) P.out_n[b] = -2;
+  }
+  trace(0, 5);
+  if (s.mode != kModeNone) member_record<T>(P, sh, b, c, s);
+  trace(0, 3);
+  const bool last = last_arrival(P.draw_done + b * kCounterStride, P.nm);
   trace(0, 4);
+  if (last) {
+    if (threadIdx.x == 0) put_u64(&P.seq[b].flag, 0);
+    if (s.mode != kModeNone) {
+      critical_path();
+      trace_at(1, b, 0);
+      finish<T>(P, sh, b, s);
+      trace_at(1, b, 4);
+    }
+  }
 }
 
-// The draw of sequence b (grid: batch).
+// What workgroup x of the launch does. Launch order: the row statistics of
+// sequences 0..lag-1, then for each sequence p the row statistics of sequence
+// p + lag (while there is one) followed by the draw members of sequence p.
+struct Role {
+  bool stat;
+  int b;
+  int idx;  // row-statistics item within the sequence, or draw member
+};
+
+__device__ __forceinline__ Role role_of(const Params& P, int x) {
+  const int A = P.items_per_seq, M = P.nm, L = P.lag;
+  Role w;
+  if (x < L * A) {
+    w.stat = true;
+    w.b = x / A;
+    w.idx = x - w.b * A;
+    return w;
+  }
+  x -= L * A;
+  const int n1 = P.batch - L;  // pairs (row statistics of p + L, draw of p)
+  if (x < n1 * (A + M)) {
+    const int p = x / (A + M);
+    const int z = x - p * (A + M);
+    w.stat = z < A;
+    w.b = w.stat ? p + L : p;
+    w.idx = w.stat ? z : z - A;
+    return w;
+  }
+  x -= n1 * (A + M);
+  const int p = x / M;
+  w.stat = false;
+  w.b = n1 + p;
+  w.idx = x - p * M;
+  return w;
+}
+
+// Five waves per SIMD: the most the draw members' registers allow without spills.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void finish_kernel(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void verify_kernel(Params P) {
   Shared& sh = g_shared;
-  const int b = int(blockIdx.x);
-  trace(1, 0);
-  const SeqRec r = P.seq[b];
-  if (r.mode == kModeNone) return;
-  const SeqInfo s{r.mode, r.j, r.mt, r.md, r.log_rho};
-  finish<T>(P, sh, b, s);
-  trace(1, 4);
+  const Role w = role_of(P, int(blockIdx.x));
+  if (w.stat)
+    stat_role<T>(P, sh, w.b, w.idx);
+  else
+    draw_role<T>(P, sh, w.b, w.idx);
 }
 
-const char* const kStageNames[] = {"row_stats", "members", "finish"};
-constexpr int kNumStages = 3;
+const char* const kStageNames[] = {"verify"};
+constexpr int kNumStages = 1;
 
 template <typename T>
 hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t stream, hipEvent_t* ev) {
@@ -1212,32 +1384,47 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.partials = static_cast<PartialRec*>(w.partials);
   p.seq = static_cast<SeqRec*>(w.seq);
   p.records = static_cast<MemberRec*>(w.records);
+  p.stat_done = w.stat_done;
+  p.draw_done = w.draw_done;
   p.batch = a.batch;
   p.n_draft = a.n_draft;
   p.vocab = a.vocab;
   p.nch = w.n_stat_chunks;
   p.chunk = w.stat_chunk;
   p.nm = w.n_members;
-  p.n_items = int64_t(a.batch) * (2 * a.n_draft + 1) * w.n_stat_chunks;
+  p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
+  // The lag: about three chip-fulls of resident workgroups of (row
+  // statistics, draw) pairs, so a sequence's decision is normally out before
+  // its draw members start.
+  p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + p.nm)));
   p.vec_ok = (int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0;
+  const int64_t blocks = int64_t(a.batch) * (p.items_per_seq + p.nm);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(row_stats_kernel<T>, dim3(unsigned(p.n_items)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(members_kernel<T>, dim3(unsigned(int64_t(a.batch) * p.nm)), dim3(kThreads), 0, stream, p);
-  if (ev != nullptr) (void)hipEventRecord(ev[2], stream);
-  hipLaunchKernelGGL(finish_kernel<T>, dim3(unsigned(a.batch)), dim3(kThreads), 0, stream, p);
-  if (ev != nullptr) (void)hipEventRecord(ev[3], stream);
   return hipGetLastError();
 }
 
+int resident_blocks(int dtype) {
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const hipError_t e = dtype == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<float>, kThreads, 0)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_kernel<uint16_t>, kThreads, 0);
+  if (e != hipSuccess) return -1;
+  return max(1, per_cu) * max(1, cus);
+}
+
 }  // namespace
+
+int max_resident_blocks(int dtype) { return resident_blocks(dtype); }
 
 const char* stage_name(int stage) {
   return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
 }
 
 #if defined(SPECV_TRACE)
-// Copies the stamps of the last launches (members, then finish) into out and clears them.
+// Copies the stamps of the last launches (draw members, finishers, row-statistics items) into out and clears them.
 extern "C" __attribute__((visibility("default"))) int specv_debug_trace(uint64_t* out, int64_t cap_words) {
   const size_t bytes = sizeof(g_trace);
   if (out == nullptr || cap_words * int64_t(sizeof(uint64_t)) < int64_t(bytes)) return -1;

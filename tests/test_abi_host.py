@@ -76,8 +76,8 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
     n = ctypes.c_int()
     assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
-    assert [specv.specv_stage_name(i) for i in range(3)] == ["row_stats", "members", "finish"]
-    assert specv.specv_stage_name(3) is None
+    assert specv.specv_stage_name(0) == "verify"
+    assert specv.specv_stage_name(1) is None
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

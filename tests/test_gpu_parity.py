@@ -14,7 +14,7 @@ from scipy import special, stats
 
 import oracle
 import synth
-from parity import (MARGIN, Tally, check_row_stats, compare, require_gpu, run_gpu, run_oracle,
+from parity import (MARGIN, GpuResult, Tally, check_row_stats, compare, require_gpu, run_gpu, run_oracle,
                     to_device)
 from speculative_sampling_verification_specv_amd import SpecvError, Verifier, _lib
 
@@ -216,6 +216,66 @@ def test_determinism():
         c = run_gpu(b, v)
     assert np.array_equal(a.tokens, c.tokens) and np.array_equal(a.n_accepted, c.n_accepted)
     assert np.array_equal(a.lse.view(np.uint32), c.lse.view(np.uint32))
+
+
+def test_graph_replay_matches_eager():
+    """A captured call replays correctly with new inputs each time.
+
+    The per-sequence device state a call uses to hand work between its
+    workgroups (counters, decision flags) is back at zero when the call ends,
+    so a replay of the captured launch sees only its own inputs. Replays are
+    interleaved with eager work and checked one by one against eager calls.
+    """
+    dev = require_gpu()
+    wl = synth.workload("b256_n7_v151936_bf16_mixed").with_sizes(batch=16, vocab=20000)
+    batches = [synth.make_batch(wl, seed) for seed in (11, 12, 13)]
+    B, N = wl.batch, wl.n_draft
+    v = Verifier(B, N, wl.vocab, wl.dtype)
+    try:
+        static = to_device(batches[0], dev)
+        out_t = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+
+        def load(i):
+            src = to_device(batches[i], dev)
+            for k in static:
+                static[k].copy_(src[k])
+
+        eager = []
+        for i in range(len(batches)):
+            load(i)
+            v.verify(**static, out_tokens=out_t, out_n_accepted=out_n)
+            torch.cuda.synchronize()
+            eager.append((out_t.cpu().numpy().copy(), out_n.cpu().numpy().copy()))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            v.verify(**static, out_tokens=out_t, out_n_accepted=out_n)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            v.verify(**static, out_tokens=out_t, out_n_accepted=out_n)
+        for rep in range(7):
+            i = rep % len(batches)
+            load(i)
+            out_t.fill_(-7)
+            out_n.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out_t.cpu().numpy(), eager[i][0]), (rep, i)
+            assert np.array_equal(out_n.cpu().numpy(), eager[i][1]), (rep, i)
+            if rep == 3:  # an eager call between replays
+                load(2)
+                v.verify(**static, out_tokens=out_t, out_n_accepted=out_n)
+                torch.cuda.synchronize()
+                assert np.array_equal(out_t.cpu().numpy(), eager[2][0])
+        # The eager results themselves are the oracle's.
+        for i, bt in enumerate(batches):
+            gpu = GpuResult(eager[i][0], eager[i][1], None, None)
+            compare(bt, gpu, run_oracle(bt)).check(f"graph batch {i}")
+    finally:
+        v.close()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
