@@ -86,8 +86,8 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const int nch = specv::ceil_div(vocab, chunk);
   const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
-  // Grid: one workgroup per row-statistics item and per draw member.
-  if (int64_t(rows) * nch + int64_t(max_batch) * nm >= (int64_t(1) << 31)) return SPECV_EINVAL;
+  // Grid: one workgroup per row-statistics item, per decision and per draw member.
+  if (int64_t(rows) * nch + int64_t(max_batch) * (nm + 1) >= (int64_t(1) << 31)) return SPECV_EINVAL;
 
   size_t off = 0;
   const size_t off_partials = off;
@@ -101,7 +101,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   const size_t off_argmax = off;
   off = align_up(off + rows * sizeof(int), 256);
   const size_t off_counters = off;
-  off = align_up(off + 2 * size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
+  off = align_up(off + size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
 
   DeviceGuard guard(device);
   if (!guard.ok()) return SPECV_EHIP;
@@ -124,8 +124,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   h->ws.records = base + off_records;
   h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
   h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
-  h->ws.stat_done = reinterpret_cast<int*>(base + off_counters);
-  h->ws.draw_done = h->ws.stat_done + size_t(max_batch) * specv::kCounterStride;
+  h->ws.draw_done = reinterpret_cast<int*>(base + off_counters);
   h->ws.n_stat_chunks = nch;
   h->ws.n_members = nm;
   h->ws.stat_chunk = chunk;

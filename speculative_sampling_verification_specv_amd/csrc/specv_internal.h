@@ -8,7 +8,7 @@
 namespace specv {
 
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64s)
-constexpr int kStatBytes = 32768;  // row-statistics item: 32 KB of one row, either dtype
+constexpr int kStatBytes = 65536;  // row-statistics item: 64 KB of one row, either dtype
 
 // A draw member covers 8 KB of each row it reads: 4096 bfloat16 or 2048
 // float32 logits, split into kSubs sub-chunks of 32 consecutive threads.
@@ -40,12 +40,11 @@ struct Workspace {
   void* records;     // [max_batch][n_members] draw-member records
   float* row_lse;    // [batch][2N+1] of the last call
   int* row_argmax;   // [batch][2N+1] of the last call
-  // Per sequence, how many workgroups of a launch are done with it; the last
-  // one resets its count to zero. Zero between calls. One counter per
+  // Per sequence, how many draw members of a launch are done with it; the
+  // last one resets its count to zero. Zero between calls. One counter per
   // kCounterStride ints (its own 256-byte line), so that atomics on different
   // sequences' counters never contend for a line.
-  int* stat_done;    // [max_batch * kCounterStride] row-statistics items
-  int* draw_done;    // [max_batch * kCounterStride] draw members
+  int* draw_done;    // [max_batch * kCounterStride]
   int n_stat_chunks;
   int resident_blocks;  // workgroups of the verification kernel the device holds at once
   int n_members;     // draw members per sequence
@@ -79,7 +78,8 @@ int max_resident_blocks(int dtype);
 // Names of the kernel stages launch_verify enqueues, in order.
 const char* stage_name(int stage);
 
-// Record sizes (bytes) the workspace must hold per unit.
+// Record sizes (bytes) the workspace must hold per unit: per row-statistics
+// item, per sequence, per draw member.
 size_t partial_bytes();
 size_t seq_bytes();
 size_t member_bytes();

@@ -236,6 +236,16 @@ __device__ __forceinline__ void load_packed(const T* __restrict__ row, int e, in
   }
 }
 
+// Element k (a run-time index) of logits packed as stored, by selection:
+// registers cannot be indexed at run time.
+template <typename T, int n>
+__device__ __forceinline__ float element_at(const uint4 (&x)[n], int k) {
+  float r = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < n * Logit<T>::kVec; ++kk) r = (k == kk) ? Logit<T>::element(x, kk) : r;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Block reductions (fixed order). `red` holds 2 * kWaves doubles.
 
@@ -339,38 +349,15 @@ __device__ __forceinline__ void acc_merge(float& m, float& s, int& idx, float m2
   m = mm;
 }
 
-struct StatShared {
-  float m[kWaves], s[kWaves];
-  int idx[kWaves];
-};
-
-// Merge every thread's state into thread 0's.
+// Merge every lane's state of the wave into every lane's (fixed butterfly).
 template <bool kSampled>
-__device__ __forceinline__ void block_merge(StatAcc& a, float c, StatShared& sh) {
-  float m = a.m, s = a.s;
-  int idx = a.idx;
+__device__ __forceinline__ void wave_merge(StatAcc& a, float c) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float s2 = __shfl_xor(s, off);
-    const int i2 = __shfl_xor(idx, off);
-    acc_merge<kSampled>(m, s, idx, m2, s2, i2, c);
-  }
-  barrier();  // thread 0 is done reading the previous merge
-  if ((threadIdx.x & 63) == 0) {
-    sh.m[threadIdx.x >> 6] = m;
-    sh.s[threadIdx.x >> 6] = s;
-    sh.idx[threadIdx.x >> 6] = idx;
-  }
-  barrier();
-  if (threadIdx.x == 0) {
-    m = sh.m[0];
-    s = sh.s[0];
-    idx = sh.idx[0];
-    for (int w = 1; w < kWaves; ++w) acc_merge<kSampled>(m, s, idx, sh.m[w], sh.s[w], sh.idx[w], c);
-    a.m = m;
-    a.s = s;
-    a.idx = idx;
+    const float m2 = __shfl_xor(a.m, off);
+    const float s2 = __shfl_xor(a.s, off);
+    const int i2 = __shfl_xor(a.idx, off);
+    acc_merge<kSampled>(a.m, a.s, a.idx, m2, s2, i2, c);
   }
 }
 
@@ -379,9 +366,7 @@ __device__ __forceinline__ void block_merge(StatAcc& a, float c, StatShared& sh)
 // launch are written and read only as agent-scope relaxed atomics: these
 // bypass the per-XCD L2s' stale or dirty copies, so no L2 write-back or
 // invalidation (what an agent-scope release or acquire fence costs) is ever
-// needed. A writer waits for its record stores to complete before it reports
-// on the unit's counter (last_arrival), and a reader loads a record only
-// after the counter told it that every writer has reported.
+// needed.
 
 __device__ __forceinline__ void put_u64(void* p, uint64_t v) {
   __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -402,10 +387,15 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 }
 
 // Records written by one workgroup and read by another (or the next launch).
-struct alignas(16) PartialRec {  // one (row, chunk) of row statistics
-  float m, s;        // max logit, sum of 2^(z*c - fl(m*c))
-  int idx;           // first argmax
-  float zg;          // logit at the row's draft token (0 if not in the chunk)
+// Row statistics of one wave of an item as two words, neither of them zero
+// once written: w0 = (first argmax + 1) | max logit << 32, w1 = s | zg << 32
+// (s = sum of 2^(z*c - fl(max*c)), >= 1/2 when max is finite; stored as 1
+// when it is 0, i.e. for a greedy or skipped item, or an all -inf one, where no
+// merge uses it; zg = the logit at the row's draft token if the item holds it,
+// else 0). The decision zeroes both after reading them, so a zero word means
+// "not written yet in this call", and no word is read against another.
+struct PartialRec {
+  uint64_t w0, w1;
 };
 struct SeqRec {     // one sequence's decision, published for its draw members
   uint64_t flag;    // kPublished | j << 8 | mode, written after the other words; 0 between calls
@@ -436,7 +426,6 @@ struct Params {
   PartialRec* partials;  // [batch][2N+1][nch]
   SeqRec* seq;           // [batch]
   MemberRec* records;    // [batch][nm]
-  int* stat_done;        // [batch * kCounterStride] row-statistics items done (zero between launches)
   int* draw_done;        // [batch * kCounterStride] draw members done (zero between launches)
   int items_per_seq;     // row-statistics items per sequence: (2N+1) * nch
   int lag;               // draw members of sequence b follow the row statistics of sequence b + lag
@@ -449,8 +438,9 @@ struct Params {
   int vec_ok;  // rows start 16-byte aligned
 };
 
-__device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r, int c) {
-  return P.partials + (int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c;
+// Partial of wave w of item (row r, chunk c) of sequence b.
+__device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r, int c, int w) {
+  return P.partials + ((int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c) * kWaves + w;
 }
 
 // The draft token of row r (draft row i or target row i: d_i), or -1 for target row N.
@@ -569,32 +559,31 @@ struct Partial {
   int idx;
 };
 
-// Fold a loaded item (whole workgroup); thread 0 gets the item's partial.
+// Fold a loaded item's share of one wave; every lane gets the wave's partial.
 template <typename T>
-__device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g, StatShared& sh) {
+__device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g) {
   StatAcc a;
   acc_init(a);
   if (it.sampled) {
     item_fold<T, true>(it, g, a);
-    block_merge<true>(a, it.coef, sh);
+    wave_merge<true>(a, it.coef);
   } else {
     item_fold<T, false>(it, g, a);
-    block_merge<false>(a, 0.0f, sh);
+    wave_merge<false>(a, 0.0f);
   }
   // The logit at the row's draft token if this chunk holds it.
   const float zg = (it.tok >= it.e0 && it.tok < it.e1) ? Logit<T>::from_bits(g.zg) : 0.0f;
   return Partial{a.m, a.s, zg, a.idx};
 }
 
-// Thread 0 stores an item's partial.
-__device__ __forceinline__ void item_write(const Params& P, const Item& it, const Partial& q) {
-  if (threadIdx.x == 0) {
-    PartialRec* r = partial_at(P, it.b, it.r, it.c);
-    put_u64(&r->m, pack2(q.m, q.s));
-    put_u64(&r->idx, pack2(__int_as_float(q.idx), q.zg));
+// Lane 0 of each wave stores the wave's partial (see PartialRec).
+__device__ __forceinline__ void partial_write(const Params& P, int b, int r, int c, const Partial& q) {
+  if ((threadIdx.x & 63) == 0) {
+    PartialRec* p = partial_at(P, b, r, c, threadIdx.x >> 6);
+    put_u64(&p->w0, uint64_t(uint32_t(q.idx + 1)) | (uint64_t(__float_as_uint(q.m)) << 32));
+    put_u64(&p->w1, pack2(q.s != 0.0f ? q.s : 1.0f, q.zg));
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Hand-over between the workgroups of one launch.
@@ -640,18 +629,19 @@ __device__ __forceinline__ void publish(const Params& P, int b, int mode, int j,
 __device__ __forceinline__ bool has_draw_members(float t) { return t > 0.0f && temperature_valid(t); }
 
 constexpr int kStageParts = 256;  // row partials the decision holds in LDS at once
+constexpr int kWaitPolls = 1 << 20;  // bound of every wait (about a second)
 
 struct DecideShared {
   float row_m[kMaxRows];
   double row_logz[kMaxRows];
   int row_idx[kMaxRows];
   float row_zg[kMaxRows];
-  PartialRec part[kStageParts];
+  Partial part[kStageParts];
   int tok[kMaxRows / 2];
   unsigned long long rej_mask;
 };
 static_assert(kStageParts == kThreads, "one staged row partial per thread");
-static_assert(int64_t(kMaxVocab) * 4 / kStatBytes <= kStageParts, "a row's partials fit one group");
+static_assert(int64_t(kMaxVocab) * 4 / kStatBytes * kWaves <= kStageParts, "a row's partials fit one group");
 
 struct DrawShared {
   double red[4 * kWaves];
@@ -665,7 +655,6 @@ struct DrawShared {
 };
 
 struct Shared {
-  StatShared st;
   union {
     DecideShared dec;
     DrawShared drw;
@@ -681,6 +670,22 @@ struct SeqInfo {
   float m_draft;
   double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
 };
+
+// Waits (bounded) until partial q of this call is written, then takes it and
+// zeroes its words for the next call. Returns false if it timed out.
+__device__ __forceinline__ bool take_partial(PartialRec* q, Partial& out) {
+  uint64_t w0 = get_u64(&q->w0), w1 = get_u64(&q->w1);
+  for (int i = 0; (w0 == 0 || w1 == 0) && i < kWaitPolls; ++i) {
+    __builtin_amdgcn_s_sleep(4);
+    if (w0 == 0) w0 = get_u64(&q->w0);
+    if (w1 == 0) w1 = get_u64(&q->w1);
+  }
+  put_u64(&q->w0, 0);
+  put_u64(&q->w1, 0);
+  out = Partial{__uint_as_float(uint32_t(w0 >> 32)), __uint_as_float(uint32_t(w1)), __uint_as_float(uint32_t(w1 >> 32)),
+                int(uint32_t(w0) - 1u)};
+  return w0 != 0 && w1 != 0;
+}
 
 // The decision for sequence b (whole workgroup, once per sequence): per-row
 // log-normalisers and argmaxes from the row partials, the N accept tests, the
@@ -703,69 +708,61 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   float* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  // Everything the decision reads is requested at once (unconditional loads
-  // at clamped addresses): the first group of row partials, the draft tokens,
-  // the accept uniforms, the temperature.
-  const int rows_per_group = max(1, kStageParts / P.nch);
-  const PartialRec* part_b = P.partials + int64_t(b) * R * P.nch;
-  const PartialRec* q0 = part_b + min(tid, min(rows_per_group, R) * P.nch - 1);
-  uint64_t pw0 = get_u64(&q0->m), pw1 = get_u64(&q0->idx);
+  // Every row partial of the sequence is taken (and zeroed) whatever the
+  // outcome, a group of rows at a time (thread i takes partial i of the
+  // group); the draft tokens, accept uniforms and temperature are requested
+  // alongside the first group.
+  const int pr = P.nch * kWaves;  // partials per row
+  const int rows_per_group = max(1, kStageParts / pr);
+  PartialRec* part_b = P.partials + int64_t(b) * R * pr;
   const int ti = min(tid, N - 1);
   const int d = tok[ti];
   const float ua = P.accept_u[int64_t(b) * N + ti];
   const float t = load_uniform(P.temperature + b);
   if (tid < N) ds.tok[tid] = d;
-  if (block_any(!temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab)))) {
-    for (int i = tid; i <= N; i += kThreads) otok[i] = -1;
-    for (int r = tid; r < R; r += kThreads) {
-      lse[r] = NAN;
-      amax[r] = -1;
-    }
-    if (tid == 0) {
-      P.out_n[b] = -1;
-      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0);
-    }
-    return;
-  }
-  trace(2, 4);
+  const bool bad = !temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab));
   const bool greedy = (t == 0.0f);
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
-
-  // The row partials, a group of rows at a time: thread i holds partial i of
-  // the group; then the group's rows are merged (greedy sequences only their
-  // target rows) in a fixed order.
+  // Segments of cs lanes (the row's partial count rounded up to a power of
+  // two, at most 64) each merge one row: lane k of a segment folds partials
+  // k, k + cs, ... of the row in order, then a butterfly within the segment.
   int cs = 1;
-  while (cs < P.nch) cs <<= 1;
+  while (cs < pr && cs < 64) cs <<= 1;
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
+  bool timed_out = false, any_bad = false;
   for (int rg = 0; rg < R; rg += rows_per_group) {
     const int nr = min(rows_per_group, R - rg);
-    const int np = nr * P.nch;
-    if (rg > 0) {
-      const PartialRec* q = part_b + int64_t(rg) * P.nch + min(tid, np - 1);
-      pw0 = get_u64(&q->m);
-      pw1 = get_u64(&q->idx);
+    const int np = nr * pr;
+    if (tid < np) {
+      Partial q;
+      timed_out = !take_partial(part_b + int64_t(rg) * pr + tid, q) || timed_out;
+      ds.part[tid] = q;
     }
-    if (tid < np)
-      ds.part[tid] = PartialRec{__uint_as_float(uint32_t(pw0)), __uint_as_float(uint32_t(pw0 >> 32)),
-                                int(uint32_t(pw1)), __uint_as_float(uint32_t(pw1 >> 32))};
-    barrier();
-    // Segments of cs lanes (nch rounded up to a power of two) each merge one
-    // row: lane k of a segment holds chunk k, then a butterfly within the
-    // segment. A wave takes 64 / cs rows at a time.
+    if (rg == 0) {
+      any_bad = block_any(bad || timed_out);
+      if (any_bad) continue;
+      trace(2, 4);
+    } else {
+      barrier();
+    }
+    if (any_bad) continue;
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
       const int rr = r0 + seg;
       const int r = rg + rr;
       const bool row_ok = rr < nr && r >= r_first;
       float m = -INFINITY, s = 0.0f;
       int idx = INT_MAX;
-      if (row_ok && k_in_seg < P.nch) {
-        const PartialRec& q = ds.part[rr * P.nch + k_in_seg];
-        m = q.m;
-        s = q.s;
-        idx = q.idx;
+      if (row_ok) {
+        for (int k = k_in_seg; k < pr; k += cs) {
+          const Partial& q = ds.part[rr * pr + k];
+          if (greedy)
+            acc_merge<false>(m, s, idx, q.m, q.s, q.idx, c);
+          else
+            acc_merge<true>(m, s, idx, q.m, q.s, q.idx, c);
+        }
       }
       for (int off = 1; off < cs; off <<= 1) {
         const float m2 = __shfl_xor(m, off);
@@ -783,12 +780,27 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * P.nch + ds.tok[r < N ? r : r - N] / P.chunk].zg : 0.0f;
+        // Every wave of the item holding the draft token carries its logit.
+        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * pr + (ds.tok[r < N ? r : r - N] / P.chunk) * kWaves].zg : 0.0f;
         lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
         amax[r] = idx;
       }
     }
     barrier();
+  }
+  if (any_bad) {
+    // Invalid inputs (or, not expected, a partial that never came): sentinels.
+    const bool late = block_any(timed_out);
+    for (int i = tid; i <= N; i += kThreads) otok[i] = late ? -2 : -1;
+    for (int r = tid; r < R; r += kThreads) {
+      lse[r] = NAN;
+      amax[r] = -1;
+    }
+    if (tid == 0) {
+      P.out_n[b] = late ? -2 : -1;
+      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0);
+    }
+    return;
   }
   trace(2, 5);
   if (greedy) {
@@ -1023,16 +1035,17 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   }
   trace(0, 2);
   // The first two uncertain tokens of this thread: their exps again (the same
-  // bits), staged in LDS; more overflow the record.
+  // bits, from the logits still in registers), staged in LDS; more overflow
+  // the record.
   const int n_unc = __popc(unc);
   int unc_k0 = 0, unc_k1 = 0;
   if (n_unc > 0) {
     unc_k0 = __ffs(int(unc)) - 1;
     unc_k1 = n_unc > 1 ? __ffs(int(unc & (unc - 1))) - 1 : 0;
     for (int i = 0; i < min(n_unc, 2); ++i) {
-      const int x = e + (i == 0 ? unc_k0 : unc_k1);
-      ws.unc_et[i][tid] = exp_nonpos(exp_arg(Logit<T>::at(d.trow, x), d.nmt, d.inv_t));
-      ws.unc_ed[i][tid] = exp_nonpos(exp_arg(Logit<T>::at(d.drow, x), d.nmd, d.inv_t));
+      const int k = i == 0 ? unc_k0 : unc_k1;
+      ws.unc_et[i][tid] = exp_nonpos(exp_arg(element_at<T>(xt, k), d.nmt, d.inv_t));
+      ws.unc_ed[i][tid] = exp_nonpos(exp_arg(element_at<T>(xd, k), d.nmd, d.inv_t));
     }
   }
   MemberRec* rec = P.records + int64_t(b) * P.nm + c;
@@ -1188,7 +1201,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     }
   }
   // Members whose uncertain tokens overflowed their record: exact weights.
-  if (residual)
+  if (residual && block_any(mine && nunc > kUncMax))
     for (int c = 0; c < nm; ++c)
       if (ws.nunc[c] > kUncMax) exact_member_weights<T>(P, ws, d, c, rt, rd, w);
   double run = 0.0;
@@ -1235,33 +1248,38 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
 // fp64 sums: their waves take issue priority.
 __device__ __forceinline__ void critical_path() { __builtin_amdgcn_s_setprio(3); }
 
-// Row-statistics item `idx` of sequence b; the last item of a sequence to
-// finish takes the sequence's decision.
+// Row-statistics item `idx` of sequence b: every wave stores its partial (a
+// placeholder when the item is not read) and is done.
 template <typename T>
-__device__ __forceinline__ void stat_role(const Params& P, Shared& sh, int b, int idx) {
-  trace_set(unsigned(b) * unsigned(P.items_per_seq) + unsigned(idx));
+__device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
+  trace_set(unsigned(b) * unsigned(P.items_per_seq + 1) + unsigned(idx));
   trace(2, 0);
   const Item it = item_at<T>(P, int64_t(b) * P.items_per_seq + idx);
+  Partial q{-INFINITY, 0.0f, 0.0f, INT_MAX - 1};
   if (it.live) {
     ItemRegs g;
     item_load<T>(P, it, g);
-    const Partial q = item_reduce<T>(it, g, sh.st);
-    trace(2, 1);
-    item_write(P, it, q);
+    q = item_reduce<T>(it, g);
   }
-  const bool last = last_arrival(P.stat_done + b * kCounterStride, P.items_per_seq);
-  trace(2, 2);
-  if (last) {
-    critical_path();
-    decide<T>(P, sh, b);
-    trace(2, 3);
-  }
+  trace(2, 1);
+  partial_write(P, b, it.r, it.c, q);
+}
+
+// The decision of sequence b, in a workgroup of its own that follows the
+// sequence's row-statistics items in the launch order.
+template <typename T>
+__device__ __forceinline__ void decision_role(const Params& P, Shared& sh, int b) {
+  trace_set(unsigned(b) * unsigned(P.items_per_seq + 1) + unsigned(P.items_per_seq));
+  trace(2, 0);
+  critical_path();
+  decide<T>(P, sh, b);
+  trace(2, 3);
 }
 
 // Waits (bounded) for sequence b's decision. A draw member only waits for
-// row-statistics workgroups that precede it in the launch order and never
-// wait themselves, so the wait ends. Returns false if it timed out.
-constexpr int kWaitPolls = 1 << 20;
+// the decision workgroup, which precedes it in the launch order and waits only
+// for row-statistics workgroups that precede it and never wait, so the wait
+// ends. Returns false if it timed out.
 
 __shared__ SeqInfo g_seq;
 __shared__ int g_seq_ok;
@@ -1318,39 +1336,46 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
   }
 }
 
-// What workgroup x of the launch does. Launch order: the row statistics of
-// sequences 0..lag-1, then for each sequence p the row statistics of sequence
-// p + lag (while there is one) followed by the draw members of sequence p.
+// What workgroup x of the launch does. A sequence's statistics group is its
+// row-statistics items followed by its decision workgroup. Launch order: the
+// statistics groups of sequences 0..lag-1, then for each sequence p the
+// statistics group of sequence p + lag (while there is one) followed by the
+// draw members of sequence p.
 struct Role {
-  bool stat;
+  int kind;  // 0 row statistics, 1 decision, 2 draw member
   int b;
-  int idx;  // row-statistics item within the sequence, or draw member
+  int idx;   // row-statistics item within the sequence, or draw member
 };
 
 __device__ __forceinline__ Role role_of(const Params& P, int x) {
-  const int A = P.items_per_seq, M = P.nm, L = P.lag;
-  Role w;
+  const int A = P.items_per_seq + 1, M = P.nm, L = P.lag;
+  int b, z;
+  bool stat;
   if (x < L * A) {
-    w.stat = true;
-    w.b = x / A;
-    w.idx = x - w.b * A;
-    return w;
+    stat = true;
+    b = x / A;
+    z = x - b * A;
+  } else {
+    x -= L * A;
+    const int n1 = P.batch - L;  // pairs (statistics group of p + L, draw of p)
+    if (x < n1 * (A + M)) {
+      const int p = x / (A + M);
+      z = x - p * (A + M);
+      stat = z < A;
+      b = stat ? p + L : p;
+      if (!stat) z -= A;
+    } else {
+      x -= n1 * (A + M);
+      const int p = x / M;
+      stat = false;
+      b = n1 + p;
+      z = x - p * M;
+    }
   }
-  x -= L * A;
-  const int n1 = P.batch - L;  // pairs (row statistics of p + L, draw of p)
-  if (x < n1 * (A + M)) {
-    const int p = x / (A + M);
-    const int z = x - p * (A + M);
-    w.stat = z < A;
-    w.b = w.stat ? p + L : p;
-    w.idx = w.stat ? z : z - A;
-    return w;
-  }
-  x -= n1 * (A + M);
-  const int p = x / M;
-  w.stat = false;
-  w.b = n1 + p;
-  w.idx = x - p * M;
+  Role w;
+  w.kind = stat ? (z < A - 1 ? 0 : 1) : 2;
+  w.b = b;
+  w.idx = z;
   return w;
 }
 
@@ -1359,8 +1384,10 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void verify_kernel(Params P) {
   Shared& sh = g_shared;
   const Role w = role_of(P, int(blockIdx.x));
-  if (w.stat)
-    stat_role<T>(P, sh, w.b, w.idx);
+  if (w.kind == 0)
+    stat_role<T>(P, w.b, w.idx);
+  else if (w.kind == 1)
+    decision_role<T>(P, sh, w.b);
   else
     draw_role<T>(P, sh, w.b, w.idx);
 }
@@ -1384,7 +1411,6 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.partials = static_cast<PartialRec*>(w.partials);
   p.seq = static_cast<SeqRec*>(w.seq);
   p.records = static_cast<MemberRec*>(w.records);
-  p.stat_done = w.stat_done;
   p.draw_done = w.draw_done;
   p.batch = a.batch;
   p.n_draft = a.n_draft;
@@ -1396,9 +1422,9 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   // The lag: about three chip-fulls of resident workgroups of (row
   // statistics, draw) pairs, so a sequence's decision is normally out before
   // its draw members start.
-  p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + p.nm)));
+  p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + 1 + p.nm)));
   p.vec_ok = (int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0;
-  const int64_t blocks = int64_t(a.batch) * (p.items_per_seq + p.nm);
+  const int64_t blocks = int64_t(a.batch) * (p.items_per_seq + 1 + p.nm);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
@@ -1437,7 +1463,7 @@ extern "C" __attribute__((visibility("default"))) int specv_debug_trace(uint64_t
 }
 #endif
 
-size_t partial_bytes() { return sizeof(PartialRec); }
+size_t partial_bytes() { return sizeof(PartialRec) * kWaves; }
 size_t seq_bytes() { return sizeof(SeqRec); }
 size_t member_bytes() { return sizeof(MemberRec); }
 
