@@ -512,8 +512,12 @@ __device__ __forceinline__ void item_load(const Params& P, const Item& it, ItemR
   if (!it.live) return;
   const int tid = threadIdx.x;
   const T* row = item_row<T>(P, it);
-  // The draft token's logit: one scalar (read-only) load.
-  g.zg = (it.tok >= it.e0 && it.tok < it.e1) ? load_uniform_bits(row + it.tok) : 0u;
+  // The bulk first, so that nothing waits before it is in flight.
+  if (it.nv > 0) {
+    const uint4* __restrict__ v = reinterpret_cast<const uint4*>(row + it.ea);
+#pragma unroll
+    for (int u = 0; u < kStatVecs; ++u) g.x[u] = v[min(tid + u * kThreads, it.nv - 1)];
+  }
   // Head and tail elements exist only for chunks that are not 16-byte aligned
   // (a uniform test).
   if (it.ea > it.e0 || it.et < it.e1) {
@@ -523,11 +527,8 @@ __device__ __forceinline__ void item_load(const Params& P, const Item& it, ItemR
     g.head = 0u;
     g.tail = 0u;
   }
-  if (it.nv > 0) {
-    const uint4* __restrict__ v = reinterpret_cast<const uint4*>(row + it.ea);
-#pragma unroll
-    for (int u = 0; u < kStatVecs; ++u) g.x[u] = v[min(tid + u * kThreads, it.nv - 1)];
-  }
+  // The draft token's logit: one scalar (read-only) load.
+  g.zg = (it.tok >= it.e0 && it.tok < it.e1) ? load_uniform_bits(row + it.tok) : 0u;
 }
 
 template <typename T, bool kSampled>
@@ -1259,6 +1260,9 @@ __device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
   if (it.live) {
     ItemRegs g;
     item_load<T>(P, it, g);
+    // Loads in flight: folding them takes issue priority over the draw
+    // members' fp64 work on the same CU, so items free their slots sooner.
+    __builtin_amdgcn_s_setprio(2);
     q = item_reduce<T>(it, g);
   }
   trace(2, 1);
