@@ -18,7 +18,7 @@
 //              item of a sequence merges its row partials into
 //              log-normalisers, takes the N accept decisions and writes them
 //              out (the token itself when greedy) with the draw's record.
-//   draw       one workgroup per (sequence, 8 KB chunk of the draw's row(s)):
+//   draw       one workgroup per (sequence, 8 KB of each of the draw's row(s)):
 //              fp64 exps of the chunk summed into a member record. The last
 //              member of a sequence is its finisher: the fp64 normalisers and
 //              sub-chunk weights from the records, the sub-chunk where the
@@ -131,7 +131,7 @@ struct Logit;
 template <>
 struct Logit<float> {
   static constexpr int kVec = 4;   // logits per 16-byte load
-  static constexpr int kPer = 8;  // logits of one row per draw-member thread (32 bytes)
+  static constexpr int kPer = 8;  // logits of one row per draw-member thread
   __device__ static float at(const float* p, int64_t i) { return p[i]; }
   __device__ static uint32_t bits(const float* p, int64_t i) { return __float_as_uint(p[i]); }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b); }
@@ -836,6 +836,12 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const unsigned long long rej = ds.rej_mask;
   const int j = rej ? (__ffsll(rej) - 1) : N;
   const int mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
+  // The draw's record first: the draw members wait for it.
+  if (tid == 0 && !greedy) {
+    const float md = j < N ? ds.row_m[j] : 0.0f;
+    const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
+    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
+  }
   for (int i = tid; i <= N; i += kThreads) {
     if (i < j)
       otok[i] = ds.tok[i];
@@ -844,12 +850,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     else if (greedy)
       otok[i] = ds.row_idx[N + j];
   }
-  if (tid == 0) {
-    P.out_n[b] = j;
-    const float md = (j < N && !greedy) ? ds.row_m[j] : 0.0f;
-    const double log_rho = (j < N && !greedy) ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-    if (!greedy) publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
-  }
+  if (tid == 0) P.out_n[b] = j;
 }
 
 // ---------------------------------------------------------------------------

@@ -39,10 +39,11 @@ __host__ __device__ inline uint64_t double_to_bits(double d) {
 // |r| <= ln2/2, exp(a) = 2^n exp(r). n comes from the 1.5*2^52 shifter (the
 // low word of the shifted value holds it); r from a two-part ln2 (Cody and
 // Waite: n * ln2_hi is exact for |n| < 2^11, the low part adds 1e-16
-// relative); exp(r) from its degree-11 Taylor polynomial evaluated by
-// Estrin's scheme (truncation below 1e-14 relative on |r| <= ln2/2); 2^n by
-// ldexp. Below a = -708 (and for -inf or NaN) the result is 0, which drops
-// only terms under 3.3e-308 of the row maximum. Relative error below 1e-13.
+// relative); exp(r) from its degree-11 Taylor polynomial by Horner's rule
+// (truncation below 1e-14 relative on |r| <= ln2/2; one coefficient per
+// step, so the coefficients stay scalar operands); 2^n by ldexp. Below
+// a = -708 (and for -inf or NaN) the result is 0, which drops only terms under
+// 3.3e-308 of the row maximum. Relative error below 1e-13.
 __host__ __device__ inline double exp_nonpos(double a) {
   const double kShift = 6755399441055744.0;         // 1.5 * 2^52
   const double kInvLn2 = 1.4426950408889634;        // 1 / ln 2
@@ -53,20 +54,17 @@ __host__ __device__ inline double exp_nonpos(double a) {
   const int32_t n = static_cast<int32_t>(static_cast<uint32_t>(double_to_bits(t)));
   double r = fma(kd, -kLn2Hi, a);
   r = fma(kd, -kLn2Lo, r);
-  // Estrin's scheme: pairs, then pairs of pairs (a short dependency chain).
-  const double r2 = r * r;
-  const double r4 = r2 * r2;
-  const double r8 = r4 * r4;
-  const double q0 = fma(r, 1.0, 1.0);                      // 1 + r
-  const double q1 = fma(r, 1.0 / 6.0, 0.5);                // 1/2! + r/3!
-  const double q2 = fma(r, 1.0 / 120.0, 1.0 / 24.0);       // 1/4! + r/5!
-  const double q3 = fma(r, 1.0 / 5040.0, 1.0 / 720.0);     // 1/6! + r/7!
-  const double q4 = fma(r, 1.0 / 362880.0, 1.0 / 40320.0);  // 1/8! + r/9!
-  const double q5 = fma(r, 1.0 / 39916800.0, 1.0 / 3628800.0);  // 1/10! + r/11!
-  const double s0 = fma(q1, r2, q0);
-  const double s1 = fma(q3, r2, q2);
-  const double s2 = fma(q5, r2, q4);
-  const double p = fma(s2, r8, fma(s1, r4, s0));
+  double p = fma(r, 1.0 / 39916800.0, 1.0 / 3628800.0);  // 1/11!, 1/10!
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
   const double res = ldexp(p, n);
   return (a >= -708.0) ? res : 0.0;
 }
