@@ -69,8 +69,8 @@ enum specv_status {
 /* Largest n_draft a handle accepts (one 64-lane wavefront holds a sequence's decisions). */
 #define SPECV_MAX_DRAFT 64
 
-/* Largest vocabulary a handle accepts (2^19 tokens). */
-#define SPECV_MAX_VOCAB 524288
+/* Largest vocabulary a handle accepts (2^18 tokens). */
+#define SPECV_MAX_VOCAB 262144
 
 /*
  * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,

@@ -22,7 +22,7 @@ SPECV_EHIP = -3
 SPECV_EALIGN = -4
 SPECV_ESTATE = -5
 SPECV_MAX_DRAFT = 64
-SPECV_MAX_VOCAB = 1 << 19
+SPECV_MAX_VOCAB = 1 << 18
 
 # Entry points declared in include/specv.h, with their ctypes signatures.
 _SIGNATURES = {

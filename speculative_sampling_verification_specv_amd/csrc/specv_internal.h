@@ -10,18 +10,17 @@ namespace specv {
 constexpr int kThreads = 256;      // threads per workgroup (4 wave64s)
 constexpr int kStatBytes = 65536;  // row-statistics item: 64 KB of one row, either dtype
 
-// A draw member covers 8 KB of each row it reads: 4096 bfloat16 or 2048
-// float32 logits, split into kSubs sub-chunks of 32 consecutive threads.
-constexpr int kMemberBytes = 8192;
-inline int member_elems(int dtype) { return kMemberBytes / (dtype == 0 ? 4 : 2); }
-constexpr int kMinMemberElems = kMemberBytes / 4;
+// A draw member covers 4096 logits of each row it reads (16 per thread),
+// split into kSubs sub-chunks of 32 consecutive threads.
+constexpr int kMemberElems = 4096;
+inline int member_elems(int) { return kMemberElems; }
 constexpr int kSubs = 8;
 constexpr int kUncMax = 8;  // uncertain-sign tokens a member record lists
 
 // Largest vocabulary a handle accepts, so a sequence's members fit one per
-// thread of the finisher.
-constexpr int kMaxVocab = 1 << 19;
-constexpr int kMaxMembers = kMaxVocab / kMinMemberElems;
+// lane of a wave in the finisher.
+constexpr int kMaxVocab = 1 << 18;
+constexpr int kMaxMembers = kMaxVocab / kMemberElems;
 
 // Smallest positive temperature accepted: keeps log2(e)/T and max|z|*log2(e)/T
 // finite in fp32 for logits up to 2^64 in magnitude.

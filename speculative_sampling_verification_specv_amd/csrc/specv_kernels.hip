@@ -42,8 +42,8 @@ constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRows = 2 * 64 + 1;
 constexpr int kStatVecs = kStatBytes / 16 / kThreads;  // 16-byte vectors per thread per item
-static_assert(kMaxMembers <= kThreads, "one member per thread in the finisher");
-static_assert(kMaxMembers * kSubs % 64 == 0, "sub-chunk search layout");
+static_assert(kMaxMembers <= 64, "one member per lane of the finisher's wave 0");
+
 
 __device__ __forceinline__ bool temperature_valid(float t) {
   return t == 0.0f || (t >= kMinTemperature && t <= kFltMax);
@@ -131,7 +131,7 @@ struct Logit;
 template <>
 struct Logit<float> {
   static constexpr int kVec = 4;   // logits per 16-byte load
-  static constexpr int kPer = 8;  // logits of one row per draw-member thread
+  static constexpr int kPer = 16;  // logits of one row per draw-member thread
   __device__ static float at(const float* p, int64_t i) { return p[i]; }
   __device__ static uint32_t bits(const float* p, int64_t i) { return __float_as_uint(p[i]); }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b); }
@@ -397,19 +397,30 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 struct PartialRec {
   uint64_t w0, w1;
 };
-struct SeqRec {     // one sequence's decision, published for its draw members
-  uint64_t flag;    // kPublished | j << 8 | mode, written after the other words; 0 between calls
-  uint64_t maxima;  // maxima of target row j (low half) and draft row j
-  double log_rho;   // log(Zt/Zd) of row j from the fp32 row sums
+// One sequence's decision, published for its draw members as three words that
+// each carry kPublished, so a reader takes each word once it is set and needs
+// no order between them; all three are zero between calls.
+struct SeqRec {
+  uint64_t w0;  // kPublished | j << 40 | mode << 32 | maximum of target row j (low half)
+  uint64_t w1;  // kPublished | maximum of draft row j (low half)
+  uint64_t w2;  // kPublished | log(Zt/Zd) of row j, from the fp32 row sums, as fp32 (low half)
 };
 constexpr uint64_t kPublished = uint64_t(1) << 63;
-struct MemberRec {  // one draw member's fp64 sums
-  double zt, zd;                  // sums of the target and draft exps
-  double a[kSubs], bs[kSubs];     // per sub-chunk: sums of et and ed of certainly positive weight
-  int n_unc;                      // uncertain-sign tokens (kUncMax + 1: more than listed)
-  int pos[kUncMax];               // their positions, ascending
-  double uet[kUncMax], ued[kUncMax];
+// One draw member's fp64 sums as 64-bit words (written once each, read by
+// the finisher after the member has reported):
+struct MemberRec {
+  static constexpr int kZt = 0, kZd = 1;  // sums of the target and draft exps
+  static constexpr int kA = 2;            // + k: sub-chunk k's sum of et over certainly positive tokens
+  static constexpr int kB = kA + kSubs;   // + k: the same sum of ed
+  static constexpr int kNUnc = kB + kSubs;  // uncertain-sign tokens (kUncMax + 1: more than listed)
+  static constexpr int kPos = kNUnc + 1;    // + i: their positions, ascending
+  static constexpr int kEt = kPos + kUncMax;  // + i: their exps in the target row
+  static constexpr int kEd = kEt + kUncMax;   // + i: and in the draft row
+  static constexpr int kWords = kEd + kUncMax;
+  uint64_t w[kWords];
 };
+
+__device__ __forceinline__ void put_d_word(MemberRec* r, int word, double v) { put_d(reinterpret_cast<double*>(&r->w[word]), v); }
 
 // Everything the launches need; passed by value.
 struct Params {
@@ -612,17 +623,16 @@ __device__ __forceinline__ bool last_arrival(int* count, int total) {
 // ---------------------------------------------------------------------------
 // Decision.
 
-// Publishes sequence b's decision for its draw members: the data words, then
-// (once they are complete) the flag word. Only sampled sequences (T > 0) have
-// draw members waiting; the last of them clears the flag again, so it reads
-// zero at every call's start (also when a captured launch is replayed).
+// Publishes sequence b's decision for its draw members. Only sampled
+// sequences (T > 0) have draw members waiting; the last of them zeroes the
+// record again, so it reads zero at every call's start (also when a captured
+// launch is replayed).
 __device__ __forceinline__ void publish(const Params& P, int b, int mode, int j, float mt, float md,
                                         double log_rho) {
   SeqRec* q = P.seq + b;
-  put_u64(&q->maxima, pack2(mt, md));
-  put_d(&q->log_rho, log_rho);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  put_u64(&q->flag, kPublished | (uint32_t(j) << 8) | uint32_t(mode));
+  put_u64(&q->w0, kPublished | (uint64_t(uint32_t(j)) << 40) | (uint64_t(uint32_t(mode)) << 32) | __float_as_uint(mt));
+  put_u64(&q->w1, kPublished | __float_as_uint(md));
+  put_u64(&q->w2, kPublished | __float_as_uint(float(log_rho)));
 }
 
 // Whether sequence b's draw members wait for its decision: a positive valid
@@ -646,13 +656,20 @@ static_assert(int64_t(kMaxVocab) * 4 / kStatBytes * kWaves <= kStageParts, "a ro
 
 struct DrawShared {
   double red[4 * kWaves];
-  double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
-  double unc_ed[2][kThreads];
+  union {
+    struct {
+      double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
+      double unc_ed[2][kThreads];
+    } mem;
+    uint64_t stage[kMaxMembers * MemberRec::kWords];  // finisher: the sequence's member records
+  };
+  double tw[32 * 16];  // finisher: the crossing sub-chunk's token weights
   int unc_base[kWaves];
-  int nunc[kMaxMembers];  // finisher: per member its uncertain count
   int slots[kWaves];
   int pick;
   double rem;
+  double rt, rd, total;
+  unsigned long long over;
 };
 
 struct Shared {
@@ -776,8 +793,11 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
       }
       if (row_ok && k_in_seg == 0) {
         if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
-        // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c) exactly.
-        const double logz = greedy ? 0.0 : kLn2 * (log2(double(s)) - double(fmaf(m, c, -scaled_max(m, c))));
+        // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c)
+        // exactly; log2 s in fp32 (within 1e-7 of |log2 s|: s carries fp32
+        // rounding already).
+        const double logz =
+            greedy ? 0.0 : kLn2 * (double(__builtin_amdgcn_logf(s)) - double(fmaf(m, c, -scaled_max(m, c))));
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
@@ -823,7 +843,8 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
       // log(q(d)/p(d)); the test is u < exp of it.
       const double lr = ((double(zt) - double(ds.row_m[N + tid])) - (double(zd) - double(ds.row_m[tid]))) * inv_t -
                         (ds.row_logz[N + tid] - ds.row_logz[tid]);
-      accept = double(ua) < exp(lr);
+      // u < 1 <= exp(lr) when lr >= 0; the library exp only where the local one underflows.
+      accept = lr >= 0.0 || double(ua) < (lr >= -708.0 ? exp_nonpos(lr) : exp(lr));
     }
   }
   // N <= 64: every decision lives in wave 0.
@@ -1046,8 +1067,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     unc_k1 = n_unc > 1 ? __ffs(int(unc & (unc - 1))) - 1 : 0;
     for (int i = 0; i < min(n_unc, 2); ++i) {
       const int k = i == 0 ? unc_k0 : unc_k1;
-      ws.unc_et[i][tid] = exp_nonpos(exp_arg(element_at<T>(xt, k), d.nmt, d.inv_t));
-      ws.unc_ed[i][tid] = exp_nonpos(exp_arg(element_at<T>(xd, k), d.nmd, d.inv_t));
+      ws.mem.unc_et[i][tid] = exp_nonpos(exp_arg(element_at<T>(xt, k), d.nmt, d.inv_t));
+      ws.mem.unc_ed[i][tid] = exp_nonpos(exp_arg(element_at<T>(xd, k), d.nmd, d.inv_t));
     }
   }
   MemberRec* rec = P.records + int64_t(b) * P.nm + c;
@@ -1059,41 +1080,51 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     sb += __shfl_xor(sb, off);
   }
   if ((lane & 31) == 0) {
-    put_d(&rec->a[tid >> 5], sa);
-    put_d(&rec->bs[tid >> 5], sb);
+    put_d_word(rec, MemberRec::kA + (tid >> 5), sa);
+    put_d_word(rec, MemberRec::kB + (tid >> 5), sb);
   }
-  block_sum2(st, sd, ws.red);
-  int total = 0;
-  if (residual) {
-    // Uncertain tokens in ascending token order (threads own ascending runs);
-    // a thread past its staging capacity overflows the record.
-    const int cnt = (n_unc <= 2) ? n_unc : kUncMax + 1;
-    int incl = cnt;
+  // One exchange through LDS for the wave totals of st and sd and the wave
+  // counts of uncertain tokens (in ascending token order: threads own
+  // ascending runs; a thread past its staging capacity overflows the record).
+  const int cnt = !residual ? 0 : (n_unc <= 2) ? n_unc : kUncMax + 1;
+  int incl = cnt;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int up = __shfl_up(incl, off);
-      if (lane >= off) incl += up;
-    }
-    if (lane == 63) ws.unc_base[tid >> 6] = incl;
-    barrier();
-    int slot = incl - cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    st += __shfl_xor(st, off);
+    sd += __shfl_xor(sd, off);
+    const int up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  const int wave = tid >> 6;
+  if (lane == 63) {
+    ws.red[wave] = st;
+    ws.red[kWaves + wave] = sd;
+    ws.unc_base[wave] = incl;
+  }
+  barrier();
+  int slot = incl - cnt, total = 0;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
-      if (wv < (tid >> 6)) slot += ws.unc_base[wv];
-      total += ws.unc_base[wv];
-    }
-    if (total <= kUncMax) {
-      for (int i = 0; i < cnt; ++i) {
-        put_i(&rec->pos[slot + i], e + (i == 0 ? unc_k0 : unc_k1));
-        put_d(&rec->uet[slot + i], ws.unc_et[i][tid]);
-        put_d(&rec->ued[slot + i], ws.unc_ed[i][tid]);
-      }
+  for (int wv = 0; wv < kWaves; ++wv) {
+    if (wv < wave) slot += ws.unc_base[wv];
+    total += ws.unc_base[wv];
+  }
+  if (total <= kUncMax) {
+    for (int i = 0; i < cnt; ++i) {
+      put_u64(&rec->w[MemberRec::kPos + slot + i], uint64_t(uint32_t(e + (i == 0 ? unc_k0 : unc_k1))));
+      put_d_word(rec, MemberRec::kEt + slot + i, ws.mem.unc_et[i][tid]);
+      put_d_word(rec, MemberRec::kEd + slot + i, ws.mem.unc_ed[i][tid]);
     }
   }
   if (tid == 0) {
-    put_d(&rec->zt, st);
-    put_d(&rec->zd, sd);
-    put_i(&rec->n_unc, min(total, kUncMax + 1));
+    double zt = ws.red[0], zd = ws.red[kWaves];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) {
+      zt += ws.red[wv];
+      zd += ws.red[kWaves + wv];
+    }
+    put_d_word(rec, MemberRec::kZt, zt);
+    put_d_word(rec, MemberRec::kZd, zd);
+    put_u64(&rec->w[MemberRec::kNUnc], uint64_t(min(total, kUncMax + 1)));
   }
 }
 
@@ -1141,104 +1172,185 @@ __device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared
 }
 
 // ---------------------------------------------------------------------------
-// The finisher (the last member of a sequence): from the member records, the
-// normalisers and sub-chunk weights (thread c holds member c's), the
-// sub-chunk where the inverse CDF crosses u*S, an exact rescan of it, the
-// token.
+// The finisher (the last member of a sequence to report): the member records
+// staged in LDS; wave 0 (lane c = member c) forms the normalisers, the
+// sub-chunk weights and the sub-chunk where the inverse CDF crosses u*S; the
+// workgroup forms the exact weights of that sub-chunk's tokens; wave 0 finds
+// the token.
+
+// Inverse CDF within wave 0 over n values per lane, in lane order then value
+// order, against `target`: the first value with positive weight whose
+// inclusive prefix exceeds it, else the last positive one; returns lane*n +
+// index (-1 if none is positive) and rem = target minus the prefix before it.
+// `total` gets the sum of all values. Uniform over the wave.
+template <int n>
+__device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, bool scale_by_total, double& rem,
+                                                double& total) {
+  const int lane = threadIdx.x & 63;
+  double own = 0.0;
+#pragma unroll
+  for (int k = 0; k < n; ++k) own += w[k];
+  double incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  total = __shfl(incl, 63);
+  const double target = scale_by_total ? u * total : u;
+  double cum = __shfl_up(incl, 1);
+  if (lane == 0) cum = 0.0;
+  double hit_pre = 0.0, last_pre = 0.0;
+  int hit = -1, lastp = -1;
+#pragma unroll
+  for (int k = 0; k < n; ++k) {
+    const double x = w[k];
+    if (x > 0.0) {
+      if (hit < 0 && cum + x > target) {
+        hit = k;
+        hit_pre = cum;
+      }
+      lastp = k;
+      last_pre = cum;
+    }
+    cum += x;
+  }
+  const unsigned long long hm = __ballot(hit >= 0);
+  if (hm) {
+    const int src = __ffsll(hm) - 1;
+    rem = target - __shfl(hit_pre, src);
+    return src * n + __shfl(hit, src);
+  }
+  const unsigned long long pm = __ballot(lastp >= 0);
+  if (pm) {
+    const int src = 63 - __clzll(pm);
+    rem = target - __shfl(last_pre, src);
+    return src * n + __shfl(lastp, src);
+  }
+  rem = target;
+  return -1;
+}
 
 template <typename T>
 __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s) {
   const bool residual = s.mode == kModeResidual;
   constexpr int kPer = Logit<T>::kPer;
-  constexpr int kQ = kPer / 8;
+  constexpr int kQ = kPer / 8;  // tokens per thread in the rescan
+  static_assert(32 * kPer <= 32 * 16, "rescan buffer");
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
-  const int nm = P.nm;
-  const bool mine = tid < nm;
-  const MemberRec* rec = P.records + int64_t(b) * nm + (mine ? tid : 0);
-  double zt = 0.0, zd = 0.0;
-  double a[kSubs], bs[kSubs], w[kSubs];
-  int nunc = 0;
+  const int lane = tid & 63;
+  const int nm = P.nm;  // <= 64
+  // The sequence's member records, in one coalesced round trip: every load
+  // is issued (at a clamped index) before any is stored.
+  constexpr int kW = MemberRec::kWords;
+  constexpr int kStageIters = (kMaxMembers * kW + kThreads - 1) / kThreads;
+  const uint64_t* src = P.records[0].w + (int64_t(b) * nm) * kW;
+  const int n_words = nm * kW;
+  uint64_t words[kStageIters];
 #pragma unroll
-  for (int k = 0; k < kSubs; ++k) a[k] = bs[k] = 0.0;
-  if (mine) {
-    zt = get_d(&rec->zt);
-    zd = get_d(&rec->zd);
-    nunc = get_i(&rec->n_unc);
+  for (int u = 0; u < kStageIters; ++u) words[u] = get_u64(src + min(tid + u * kThreads, n_words - 1));
+#pragma unroll
+  for (int u = 0; u < kStageIters; ++u)
+    if (tid + u * kThreads < n_words) ws.stage[tid + u * kThreads] = words[u];
+  barrier();
+  trace_at(1, b, 1);
+  const DrawRows<T> d = draw_rows<T>(P, b, s);
+  double w[kSubs];
+#pragma unroll
+  for (int k = 0; k < kSubs; ++k) w[k] = 0.0;
+  const bool mine = lane < nm;
+  const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
+  if (tid < 64) {
+    // Normalisers (a fixed butterfly over the members), then member lane's
+    // sub-chunk weights: A/Zt - B/Zd of the certain tokens plus the listed
+    // uncertain ones in token order.
+    double zt = mine ? bits_to_double(r[MemberRec::kZt]) : 0.0;
+    double zd = mine ? bits_to_double(r[MemberRec::kZd]) : 0.0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      zt += __shfl_xor(zt, off);
+      zd += __shfl_xor(zd, off);
+    }
+    const double rt = 1.0 / zt;
+    const double rd = residual ? 1.0 / zd : 0.0;
+    const int nunc = mine ? int(r[MemberRec::kNUnc]) : 0;
 #pragma unroll
     for (int k = 0; k < kSubs; ++k) {
-      a[k] = get_d(&rec->a[k]);
-      bs[k] = get_d(&rec->bs[k]);
+      const double ak = bits_to_double(r[MemberRec::kA + k]);
+      w[k] = !mine ? 0.0 : residual ? fma(ak, rt, -__dmul_rn(bits_to_double(r[MemberRec::kB + k]), rd)) : ak;
     }
-    ws.nunc[tid] = nunc;
-  }
-  // Normalisers (fixed order: thread c holds member c's sums).
-  block_sum2(zt, zd, ws.red);
-  trace_at(1, b, 1);
-  const double rt = 1.0 / zt;
-  const double rd = residual ? 1.0 / zd : 0.0;
-  const DrawRows<T> d = draw_rows<T>(P, b, s);
-  // Sub-chunk weights A/Zt - B/Zd of the certain tokens, then the listed
-  // uncertain tokens in token order.
-#pragma unroll
-  for (int k = 0; k < kSubs; ++k) w[k] = !mine ? 0.0 : residual ? fma(a[k], rt, -__dmul_rn(bs[k], rd)) : a[k];
-  if (residual && mine && nunc > 0 && nunc <= kUncMax) {
-    // The whole list at once, then its first nunc entries in order.
-    int upos[kUncMax];
-    double uet[kUncMax], ued[kUncMax];
-#pragma unroll
-    for (int i = 0; i < kUncMax; ++i) {
-      upos[i] = get_i(&rec->pos[i]);
-      uet[i] = get_d(&rec->uet[i]);
-      ued[i] = get_d(&rec->ued[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kUncMax; ++i) {
-      if (i < nunc) {
-        const int sub = (upos[i] - tid * kThreads * kPer) / (32 * kPer);
-        const double v = resid_weight(uet[i], ued[i], rt, rd);
+    if (residual && nunc <= kUncMax) {
+      for (int i = 0; i < nunc; ++i) {
+        const int sub = (int(r[MemberRec::kPos + i]) - lane * kThreads * kPer) / (32 * kPer);
+        const double v = resid_weight(bits_to_double(r[MemberRec::kEt + i]), bits_to_double(r[MemberRec::kEd + i]), rt, rd);
 #pragma unroll
         for (int k = 0; k < kSubs; ++k) w[k] += (k == sub) ? v : 0.0;
       }
     }
+    const unsigned long long over = __ballot(residual && mine && nunc > kUncMax);
+    if (lane == 0) {
+      ws.rt = rt;
+      ws.rd = rd;
+      ws.over = over;
+    }
   }
-  // Members whose uncertain tokens overflowed their record: exact weights.
-  if (residual && block_any(mine && nunc > kUncMax))
-    for (int c = 0; c < nm; ++c)
-      if (ws.nunc[c] > kUncMax) exact_member_weights<T>(P, ws, d, c, rt, rd, w);
-  double run = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSubs; ++k) run += w[k];
-  double S;
-  double pre = block_excl_scan(run, S, ws.red);
+  barrier();
+  const double rt = ws.rt, rd = ws.rd;
+  // Members whose uncertain tokens overflowed their record: exact weights
+  // (whole workgroup; lane c of wave 0 receives member c's).
+  for (unsigned long long over = ws.over; over != 0ull; over &= over - 1ull)
+    exact_member_weights<T>(P, ws, d, __ffsll(over) - 1, rt, rd, w);
+  const double us = double(load_uniform(P.sample_u + b));
   bool from_q = false;
-  if (residual && !(S > 0.0)) {
+  if (tid < 64) {
+    double rem, total;
+    const int pick = wave_inverse_cdf<kSubs>(w, us, true, rem, total);
+    if (lane == 0) {
+      ws.pick = pick;
+      ws.rem = rem;
+      ws.total = total;
+    }
+  }
+  barrier();
+  if (residual && !(ws.total > 0.0)) {
     // Every residual weight rounded to zero: draw from q_j itself, sub-chunk
     // by sub-chunk exactly.
     from_q = true;
     for (int c = 0; c < nm; ++c) exact_member_weights<T>(P, ws, d, c, rt, 0.0, w);
-    run = 0.0;
-#pragma unroll
-    for (int k = 0; k < kSubs; ++k) run += w[k];
-    pre = block_excl_scan(run, S, ws.red);
+    if (tid < 64) {
+      double rem, total;
+      const int pick = wave_inverse_cdf<kSubs>(w, us, true, rem, total);
+      if (lane == 0) {
+        ws.pick = pick;
+        ws.rem = rem;
+      }
+    }
+    barrier();
   }
-  const double us = double(load_uniform(P.sample_u + b));
-  block_inverse_cdf<kSubs>(ws, w, pre, us * S);
   const int pick = max(ws.pick, 0);
   const double rem = ws.rem;
   trace_at(1, b, 2);
-  // Rescan the crossing sub-chunk: exact weights, the token.
+  // The crossing sub-chunk's exact token weights (kQ per thread, in token
+  // order), then wave 0 finds the token: lane l takes weights 8l .. 8l+7.
   double wq[kQ];
   int e0;
-  const double own = sub_weights<T>(P, d, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
+  sub_weights<T>(P, d, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
   trace_at(1, b, 3);
-  double tot;
-  const double pre2 = block_excl_scan(own, tot, ws.red);
-  block_inverse_cdf<kQ>(ws, wq, pre2, rem);
-  if (tid == 0) {
-    const int k = ws.pick;
-    const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
-    P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) ws.tw[tid * kQ + q] = wq[q];
+  barrier();
+  if (tid < 64) {
+    constexpr int kL = 32 * kPer / 64;  // token weights per lane
+    double v[kL];
+#pragma unroll
+    for (int k = 0; k < kL; ++k) v[k] = ws.tw[lane * kL + k];
+    double rem2, total2;
+    const int k = wave_inverse_cdf<kL>(v, rem, false, rem2, total2);
+    if (lane == 0) {
+      const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
+      P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
+    }
   }
 }
 
@@ -1292,19 +1404,18 @@ __shared__ int g_seq_ok;
 __device__ __forceinline__ bool wait_decision(const Params& P, int b, SeqInfo& s) {
   if (threadIdx.x == 0) {
     const SeqRec* q = P.seq + b;
-    uint64_t f = get_u64(&q->flag);
-    for (int i = 0; !(f & kPublished) && i < kWaitPolls; ++i) {
+    uint64_t w0 = get_u64(&q->w0), w1 = get_u64(&q->w1), w2 = get_u64(&q->w2);
+    for (int i = 0; !(w0 & w1 & w2 & kPublished) && i < kWaitPolls; ++i) {
       __builtin_amdgcn_s_sleep(8);
-      f = get_u64(&q->flag);
+      if (!(w0 & kPublished)) w0 = get_u64(&q->w0);
+      if (!(w1 & kPublished)) w1 = get_u64(&q->w1);
+      if (!(w2 & kPublished)) w2 = get_u64(&q->w2);
     }
-    const bool ok = (f & kPublished) != 0;
+    const bool ok = (w0 & w1 & w2 & kPublished) != 0;
     g_seq_ok = ok;
-    g_seq = SeqInfo{kModeNone, 0, 0.0f, 0.0f, 0.0};
-    if (ok) {
-      const uint64_t mx = get_u64(&q->maxima);
-      g_seq = SeqInfo{int(f & 0xff), int((f >> 8) & 0xffffff), __uint_as_float(uint32_t(mx)),
-                      __uint_as_float(uint32_t(mx >> 32)), get_d(&q->log_rho)};
-    }
+    g_seq = ok ? SeqInfo{int((w0 >> 32) & 0xff), int((w0 >> 40) & 0xffff), __uint_as_float(uint32_t(w0)),
+                         __uint_as_float(uint32_t(w1)), double(__uint_as_float(uint32_t(w2)))}
+               : SeqInfo{kModeNone, 0, 0.0f, 0.0f, 0.0};
   }
   barrier();
   s = g_seq;
@@ -1331,7 +1442,11 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
   const bool last = last_arrival(P.draw_done + b * kCounterStride, P.nm);
   trace(0, 4);
   if (last) {
-    if (threadIdx.x == 0) put_u64(&P.seq[b].flag, 0);
+    if (threadIdx.x == 0) {
+      put_u64(&P.seq[b].w0, 0);
+      put_u64(&P.seq[b].w1, 0);
+      put_u64(&P.seq[b].w2, 0);
+    }
     if (s.mode != kModeNone) {
       critical_path();
       trace_at(1, b, 0);

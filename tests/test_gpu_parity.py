@@ -170,6 +170,17 @@ def test_vocab_shapes(dtype, vocab):
     tally.check(f"V={vocab}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_max_vocab(dtype):
+    """The largest vocabulary a handle takes: 64 draw members per sequence, one per lane of the finisher."""
+    require_gpu()
+    V = _lib.SPECV_MAX_VOCAB
+    wl = synth.Workload("maxv", 10, 4, 2, V, dtype, 2.5, 1.1, (0.2, 1.0), (1.0, 0.7))
+    b = synth.make_batch(wl, seed=5)
+    _, tally = _parity(b, label=f"V={V} {dtype}")
+    tally.check(f"V={V}")
+
+
 @pytest.mark.parametrize("n_draft", [1, 2, 63, 64])
 def test_n_draft_limits(n_draft):
     require_gpu()
