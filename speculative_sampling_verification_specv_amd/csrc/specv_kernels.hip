@@ -1047,8 +1047,9 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
       const float lr = fmaf(ztk - zdk, inv_tf, dmf);
       const bool pos = lr > hi;
       const bool band = !pos && lr >= lo;
-      sa += pos ? et : 0.0;
-      sb += pos ? ed : 0.0;
+      const double pos_d = pos ? 1.0 : 0.0;  // adds et and ed exactly, or nothing
+      sa = fma(pos_d, et, sa);
+      sb = fma(pos_d, ed, sb);
       unc |= band ? (1u << k) : 0u;
     }
   } else {

@@ -41,10 +41,12 @@ __host__ __device__ inline uint64_t double_to_bits(double d) {
 // Waite: n * ln2_hi is exact for |n| < 2^11, the low part adds 1e-16
 // relative); exp(r) from its degree-11 Taylor polynomial by Horner's rule
 // (truncation below 1e-14 relative on |r| <= ln2/2; one coefficient per
-// step, so the coefficients stay scalar operands); 2^n by ldexp. Below
-// a = -708 (and for -inf or NaN) the result is 0, which drops only terms under
-// 3.3e-308 of the row maximum. Relative error below 1e-13.
+// step, so the coefficients stay scalar operands); 2^n by ldexp, which also
+// gives the subnormal range. Arguments below -746 (and -inf or NaN) are
+// clamped to -746, where 2^n * exp(r) rounds to exactly 0. Relative error below
+// 1e-13 down to a = -708.
 __host__ __device__ inline double exp_nonpos(double a) {
+  a = fmax(a, -746.0);
   const double kShift = 6755399441055744.0;         // 1.5 * 2^52
   const double kInvLn2 = 1.4426950408889634;        // 1 / ln 2
   const double kLn2Hi = 6.93147180369123816490e-01;  // ln 2, upper bits (low 32 bits zero)
@@ -65,8 +67,7 @@ __host__ __device__ inline double exp_nonpos(double a) {
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  const double res = ldexp(p, n);
-  return (a >= -708.0) ? res : 0.0;
+  return ldexp(p, n);
 }
 
 }  // namespace specv

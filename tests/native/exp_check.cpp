@@ -23,6 +23,12 @@ int main() {
   printf("exp0 %.17g\n", specv::exp_nonpos(0.0));
   printf("exp_minus_inf %.17g\n", specv::exp_nonpos(-INFINITY));
   printf("exp_nan %.17g\n", specv::exp_nonpos(NAN));
-  printf("exp_below %.17g\n", specv::exp_nonpos(-709.0));
+  printf("exp_below %.17g\n", specv::exp_nonpos(-746.0));
+  printf("exp_far_below %.17g\n", specv::exp_nonpos(-1.0e300));
+  // Subnormal range: within one unit of the smallest subnormal of expl.
+  double sub_err = 0.0;
+  for (double a = -708.5; a > -745.5; a -= 0.37)
+    sub_err = fmax(sub_err, fabs(specv::exp_nonpos(a) - static_cast<double>(expl(static_cast<long double>(a)))));
+  printf("subnormal_abs_err %.3e\n", sub_err);
   return 0;
 }

@@ -35,3 +35,10 @@ def test_special_values(exp_report):
     assert float(exp_report["exp_minus_inf"]) == 0.0
     assert float(exp_report["exp_nan"]) == 0.0
     assert float(exp_report["exp_below"]) == 0.0
+    assert float(exp_report["exp_far_below"]) == 0.0
+
+
+def test_subnormal_range(exp_report):
+    # Below -708 the results are subnormal or tiny normals; they stay within a
+    # few units of the smallest subnormal (4.9e-324) of the exact value.
+    assert float(exp_report["subnormal_abs_err"].split()[0]) <= 2.0e-323
