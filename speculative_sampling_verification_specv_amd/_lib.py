@@ -192,6 +192,40 @@ class Verifier:
         self._last = (B, N)
         return out_tokens, out_n_accepted
 
+    def bind(self, draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms, temperature,
+             out_tokens, out_n_accepted, stream=None):
+        """Check one call's arguments once; return a function that enqueues exactly that call.
+
+        The returned function re-issues specv_verify with the same buffers and
+        stream and no per-call Python checks, for loops that refill the same
+        tensors in place (the caller keeps them alive). It raises SpecvError on
+        a nonzero status.
+        """
+        import torch
+
+        B, N = draft_tokens.shape
+        V = self.vocab
+        self._expect(draft_logits, "draft_logits", (B, N, V), self.torch_dtype)
+        self._expect(target_logits, "target_logits", (B, N + 1, V), self.torch_dtype)
+        self._expect(draft_tokens, "draft_tokens", (B, N), torch.int32)
+        self._expect(accept_uniforms, "accept_uniforms", (B, N), torch.float32)
+        self._expect(sample_uniforms, "sample_uniforms", (B,), torch.float32)
+        self._expect(temperature, "temperature", (B,), torch.float32)
+        self._expect(out_tokens, "out_tokens", (B, N + 1), torch.int32)
+        self._expect(out_n_accepted, "out_n_accepted", (B,), torch.int32)
+        fn = load_library().specv_verify
+        args = (self.handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
+                _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
+                _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device))
+        self._last = (int(B), int(N))
+
+        def call() -> None:
+            rc = fn(*args)
+            if rc != SPECV_OK:
+                raise SpecvError(rc, "specv_verify")
+
+        return call
+
     def set_timing(self, enable: bool) -> None:
         specv_set_timing(self.handle, enable)
 

@@ -1242,6 +1242,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int nm = P.nm;  // <= 64
+  const double us = double(load_uniform(P.sample_u + b));  // in flight from the start
   // The sequence's member records, in one coalesced round trip: every load
   // is issued (at a clamped index) before any is stored.
   constexpr int kW = MemberRec::kWords;
@@ -1302,7 +1303,6 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   // (whole workgroup; lane c of wave 0 receives member c's).
   for (unsigned long long over = ws.over; over != 0ull; over &= over - 1ull)
     exact_member_weights<T>(P, ws, d, __ffsll(over) - 1, rt, rd, w);
-  const double us = double(load_uniform(P.sample_u + b));
   bool from_q = false;
   if (tid < 64) {
     double rem, total;

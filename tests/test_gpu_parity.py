@@ -229,6 +229,28 @@ def test_determinism():
     assert np.array_equal(a.lse.view(np.uint32), c.lse.view(np.uint32))
 
 
+def test_bound_call_matches_verify():
+    """Verifier.bind: the re-enqueued call gives what verify gives, also after the inputs are refilled in place."""
+    dev = require_gpu()
+    wl = _scaled("b64_n5_v128256_bf16", 8, 20000)
+    b1, b2 = synth.make_batch(wl, seed=21), synth.make_batch(wl, seed=22)
+    B, N = wl.batch, wl.n_draft
+    with Verifier(B, N, wl.vocab, wl.dtype) as v:
+        args = to_device(b1, dev)
+        out_t = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+        call = v.bind(**args, out_tokens=out_t, out_n_accepted=out_n)
+        for bt in (b1, b2, b1):
+            src = to_device(bt, dev)
+            for k in args:
+                args[k].copy_(src[k])
+            ref_t, ref_n = v.verify(**src)
+            out_t.fill_(-7)
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(out_t, ref_t) and torch.equal(out_n, ref_n)
+
+
 def test_graph_replay_matches_eager():
     """A captured call replays correctly with new inputs each time.
 
