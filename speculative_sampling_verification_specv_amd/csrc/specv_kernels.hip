@@ -6,23 +6,26 @@
 // (Speculative Decoding)과 검증 샘플링 아키텍처" (tech.blogsailing.com), section 3's
 // verification loop.
 //
-// Two launches per call, in order on the caller's stream; the second starts
-// when the first's results are complete and visible. Within a launch no
-// workgroup waits for another: per sequence, the workgroup that reports last
-// on an atomic counter carries on with what needs all of them.
+// One launch per call, on the caller's stream. Each workgroup takes a role
+// from its index (role_of); a workgroup only ever waits for workgroups that
+// precede it in the launch order, and every wait is bounded.
 //
-//   row_stats  one workgroup per row-statistics item (32 KB of one row):
-//              fp32 max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T, first
-//              argmax, and the logit at the row's draft token. Pure streaming,
-//              HBM-bound; greedy sequences skip their draft rows. The last
-//              item of a sequence merges its row partials into
-//              log-normalisers, takes the N accept decisions and writes them
-//              out (the token itself when greedy) with the draw's record.
-//   draw       one workgroup per (sequence, 8 KB of each of the draw's row(s)):
-//              fp64 exps of the chunk summed into a member record. The last
-//              member of a sequence is its finisher: the fp64 normalisers and
-//              sub-chunk weights from the records, the sub-chunk where the
-//              inverse CDF crosses u*S, an exact rescan of it, the token.
+//   row statistics  one workgroup per item (kStatBytes of one row): fp32
+//                   max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T, first
+//                   argmax, and the logit at the row's draft token; each wave
+//                   stores its partial. Pure streaming, HBM-bound; greedy
+//                   sequences skip their draft rows.
+//   decision        one workgroup per sequence, after its items: merges the
+//                   row partials into log-normalisers, takes the N accept
+//                   decisions, writes them out (the token itself when greedy)
+//                   and publishes the draw's record.
+//   draw member     one workgroup per (sampled sequence, kMemberElems logits of
+//                   each of the draw's row(s)), after the decision: fp64 exps
+//                   of its logits summed into a member record. The last member
+//                   of a sequence to report is its finisher: the fp64
+//                   normalisers and sub-chunk weights from the records, the
+//                   sub-chunk where the inverse CDF crosses u*S, an exact
+//                   rescan of it, the token.
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
@@ -101,6 +104,92 @@ __device__ __forceinline__ bool block_any(bool v) {
   for (int w = 0; w < kThreads / 64; ++w) r = r || g_vote[w];
   barrier();
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane steps within a wave through DPP (data-parallel primitives: an
+// operand read from another lane of the same row of 16, or broadcast from the
+// last lane of a row), which cost about as much as an ordinary VALU op, where
+// a shuffle through the LDS crossbar waits on a memory round trip.
+//
+// Lane patterns: kXor1 and kXor2 exchange within quads; kHalfMirror pairs
+// lane i with 7 - i and kMirror lane i with 15 - i, so after kXor1, kXor2,
+// kHalfMirror and kMirror every lane holds its row's combination (the
+// combining operation must be commutative and associative up to the fixed
+// order this gives). kRowShr(k) reads lane i - k of the row; kBcast15 and
+// kBcast31 read lane 15 (31) into the rows that row_mask enables; kWaveShr1
+// reads lane i - 1 of the wave. Lanes with no source, or outside row_mask,
+// get `old`.
+constexpr int kXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kBcast15 = 0x142;
+constexpr int kBcast31 = 0x143;
+constexpr int kWaveShr1 = 0x138;
+constexpr int kRowShr(int k) { return 0x110 + k; }
+
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old = 0u) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), kCtrl, kRowMask, 0xf, false));
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp_f32(float v, float old = 0.0f) {
+  return __uint_as_float(dpp_u32<kCtrl, kRowMask>(__float_as_uint(v), __float_as_uint(old)));
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ int dpp_i32(int v, int old = 0) {
+  return int(dpp_u32<kCtrl, kRowMask>(uint32_t(v), uint32_t(old)));
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {  // `old` is 0.0
+  const uint64_t b = double_to_bits(v);
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask>(uint32_t(b)), hi = dpp_u32<kCtrl, kRowMask>(uint32_t(b >> 32));
+  return bits_to_double((uint64_t(hi) << 32) | lo);
+}
+
+// Lane `lane` (uniform) of v.
+__device__ __forceinline__ double read_lane(double v, int lane) {
+  const uint64_t b = double_to_bits(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), lane));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), lane));
+  return bits_to_double((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int read_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ double row_sum(double v) {
+  v += dpp_f64<kXor1>(v);
+  v += dpp_f64<kXor2>(v);
+  v += dpp_f64<kHalfMirror>(v);
+  v += dpp_f64<kMirror>(v);
+  return v;
+}
+
+// Sum over the wave, the same in every lane (rows added in a fixed order).
+__device__ __forceinline__ double wave_sum(double v) {
+  v = row_sum(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
+}
+
+// Inclusive prefix sums over the wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<kRowShr(1)>(v);
+  v += dpp_f64<kRowShr(2)>(v);
+  v += dpp_f64<kRowShr(4)>(v);
+  v += dpp_f64<kRowShr(8)>(v);
+  v += dpp_f64<kBcast15, 0xa>(v);
+  v += dpp_f64<kBcast31, 0xc>(v);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i32<kRowShr(1)>(v);
+  v += dpp_i32<kRowShr(2)>(v);
+  v += dpp_i32<kRowShr(4)>(v);
+  v += dpp_i32<kRowShr(8)>(v);
+  v += dpp_i32<kBcast15, 0xa>(v);
+  v += dpp_i32<kBcast31, 0xc>(v);
+  return v;
 }
 
 // A read-only value at a uniform address, through the constant address space
@@ -249,30 +338,8 @@ __device__ __forceinline__ float element_at(const uint4 (&x)[n], int k) {
 // ---------------------------------------------------------------------------
 // Block reductions (fixed order). `red` holds 2 * kWaves doubles.
 
-__device__ __forceinline__ void block_sum2(double& a, double& b, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    a += __shfl_xor(a, off);
-    b += __shfl_xor(b, off);
-  }
-  barrier();
-  if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6] = a;
-    red[kWaves + (threadIdx.x >> 6)] = b;
-  }
-  barrier();
-  a = red[0];
-  b = red[kWaves];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    a += red[w];
-    b += red[kWaves + w];
-  }
-}
-
 __device__ __forceinline__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum(v);
   barrier();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   barrier();
@@ -349,16 +416,26 @@ __device__ __forceinline__ void acc_merge(float& m, float& s, int& idx, float m2
   m = mm;
 }
 
-// Merge every lane's state of the wave into every lane's (fixed butterfly).
+// One merge step with the state DPP pattern kCtrl brings from another lane
+// (lanes outside kRowMask merge the empty state: no change).
+template <bool kSampled, int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ void merge_step(float& m, float& s, int& idx, float c) {
+  const float m2 = dpp_f32<kCtrl, kRowMask>(m, -INFINITY);
+  const float s2 = dpp_f32<kCtrl, kRowMask>(s, 0.0f);
+  const int i2 = dpp_i32<kCtrl, kRowMask>(idx, INT_MAX);
+  acc_merge<kSampled>(m, s, idx, m2, s2, i2, c);
+}
+
+// Merge every lane's state of the wave (a fixed order); lane 63 holds the
+// whole wave's.
 template <bool kSampled>
 __device__ __forceinline__ void wave_merge(StatAcc& a, float c) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(a.m, off);
-    const float s2 = __shfl_xor(a.s, off);
-    const int i2 = __shfl_xor(a.idx, off);
-    acc_merge<kSampled>(a.m, a.s, a.idx, m2, s2, i2, c);
-  }
+  merge_step<kSampled, kXor1>(a.m, a.s, a.idx, c);
+  merge_step<kSampled, kXor2>(a.m, a.s, a.idx, c);
+  merge_step<kSampled, kHalfMirror>(a.m, a.s, a.idx, c);
+  merge_step<kSampled, kMirror>(a.m, a.s, a.idx, c);
+  merge_step<kSampled, kBcast15, 0xa>(a.m, a.s, a.idx, c);
+  merge_step<kSampled, kBcast31, 0xc>(a.m, a.s, a.idx, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -375,12 +452,8 @@ __device__ __forceinline__ uint64_t get_u64(const void* p) {
   return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void put_d(double* p, double v) { put_u64(p, double_to_bits(v)); }
-__device__ __forceinline__ double get_d(const double* p) { return bits_to_double(get_u64(p)); }
 __device__ __forceinline__ void put_i(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int get_i(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
   return uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
@@ -402,7 +475,7 @@ struct PartialRec {
 // no order between them; all three are zero between calls.
 struct SeqRec {
   uint64_t w0;  // kPublished | j << 40 | mode << 32 | maximum of target row j (low half)
-  uint64_t w1;  // kPublished | maximum of draft row j (low half)
+  uint64_t w1;  // kPublished | temperature << 32 | maximum of draft row j (low half)
   uint64_t w2;  // kPublished | log(Zt/Zd) of row j, from the fp32 row sums, as fp32 (low half)
 };
 constexpr uint64_t kPublished = uint64_t(1) << 63;
@@ -571,7 +644,7 @@ struct Partial {
   int idx;
 };
 
-// Fold a loaded item's share of one wave; every lane gets the wave's partial.
+// Fold a loaded item's share of one wave; lane 63 gets the wave's partial.
 template <typename T>
 __device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g) {
   StatAcc a;
@@ -588,9 +661,9 @@ __device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g
   return Partial{a.m, a.s, zg, a.idx};
 }
 
-// Lane 0 of each wave stores the wave's partial (see PartialRec).
+// Lane 63 of each wave stores the wave's partial (see PartialRec).
 __device__ __forceinline__ void partial_write(const Params& P, int b, int r, int c, const Partial& q) {
-  if ((threadIdx.x & 63) == 0) {
+  if ((threadIdx.x & 63) == 63) {
     PartialRec* p = partial_at(P, b, r, c, threadIdx.x >> 6);
     put_u64(&p->w0, uint64_t(uint32_t(q.idx + 1)) | (uint64_t(__float_as_uint(q.m)) << 32));
     put_u64(&p->w1, pack2(q.s != 0.0f ? q.s : 1.0f, q.zg));
@@ -628,10 +701,11 @@ __device__ __forceinline__ bool last_arrival(int* count, int total) {
 // record again, so it reads zero at every call's start (also when a captured
 // launch is replayed).
 __device__ __forceinline__ void publish(const Params& P, int b, int mode, int j, float mt, float md,
-                                        double log_rho) {
+                                        double log_rho, float temp) {
   SeqRec* q = P.seq + b;
   put_u64(&q->w0, kPublished | (uint64_t(uint32_t(j)) << 40) | (uint64_t(uint32_t(mode)) << 32) | __float_as_uint(mt));
-  put_u64(&q->w1, kPublished | __float_as_uint(md));
+  // A sampled sequence's temperature is positive: 31 bits hold it.
+  put_u64(&q->w1, kPublished | (uint64_t(__float_as_uint(temp)) << 32) | __float_as_uint(md));
   put_u64(&q->w2, kPublished | __float_as_uint(float(log_rho)));
 }
 
@@ -682,6 +756,7 @@ struct Shared {
 __shared__ Shared g_shared;
 
 struct SeqInfo {
+  float temp;
   int mode;
   int j;
   float m_target;
@@ -743,11 +818,9 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
-  // Segments of cs lanes (the row's partial count rounded up to a power of
-  // two, at most 64) each merge one row: lane k of a segment folds partials
-  // k, k + cs, ... of the row in order, then a butterfly within the segment.
-  int cs = 1;
-  while (cs < pr && cs < 64) cs <<= 1;
+  // Quads of lanes each merge one row: lane k of a quad folds partials k,
+  // k + 4, ... of the row in order, then two exchange steps within the quad.
+  constexpr int cs = 4;
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
   bool timed_out = false, any_bad = false;
@@ -782,14 +855,12 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
             acc_merge<true>(m, s, idx, q.m, q.s, q.idx, c);
         }
       }
-      for (int off = 1; off < cs; off <<= 1) {
-        const float m2 = __shfl_xor(m, off);
-        const float s2 = __shfl_xor(s, off);
-        const int i2 = __shfl_xor(idx, off);
-        if (greedy)
-          acc_merge<false>(m, s, idx, m2, s2, i2, c);
-        else
-          acc_merge<true>(m, s, idx, m2, s2, i2, c);
+      if (greedy) {
+        merge_step<false, kXor1>(m, s, idx, c);
+        merge_step<false, kXor2>(m, s, idx, c);
+      } else {
+        merge_step<true, kXor1>(m, s, idx, c);
+        merge_step<true, kXor2>(m, s, idx, c);
       }
       if (row_ok && k_in_seg == 0) {
         if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
@@ -819,7 +890,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     }
     if (tid == 0) {
       P.out_n[b] = late ? -2 : -1;
-      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0);
+      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0, t);
     }
     return;
   }
@@ -861,7 +932,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   if (tid == 0 && !greedy) {
     const float md = j < N ? ds.row_m[j] : 0.0f;
     const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
+    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho, t);
   }
   for (int i = tid; i <= N; i += kThreads) {
     if (i < j)
@@ -891,7 +962,7 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params& P, int b, const S
   DrawRows<T> d;
   d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
   d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
-  d.inv_t = 1.0 / double(load_uniform(P.temperature + b));
+  d.inv_t = 1.0 / double(s.temp);
   d.nmt = -double(s.m_target) * d.inv_t;
   d.nmd = -double(s.m_draft) * d.inv_t;
   return d;
@@ -904,32 +975,6 @@ __device__ __forceinline__ double exp_arg(float z, double nm, double inv_t) { re
 // out so every place that forms a weight gets the same bits.
 __device__ __forceinline__ double resid_weight(double et, double ed, double rt, double rd) {
   return fmax(0.0, fma(et, rt, -__dmul_rn(ed, rd)));
-}
-
-// Exclusive prefix (fixed order) of one value per thread over the workgroup,
-// in thread order; `total` gets the sum of all of them.
-__device__ __forceinline__ double block_excl_scan(double v, double& total, double* red) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  double incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double up = __shfl_up(incl, off);
-    if (lane >= off) incl += up;
-  }
-  double excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.0;
-  barrier();
-  if (lane == 63) red[wave] = incl;
-  barrier();
-  double base = 0.0, sum = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) base += red[w];
-    sum += red[w];
-  }
-  total = sum;
-  return base + excl;
 }
 
 // Lowest (kFirst) or highest thread index whose flag is set, kThreads or -1
@@ -1074,13 +1119,13 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   }
   MemberRec* rec = P.records + int64_t(b) * P.nm + c;
   // Sub-chunk sums: 32 consecutive threads per sub-chunk (lanes 0..31 and
-  // 32..63 of each wave), a fixed butterfly.
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    sa += __shfl_xor(sa, off);
-    sb += __shfl_xor(sb, off);
-  }
-  if ((lane & 31) == 0) {
+  // 32..63 of each wave): row sums, then row 0's added into row 1 and row
+  // 2's into row 3, so lanes 31 and 63 hold them.
+  sa = row_sum(sa);
+  sb = row_sum(sb);
+  sa += dpp_f64<kBcast15, 0xa>(sa);
+  sb += dpp_f64<kBcast15, 0xa>(sb);
+  if ((lane & 31) == 31) {
     put_d_word(rec, MemberRec::kA + (tid >> 5), sa);
     put_d_word(rec, MemberRec::kB + (tid >> 5), sb);
   }
@@ -1088,14 +1133,13 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   // counts of uncertain tokens (in ascending token order: threads own
   // ascending runs; a thread past its staging capacity overflows the record).
   const int cnt = !residual ? 0 : (n_unc <= 2) ? n_unc : kUncMax + 1;
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    st += __shfl_xor(st, off);
-    sd += __shfl_xor(sd, off);
-    const int up = __shfl_up(incl, off);
-    if (lane >= off) incl += up;
-  }
+  const int incl = wave_incl_scan(cnt);
+  st = row_sum(st);
+  sd = row_sum(sd);
+  st += dpp_f64<kBcast15, 0xa>(st);
+  sd += dpp_f64<kBcast15, 0xa>(sd);
+  st += dpp_f64<kBcast31, 0xc>(st);  // lane 63: the wave's totals
+  sd += dpp_f64<kBcast31, 0xc>(sd);
   const int wave = tid >> 6;
   if (lane == 63) {
     ws.red[wave] = st;
@@ -1187,20 +1231,13 @@ __device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared
 template <int n>
 __device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, bool scale_by_total, double& rem,
                                                 double& total) {
-  const int lane = threadIdx.x & 63;
-  double own = 0.0;
+    double own = 0.0;
 #pragma unroll
   for (int k = 0; k < n; ++k) own += w[k];
-  double incl = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double up = __shfl_up(incl, off);
-    if (lane >= off) incl += up;
-  }
-  total = __shfl(incl, 63);
+  const double incl = wave_incl_scan(own);
+  total = read_lane(incl, 63);
   const double target = scale_by_total ? u * total : u;
-  double cum = __shfl_up(incl, 1);
-  if (lane == 0) cum = 0.0;
+  double cum = dpp_f64<kWaveShr1>(incl);  // lane 0: 0
   double hit_pre = 0.0, last_pre = 0.0;
   int hit = -1, lastp = -1;
 #pragma unroll
@@ -1219,14 +1256,14 @@ __device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, 
   const unsigned long long hm = __ballot(hit >= 0);
   if (hm) {
     const int src = __ffsll(hm) - 1;
-    rem = target - __shfl(hit_pre, src);
-    return src * n + __shfl(hit, src);
+    rem = target - read_lane(hit_pre, src);
+    return src * n + read_lane(hit, src);
   }
   const unsigned long long pm = __ballot(lastp >= 0);
   if (pm) {
     const int src = 63 - __clzll(pm);
-    rem = target - __shfl(last_pre, src);
-    return src * n + __shfl(lastp, src);
+    rem = target - read_lane(last_pre, src);
+    return src * n + read_lane(lastp, src);
   }
   rem = target;
   return -1;
@@ -1269,11 +1306,8 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     // uncertain ones in token order.
     double zt = mine ? bits_to_double(r[MemberRec::kZt]) : 0.0;
     double zd = mine ? bits_to_double(r[MemberRec::kZd]) : 0.0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      zt += __shfl_xor(zt, off);
-      zd += __shfl_xor(zd, off);
-    }
+    zt = wave_sum(zt);
+    zd = wave_sum(zd);
     const double rt = 1.0 / zt;
     const double rd = residual ? 1.0 / zd : 0.0;
     const int nunc = mine ? int(r[MemberRec::kNUnc]) : 0;
@@ -1414,9 +1448,10 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, SeqInfo& s
     }
     const bool ok = (w0 & w1 & w2 & kPublished) != 0;
     g_seq_ok = ok;
-    g_seq = ok ? SeqInfo{int((w0 >> 32) & 0xff), int((w0 >> 40) & 0xffff), __uint_as_float(uint32_t(w0)),
-                         __uint_as_float(uint32_t(w1)), double(__uint_as_float(uint32_t(w2)))}
-               : SeqInfo{kModeNone, 0, 0.0f, 0.0f, 0.0};
+    g_seq = ok ? SeqInfo{__uint_as_float(uint32_t(w1 >> 32) & 0x7fffffffu), int((w0 >> 32) & 0xff),
+                         int((w0 >> 40) & 0xffff), __uint_as_float(uint32_t(w0)), __uint_as_float(uint32_t(w1)),
+                         double(__uint_as_float(uint32_t(w2)))}
+               : SeqInfo{0.0f, kModeNone, 0, 0.0f, 0.0f, 0.0};
   }
   barrier();
   s = g_seq;
