@@ -730,6 +730,7 @@ static_assert(int64_t(kMaxVocab) * 4 / kStatBytes * kWaves <= kStageParts, "a ro
 
 struct DrawShared {
   double red[4 * kWaves];
+  double exp2_tab[64];  // kExp2Table, for exp_nonpos_tab (members and the finisher)
   union {
     struct {
       double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
@@ -1068,10 +1069,16 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   const int lane = tid & 63;
   const DrawRows<T> d = draw_rows<T>(P, b, s);
   const int e = (c * kThreads + tid) * kPer;
+  // The exp table first (a cached read that arrives before the rows), then
+  // the rows.
+  const double tab_v = kExp2Table[tid & 63];
   uint4 xt[kG], xd[kG];
   load_packed(d.trow, e, P.vocab, P.vec_ok != 0, xt);
   if (residual) load_packed(d.drow, e, P.vocab, P.vec_ok != 0, xd);
   trace(0, 1);
+  if (tid < 64) ws.exp2_tab[tid] = tab_v;
+  barrier();
+  const double* tab = ws.exp2_tab;
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;
   uint32_t unc = 0;  // bit k: token k of this thread has an uncertain sign
   if (residual) {
@@ -1083,8 +1090,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     for (int k = 0; k < kPer; ++k) {
       const float ztk = Logit<T>::element(xt, k);
       const float zdk = Logit<T>::element(xd, k);
-      const double et = exp_nonpos(exp_arg(ztk, d.nmt, d.inv_t));
-      const double ed = exp_nonpos(exp_arg(zdk, d.nmd, d.inv_t));
+      const double et = exp_nonpos_tab(exp_arg(ztk, d.nmt, d.inv_t), tab);
+      const double ed = exp_nonpos_tab(exp_arg(zdk, d.nmd, d.inv_t), tab);
       st += et;
       sd += ed;
       // +inf when the draft gives the token zero mass, NaN (neither class)
@@ -1099,7 +1106,7 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) st += exp_nonpos(exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t));
+    for (int k = 0; k < kPer; ++k) st += exp_nonpos_tab(exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t), tab);
     sa = st;
   }
   trace(0, 2);
@@ -1113,8 +1120,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     unc_k1 = n_unc > 1 ? __ffs(int(unc & (unc - 1))) - 1 : 0;
     for (int i = 0; i < min(n_unc, 2); ++i) {
       const int k = i == 0 ? unc_k0 : unc_k1;
-      ws.mem.unc_et[i][tid] = exp_nonpos(exp_arg(element_at<T>(xt, k), d.nmt, d.inv_t));
-      ws.mem.unc_ed[i][tid] = exp_nonpos(exp_arg(element_at<T>(xd, k), d.nmd, d.inv_t));
+      ws.mem.unc_et[i][tid] = exp_nonpos_tab(exp_arg(element_at<T>(xt, k), d.nmt, d.inv_t), tab);
+      ws.mem.unc_ed[i][tid] = exp_nonpos_tab(exp_arg(element_at<T>(xd, k), d.nmd, d.inv_t), tab);
     }
   }
   MemberRec* rec = P.records + int64_t(b) * P.nm + c;
@@ -1176,10 +1183,12 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
 // Exact weights of sub-chunk `sub` of member c (whole workgroup): each thread
 // takes kPer/8 consecutive tokens; returns this thread's weights' sum and its
 // weights through w. rd = 0 after a rejection gives et/Zt instead of the
-// residual.
+// residual. The exps are the members' (the same function and table), bit
+// for bit.
 template <typename T>
-__device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>& d, int c, int sub, bool residual,
-                                              double rt, double rd, double (&w)[Logit<T>::kPer / 8], int& e0) {
+__device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>& d, const double* tab, int c, int sub,
+                                              bool residual, double rt, double rd, double (&w)[Logit<T>::kPer / 8],
+                                              int& e0) {
   constexpr int kQ = Logit<T>::kPer / 8;  // a sub-chunk holds 32*kPer tokens: kQ per thread
   e0 = c * kThreads * Logit<T>::kPer + sub * 32 * Logit<T>::kPer + int(threadIdx.x) * kQ;
   double sum = 0.0;
@@ -1187,10 +1196,10 @@ __device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>
   for (int q = 0; q < kQ; ++q) {
     const int x = e0 + q;
     const float zt = x < P.vocab ? Logit<T>::at(d.trow, x) : -INFINITY;
-    const double et = exp_nonpos(exp_arg(zt, d.nmt, d.inv_t));
+    const double et = exp_nonpos_tab(exp_arg(zt, d.nmt, d.inv_t), tab);
     if (residual) {
       const float zd = x < P.vocab ? Logit<T>::at(d.drow, x) : -INFINITY;
-      const double ed = exp_nonpos(exp_arg(zd, d.nmd, d.inv_t));
+      const double ed = exp_nonpos_tab(exp_arg(zd, d.nmd, d.inv_t), tab);
       w[q] = rd > 0.0 ? resid_weight(et, ed, rt, rd) : et * rt;
     } else {
       w[q] = et;
@@ -1209,7 +1218,7 @@ __device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared
   for (int sub = 0; sub < kSubs; ++sub) {
     double wq[Logit<T>::kPer / 8];
     int e0;
-    const double v = block_sum(sub_weights<T>(P, d, c, sub, true, rt, rd, wq, e0), ws.red);
+    const double v = block_sum(sub_weights<T>(P, d, ws.exp2_tab, c, sub, true, rt, rd, wq, e0), ws.red);
 #pragma unroll
     for (int k = 0; k < kSubs; ++k)
       if (k == sub && int(threadIdx.x) == c) w[k] = v;
@@ -1370,7 +1379,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   // order), then wave 0 finds the token: lane l takes weights 8l .. 8l+7.
   double wq[kQ];
   int e0;
-  sub_weights<T>(P, d, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
+  sub_weights<T>(P, d, ws.exp2_tab, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
   trace_at(1, b, 3);
 #pragma unroll
   for (int q = 0; q < kQ; ++q) ws.tw[tid * kQ + q] = wq[q];

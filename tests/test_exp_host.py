@@ -1,7 +1,8 @@
-"""Host check of the kernels' fp64 exponential (specv_math.h), built with g++.
+"""Host check of the kernels' fp64 exponentials (specv_math.h), built with g++.
 
 The draw sums fp64 exps of (z - max)/T; its parity with the oracle needs them
-to ~1e-10 relative. The header states 1e-13.
+to ~1e-10 relative. The header states 1e-13 for the polynomial form and about
+1 ulp for the table form, whose table entries are correctly rounded.
 """
 
 import os
@@ -26,19 +27,26 @@ def exp_report(tmp_path_factory):
     return dict(line.split(None, 1) for line in text.strip().splitlines())
 
 
-def test_relative_error_bound(exp_report):
-    assert float(exp_report["max_rel_err"].split()[0]) < 1e-13
+@pytest.mark.parametrize("form,bound", [("", 1e-13), ("tab_", 5e-16)])
+def test_relative_error_bound(exp_report, form, bound):
+    assert float(exp_report[form + "max_rel_err"].split()[0]) < bound
 
 
-def test_special_values(exp_report):
-    assert float(exp_report["exp0"]) == 1.0
-    assert float(exp_report["exp_minus_inf"]) == 0.0
-    assert float(exp_report["exp_nan"]) == 0.0
-    assert float(exp_report["exp_below"]) == 0.0
-    assert float(exp_report["exp_far_below"]) == 0.0
+@pytest.mark.parametrize("form", ["", "tab_"])
+def test_special_values(exp_report, form):
+    assert float(exp_report[form + "exp0"]) == 1.0
+    assert float(exp_report[form + "exp_minus_inf"]) == 0.0
+    assert float(exp_report[form + "exp_nan"]) == 0.0
+    assert float(exp_report[form + "exp_below"]) == 0.0
+    assert float(exp_report[form + "exp_far_below"]) == 0.0
 
 
-def test_subnormal_range(exp_report):
+@pytest.mark.parametrize("form", ["", "tab_"])
+def test_subnormal_range(exp_report, form):
     # Below -708 the results are subnormal or tiny normals; they stay within a
     # few units of the smallest subnormal (4.9e-324) of the exact value.
-    assert float(exp_report["subnormal_abs_err"].split()[0]) <= 2.0e-323
+    assert float(exp_report[form + "subnormal_abs_err"].split()[0]) <= 2.0e-323
+
+
+def test_table_correctly_rounded(exp_report):
+    assert float(exp_report["table_max_ulp"]) <= 0.5
