@@ -12,8 +12,8 @@
 //
 //   row statistics  one workgroup per item (kStatBytes of one row): fp32
 //                   max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T, first
-//                   argmax, and the logit at the row's draft token; each wave
-//                   stores its partial. Pure streaming, HBM-bound; greedy
+//                   argmax, and the logit at the row's draft token, stored as
+//                   the item's partial. Pure streaming, HBM-bound; greedy
 //                   sequences skip their draft rows.
 //   decision        one workgroup per sequence, after its items: merges the
 //                   row partials into log-normalisers, takes the N accept
@@ -352,56 +352,6 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 // ---------------------------------------------------------------------------
 // Row statistics.
 
-// Running state: m = largest logit seen, idx = its first index, s = sum of
-// 2^(z*c - k) with k = fl(m*c) once a finite logit was seen (0 before, while
-// s is 0 too). The exact product m*c differs from k by r = fma(m, c, -k); the
-// decision removes it.
-struct StatAcc {
-  float m;
-  float k;
-  float s;
-  int idx;
-};
-
-__device__ __forceinline__ void acc_init(StatAcc& a) {
-  a.m = -INFINITY;
-  a.k = 0.0f;
-  a.s = 0.0f;
-  a.idx = INT_MAX;
-}
-
-// Fold n logits with consecutive indices base..base+n-1. A thread visits its
-// indices in increasing order, so a strict '>' keeps a repeated maximum's
-// first index.
-template <bool kSampled, int n>
-__device__ __forceinline__ void acc_values(StatAcc& a, const float (&v)[n], int base, float c) {
-  float vmax = v[0];
-#pragma unroll
-  for (int k = 1; k < n; ++k) vmax = fmaxf(vmax, v[k]);
-  if (vmax > a.m) {
-    int first = n - 1;
-#pragma unroll
-    for (int k = n - 1; k >= 0; --k) first = (v[k] == vmax) ? k : first;
-    if (kSampled) {
-      const float k_new = scaled_max(vmax, c);
-      a.s = (a.s == 0.0f) ? 0.0f : a.s * fast_exp2(a.k - k_new);
-      a.k = k_new;
-    }
-    a.m = vmax;
-    a.idx = base + first;
-  }
-  if (kSampled) {
-    float e[n];
-#pragma unroll
-    for (int k = 0; k < n; ++k) e[k] = fast_exp2(fmaf(v[k], c, -a.k));
-#pragma unroll
-    for (int w = 1; w < n; w *= 2)
-#pragma unroll
-      for (int k = 0; k + w < n; k += 2 * w) e[k] += e[k + w];
-    a.s += e[0];
-  }
-}
-
 // Merge partial (m2, s2, i2) into (m, s, idx).
 template <bool kSampled>
 __device__ __forceinline__ void acc_merge(float& m, float& s, int& idx, float m2, float s2, int i2, float c) {
@@ -426,17 +376,6 @@ __device__ __forceinline__ void merge_step(float& m, float& s, int& idx, float c
   acc_merge<kSampled>(m, s, idx, m2, s2, i2, c);
 }
 
-// Merge every lane's state of the wave (a fixed order); lane 63 holds the
-// whole wave's.
-template <bool kSampled>
-__device__ __forceinline__ void wave_merge(StatAcc& a, float c) {
-  merge_step<kSampled, kXor1>(a.m, a.s, a.idx, c);
-  merge_step<kSampled, kXor2>(a.m, a.s, a.idx, c);
-  merge_step<kSampled, kHalfMirror>(a.m, a.s, a.idx, c);
-  merge_step<kSampled, kMirror>(a.m, a.s, a.idx, c);
-  merge_step<kSampled, kBcast15, 0xa>(a.m, a.s, a.idx, c);
-  merge_step<kSampled, kBcast31, 0xc>(a.m, a.s, a.idx, c);
-}
 
 // ---------------------------------------------------------------------------
 // Device-coherent words. Records that one workgroup hands to another within a
@@ -460,8 +399,7 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 }
 
 // Records written by one workgroup and read by another (or the next launch).
-// Row statistics of one wave of an item as two words, neither of them zero
-// once written: w0 = (first argmax + 1) | max logit << 32, w1 = s | zg << 32
+// Row statistics of one item as two words, neither of them zero once written: w0 = (first argmax + 1) | max logit << 32, w1 = s | zg << 32
 // (s = sum of 2^(z*c - fl(max*c)), >= 1/2 when max is finite; stored as 1
 // when it is 0, i.e. for a greedy or skipped item, or an all -inf one, where no
 // merge uses it; zg = the logit at the row's draft token if the item holds it,
@@ -507,7 +445,7 @@ struct Params {
   int* out_n;
   float* row_lse;
   int* row_argmax;
-  PartialRec* partials;  // [batch][2N+1][nch]
+  PartialRec* partials;  // [batch][2N+1][nch], one per item
   SeqRec* seq;           // [batch]
   MemberRec* records;    // [batch][nm]
   int* draw_done;        // [batch * kCounterStride] draw members done (zero between launches)
@@ -522,9 +460,9 @@ struct Params {
   int vec_ok;  // rows start 16-byte aligned
 };
 
-// Partial of wave w of item (row r, chunk c) of sequence b.
-__device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r, int c, int w) {
-  return P.partials + ((int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c) * kWaves + w;
+// Partial of item (row r, chunk c) of sequence b.
+__device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r, int c) {
+  return P.partials + (int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c;
 }
 
 // The draft token of row r (draft row i or target row i: d_i), or -1 for target row N.
@@ -615,27 +553,38 @@ __device__ __forceinline__ void item_load(const Params& P, const Item& it, ItemR
   g.zg = (it.tok >= it.e0 && it.tok < it.e1) ? load_uniform_bits(row + it.tok) : 0u;
 }
 
-template <typename T, bool kSampled>
-__device__ __forceinline__ void item_fold(const Item& it, const ItemRegs& g, StatAcc& a) {
-  constexpr int kVec = Logit<T>::kVec;
-  const int tid = threadIdx.x;
-  if (tid < it.ea - it.e0) {
-    const float v[1] = {Logit<T>::from_bits(g.head)};
-    acc_values<kSampled>(a, v, it.e0 + tid, it.coef);
-  }
-#pragma unroll
-  for (int u = 0; u < kStatVecs; ++u) {
-    const int k = tid + u * kThreads;
-    if (k < it.nv) {
-      float v[kVec];
-      Logit<T>::unpack(g.x[u], v);
-      acc_values<kSampled>(a, v, it.ea + k * kVec, it.coef);
-    }
-  }
-  if (tid < it.e1 - it.et) {
-    const float v[1] = {Logit<T>::from_bits(g.tail)};
-    acc_values<kSampled>(a, v, it.et + tid, it.coef);
-  }
+// Largest of three floats in one instruction. The logits are finite or
+// -inf, so the quieting of signalling NaNs that fmaxf implies (an extra
+// instruction per operand) is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+
+// Over the wave, the same in every lane (rows combined in a fixed order).
+__device__ __forceinline__ float lane_f(float v, int lane) { return __int_as_float(read_lane(__float_as_int(v), lane)); }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kXor1>(v));
+  v = fmaxf(v, dpp_f32<kXor2>(v));
+  v = fmaxf(v, dpp_f32<kHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, dpp_i32<kXor1>(v));
+  v = min(v, dpp_i32<kXor2>(v));
+  v = min(v, dpp_i32<kHalfMirror>(v));
+  v = min(v, dpp_i32<kMirror>(v));
+  return min(min(read_lane(v, 0), read_lane(v, 16)), min(read_lane(v, 32), read_lane(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kXor1>(v);
+  v += dpp_f32<kXor2>(v);
+  v += dpp_f32<kHalfMirror>(v);
+  v += dpp_f32<kMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 // A folded item: thread 0 holds the merged state.
@@ -644,29 +593,126 @@ struct Partial {
   int idx;
 };
 
-// Fold a loaded item's share of one wave; lane 63 gets the wave's partial.
-template <typename T>
-__device__ __forceinline__ Partial item_reduce(const Item& it, const ItemRegs& g) {
-  StatAcc a;
-  acc_init(a);
-  if (it.sampled) {
-    item_fold<T, true>(it, g, a);
-    wave_merge<true>(a, it.coef);
-  } else {
-    item_fold<T, false>(it, g, a);
-    wave_merge<false>(a, 0.0f);
-  }
-  // The logit at the row's draft token if this chunk holds it.
-  const float zg = (it.tok >= it.e0 && it.tok < it.e1) ? Logit<T>::from_bits(g.zg) : 0.0f;
-  return Partial{a.m, a.s, zg, a.idx};
+// Largest of a 16-byte group of logits as stored. bfloat16: both logits of
+// each 32-bit word are moved into place by byte permutes (not the shift and
+// mask the later pass unpacks with, so the compiler does not keep these
+// copies alive until then).
+__device__ __forceinline__ float group_max(const uint4& x, float) {
+  const float a = max3(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z));
+  return max3(a, __uint_as_float(x.w), __uint_as_float(x.w));
+}
+__device__ __forceinline__ float low_bf16(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
+__device__ __forceinline__ float high_bf16(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
+__device__ __forceinline__ float group_max(const uint4& x, uint16_t) {
+  float a = max3(high_bf16(x.x), high_bf16(x.y), high_bf16(x.z));
+  a = max3(a, high_bf16(x.w), low_bf16(x.x));
+  a = max3(a, low_bf16(x.y), low_bf16(x.z));
+  return max3(a, low_bf16(x.w), low_bf16(x.w));
 }
 
-// Lane 63 of each wave stores the wave's partial (see PartialRec).
-__device__ __forceinline__ void partial_write(const Params& P, int b, int r, int c, const Partial& q) {
-  if ((threadIdx.x & 63) == 63) {
-    PartialRec* p = partial_at(P, b, r, c, threadIdx.x >> 6);
-    put_u64(&p->w0, uint64_t(uint32_t(q.idx + 1)) | (uint64_t(__float_as_uint(q.m)) << 32));
-    put_u64(&p->w1, pack2(q.s != 0.0f ? q.s : 1.0f, q.zg));
+// One wave's share of a loaded item, in two passes over the registers:
+// (1) the largest logit of each thread and where it first occurs (its head
+// element, one of its 16-byte groups, or its tail element), then the wave's
+// largest, M; (2) for a sampled row, the sum of 2^(z*c - fl(M*c)) over the
+// wave's logits, so nothing is rescaled on the way (the last use of each
+// group's registers). The first index of M is looked for only by the lanes
+// that hold it, in the group where they first saw it, read again (from the
+// cache). kFull: every group of every thread lies inside
+// the item (nothing to mask). Returns the wave's partial, the same in every
+// lane.
+template <typename T, bool kSampled, bool kFull>
+__device__ __forceinline__ Partial wave_fold(const Params& P, const Item& it, ItemRegs& g) {
+  constexpr int kVec = Logit<T>::kVec;
+  const int tid = threadIdx.x;
+  const float hv = tid < it.ea - it.e0 ? Logit<T>::from_bits(g.head) : -INFINITY;
+  const float tv = tid < it.e1 - it.et ? Logit<T>::from_bits(g.tail) : -INFINITY;
+  // Pass 1. `where` is -1 for the head, u for group u, kStatVecs for the tail;
+  // a strict '>' keeps the first place (the thread's indices increase in
+  // that order).
+  float tmax = hv;
+  int where = -1;
+#pragma unroll
+  for (int u = 0; u < kStatVecs; ++u) {
+    float gm = group_max(g.x[u], T());
+    if (!kFull) gm = (tid + u * kThreads < it.nv) ? gm : -INFINITY;
+    const bool up = gm > tmax;
+    where = up ? u : where;
+    tmax = up ? gm : tmax;
+  }
+  {
+    const bool up = tv > tmax;
+    where = up ? kStatVecs : where;
+    tmax = up ? tv : tmax;
+  }
+  const float mw = wave_max(tmax);
+  const bool hold = mw != -INFINITY && tmax == mw;
+  int idx = INT_MAX;
+  if (hold && where < 0) idx = it.e0 + tid;
+  if (hold && where == kStatVecs) idx = it.et + tid;
+  const bool seek = hold && where >= 0 && where < kStatVecs;
+  // Pass 2: two running sums, each group's registers dead once summed.
+  float s = 0.0f;
+  if (kSampled && mw != -INFINITY) {
+    const float c = it.coef;
+    const float k = scaled_max(mw, c);
+    float acc0 = fast_exp2(fmaf(hv, c, -k)), acc1 = fast_exp2(fmaf(tv, c, -k));
+#pragma unroll
+    for (int u = 0; u < kStatVecs; ++u) {
+      float v[kVec];
+      Logit<T>::unpack(g.x[u], v);
+      const bool in = kFull || tid + u * kThreads < it.nv;
+#pragma unroll
+      for (int q = 0; q < kVec; q += 2) {
+        const float e0 = fast_exp2(fmaf(v[q], c, -k)), e1 = fast_exp2(fmaf(v[q + 1], c, -k));
+        acc0 += in ? e0 : 0.0f;
+        acc1 += in ? e1 : 0.0f;
+      }
+    }
+    s = wave_sum(acc0 + acc1);
+  }
+  uint4 again = make_uint4(0u, 0u, 0u, 0u);
+  if (seek) again = reinterpret_cast<const uint4*>(item_row<T>(P, it) + it.ea)[tid + where * kThreads];
+  if (seek) {
+    float v[kVec];
+    Logit<T>::unpack(again, v);
+    int first = kVec - 1;
+#pragma unroll
+    for (int q = kVec - 1; q >= 0; --q) first = (v[q] == mw) ? q : first;
+    idx = it.ea + (tid + where * kThreads) * kVec + first;
+  }
+  if (mw != -INFINITY) idx = wave_min(idx);
+  // The logit at the row's draft token if this chunk holds it.
+  const float zg = (it.tok >= it.e0 && it.tok < it.e1) ? Logit<T>::from_bits(g.zg) : 0.0f;
+  return Partial{mw, s, zg, idx};
+}
+
+template <typename T>
+__device__ __forceinline__ Partial item_reduce(const Params& P, const Item& it, ItemRegs& g) {
+  const bool full = it.ea == it.e0 && it.et == it.e1 && it.nv == kStatVecs * kThreads;
+  if (it.sampled) return full ? wave_fold<T, true, true>(P, it, g) : wave_fold<T, true, false>(P, it, g);
+  return full ? wave_fold<T, false, true>(P, it, g) : wave_fold<T, false, false>(P, it, g);
+}
+
+__shared__ Partial g_wave_part[kWaves];
+
+// The item's partial: the waves' partials (lane 63 of each) merged in wave
+// order through LDS, stored by thread 0 (see PartialRec).
+__device__ __forceinline__ void partial_write(const Params& P, const Item& it, const Partial& q) {
+  if ((threadIdx.x & 63) == 63) g_wave_part[threadIdx.x >> 6] = q;
+  barrier();
+  if (threadIdx.x == 0) {
+    Partial a = g_wave_part[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const Partial& o = g_wave_part[w];
+      if (it.live && it.sampled)
+        acc_merge<true>(a.m, a.s, a.idx, o.m, o.s, o.idx, it.coef);
+      else
+        acc_merge<false>(a.m, a.s, a.idx, o.m, o.s, o.idx, 0.0f);
+    }
+    PartialRec* p = partial_at(P, it.b, it.r, it.c);
+    put_u64(&p->w0, uint64_t(uint32_t(a.idx + 1)) | (uint64_t(__float_as_uint(a.m)) << 32));
+    put_u64(&p->w1, pack2(a.s != 0.0f ? a.s : 1.0f, a.zg));
   }
 }
 
@@ -726,7 +772,7 @@ struct DecideShared {
   unsigned long long rej_mask;
 };
 static_assert(kStageParts == kThreads, "one staged row partial per thread");
-static_assert(int64_t(kMaxVocab) * 4 / kStatBytes * kWaves <= kStageParts, "a row's partials fit one group");
+static_assert(int64_t(kMaxVocab) * 4 / kStatBytes <= kStageParts, "a row's partials fit one group");
 
 struct DrawShared {
   double red[4 * kWaves];
@@ -806,7 +852,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   // outcome, a group of rows at a time (thread i takes partial i of the
   // group); the draft tokens, accept uniforms and temperature are requested
   // alongside the first group.
-  const int pr = P.nch * kWaves;  // partials per row
+  const int pr = P.nch;  // partials per row
   const int rows_per_group = max(1, kStageParts / pr);
   PartialRec* part_b = P.partials + int64_t(b) * R * pr;
   const int ti = min(tid, N - 1);
@@ -873,8 +919,8 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        // Every wave of the item holding the draft token carries its logit.
-        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * pr + (ds.tok[r < N ? r : r - N] / P.chunk) * kWaves].zg : 0.0f;
+        // The item holding the draft token carries its logit.
+        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * pr + ds.tok[r < N ? r : r - N] / P.chunk].zg : 0.0f;
         lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
         amax[r] = idx;
       }
@@ -1406,7 +1452,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
 // fp64 sums: their waves take issue priority.
 __device__ __forceinline__ void critical_path() { __builtin_amdgcn_s_setprio(3); }
 
-// Row-statistics item `idx` of sequence b: every wave stores its partial (a
+// Row-statistics item `idx` of sequence b: stores the item's partial (a
 // placeholder when the item is not read) and is done.
 template <typename T>
 __device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
@@ -1420,10 +1466,10 @@ __device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
     // Loads in flight: folding them takes issue priority over the draw
     // members' fp64 work on the same CU, so items free their slots sooner.
     __builtin_amdgcn_s_setprio(2);
-    q = item_reduce<T>(it, g);
+    q = item_reduce<T>(P, it, g);
   }
   trace(2, 1);
-  partial_write(P, b, it.r, it.c, q);
+  partial_write(P, it, q);
 }
 
 // The decision of sequence b, in a workgroup of its own that follows the
@@ -1628,7 +1674,7 @@ extern "C" __attribute__((visibility("default"))) int specv_debug_trace(uint64_t
 }
 #endif
 
-size_t partial_bytes() { return sizeof(PartialRec) * kWaves; }
+size_t partial_bytes() { return sizeof(PartialRec); }
 size_t seq_bytes() { return sizeof(SeqRec); }
 size_t member_bytes() { return sizeof(MemberRec); }
 
