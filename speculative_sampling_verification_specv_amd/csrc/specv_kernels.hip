@@ -593,86 +593,98 @@ struct Partial {
   int idx;
 };
 
-// Largest of a 16-byte group of logits as stored. bfloat16: both logits of
-// each 32-bit word are moved into place by byte permutes (not the shift and
-// mask the later pass unpacks with, so the compiler does not keep these
-// copies alive until then).
-__device__ __forceinline__ float group_max(const uint4& x, float) {
-  const float a = max3(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z));
-  return max3(a, __uint_as_float(x.w), __uint_as_float(x.w));
-}
-__device__ __forceinline__ float low_bf16(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
-__device__ __forceinline__ float high_bf16(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
-__device__ __forceinline__ float group_max(const uint4& x, uint16_t) {
-  float a = max3(high_bf16(x.x), high_bf16(x.y), high_bf16(x.z));
-  a = max3(a, high_bf16(x.w), low_bf16(x.x));
-  a = max3(a, low_bf16(x.y), low_bf16(x.z));
-  return max3(a, low_bf16(x.w), low_bf16(x.w));
+template <int n>
+__device__ __forceinline__ float max_of(const float (&v)[n]) {
+  static_assert(n == 4 || n == 8, "a 16-byte group of logits");
+  float a = max3(v[0], v[1], v[2]);
+  a = max3(a, v[3], v[n == 4 ? 3 : 4]);
+  if (n == 8) {
+    a = max3(a, v[5], v[6]);
+    a = max3(a, v[7], v[7]);
+  }
+  return a;
 }
 
-// One wave's share of a loaded item, in two passes over the registers:
-// (1) the largest logit of each thread and where it first occurs (its head
-// element, one of its 16-byte groups, or its tail element), then the wave's
-// largest, M; (2) for a sampled row, the sum of 2^(z*c - fl(M*c)) over the
-// wave's logits, so nothing is rescaled on the way (the last use of each
-// group's registers). The first index of M is looked for only by the lanes
-// that hold it, in the group where they first saw it, read again (from the
-// cache). kFull: every group of every thread lies inside
-// the item (nothing to mask). Returns the wave's partial, the same in every
-// lane.
+// Sum of 2^(z*c - k) over a group (a fixed tree).
+template <int n>
+__device__ __forceinline__ float group_exp_sum(const float (&v)[n], float c, float k) {
+  float e[n];
+#pragma unroll
+  for (int q = 0; q < n; ++q) e[q] = fast_exp2(fmaf(v[q], c, -k));
+#pragma unroll
+  for (int w = 1; w < n; w *= 2)
+#pragma unroll
+    for (int q = 0; q + w < n; q += 2 * w) e[q] += e[q + w];
+  return e[0];
+}
+
+// One wave's share of a loaded item, folded group by group as the loads
+// arrive: each thread tracks its largest logit and where it first occurs
+// (its head element, one of its 16-byte groups, or its tail element); for a
+// sampled row it sums 2^(z*c - k) against one wave-wide reference k, set from
+// the first group with a finite logit and raised (rescaling the sums) only
+// when a group's logit would exceed it by 2^64, so the common path has no
+// per-group rescaling. At the end the sums are brought to k = fl(M*c) with M
+// the wave's largest logit. The first index of M is looked for only by the
+// lanes that hold it, in the group where they first saw it, read again (from
+// the cache). kFull: every group of every thread lies inside the item
+// (nothing to mask). Returns the wave's partial, the same in every lane.
 template <typename T, bool kSampled, bool kFull>
 __device__ __forceinline__ Partial wave_fold(const Params& P, const Item& it, ItemRegs& g) {
   constexpr int kVec = Logit<T>::kVec;
   const int tid = threadIdx.x;
+  const float c = it.coef;
   const float hv = tid < it.ea - it.e0 ? Logit<T>::from_bits(g.head) : -INFINITY;
   const float tv = tid < it.e1 - it.et ? Logit<T>::from_bits(g.tail) : -INFINITY;
-  // Pass 1. `where` is -1 for the head, u for group u, kStatVecs for the tail;
-  // a strict '>' keeps the first place (the thread's indices increase in
-  // that order).
+  // `where` is -1 for the head, u for group u, kStatVecs for the tail; a
+  // strict '>' keeps the first place (the thread's indices increase in that
+  // order).
   float tmax = hv;
   int where = -1;
+  float k = -INFINITY;  // the wave's reference (uniform); -inf until a finite logit
+  float s = 0.0f;
+  // Folds one group (values v, maximum gm) into the state.
+  auto fold = [&](const auto& v, float gm, int place, bool in) {
+    const bool up = gm > tmax;
+    where = up ? place : where;
+    tmax = up ? gm : tmax;
+    if (kSampled) {
+      if (__ballot(gm != -INFINITY && fmaf(gm, c, -k) > 64.0f)) {
+        // Rare: raise the reference to the wave's largest logit so far.
+        const float k2 = scaled_max(wave_max(tmax), c);
+        s = s * fast_exp2(k - k2);  // 0 while k is -inf (s is 0 then)
+        k = k2;
+      }
+      if (k != -INFINITY) {
+        const float e = group_exp_sum(v, c, k);
+        s += in ? e : 0.0f;
+      }
+    }
+  };
+  {
+    const float v[1] = {hv};
+    fold(v, hv, -1, true);
+  }
 #pragma unroll
   for (int u = 0; u < kStatVecs; ++u) {
-    float gm = group_max(g.x[u], T());
-    if (!kFull) gm = (tid + u * kThreads < it.nv) ? gm : -INFINITY;
-    const bool up = gm > tmax;
-    where = up ? u : where;
-    tmax = up ? gm : tmax;
+    float v[kVec];
+    Logit<T>::unpack(g.x[u], v);
+    const bool in = kFull || tid + u * kThreads < it.nv;
+    fold(v, in ? max_of(v) : -INFINITY, u, in);
   }
   {
-    const bool up = tv > tmax;
-    where = up ? kStatVecs : where;
-    tmax = up ? tv : tmax;
+    const float v[1] = {tv};
+    fold(v, tv, kStatVecs, true);
   }
   const float mw = wave_max(tmax);
+  if (kSampled) s = (mw == -INFINITY) ? 0.0f : wave_sum(s * fast_exp2(k - scaled_max(mw, c)));
+  // First index of M.
   const bool hold = mw != -INFINITY && tmax == mw;
   int idx = INT_MAX;
   if (hold && where < 0) idx = it.e0 + tid;
   if (hold && where == kStatVecs) idx = it.et + tid;
-  const bool seek = hold && where >= 0 && where < kStatVecs;
-  // Pass 2: two running sums, each group's registers dead once summed.
-  float s = 0.0f;
-  if (kSampled && mw != -INFINITY) {
-    const float c = it.coef;
-    const float k = scaled_max(mw, c);
-    float acc0 = fast_exp2(fmaf(hv, c, -k)), acc1 = fast_exp2(fmaf(tv, c, -k));
-#pragma unroll
-    for (int u = 0; u < kStatVecs; ++u) {
-      float v[kVec];
-      Logit<T>::unpack(g.x[u], v);
-      const bool in = kFull || tid + u * kThreads < it.nv;
-#pragma unroll
-      for (int q = 0; q < kVec; q += 2) {
-        const float e0 = fast_exp2(fmaf(v[q], c, -k)), e1 = fast_exp2(fmaf(v[q + 1], c, -k));
-        acc0 += in ? e0 : 0.0f;
-        acc1 += in ? e1 : 0.0f;
-      }
-    }
-    s = wave_sum(acc0 + acc1);
-  }
-  uint4 again = make_uint4(0u, 0u, 0u, 0u);
-  if (seek) again = reinterpret_cast<const uint4*>(item_row<T>(P, it) + it.ea)[tid + where * kThreads];
-  if (seek) {
+  if (hold && where >= 0 && where < kStatVecs) {
+    const uint4 again = reinterpret_cast<const uint4*>(item_row<T>(P, it) + it.ea)[tid + where * kThreads];
     float v[kVec];
     Logit<T>::unpack(again, v);
     int first = kVec - 1;
