@@ -1368,7 +1368,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   const bool mine = lane < nm;
   const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
   if (tid < 64) {
-    // Normalisers (a fixed butterfly over the members), then member lane's
+    // Normalisers (fixed-order DPP sums over the members), then member lane's
     // sub-chunk weights: A/Zt - B/Zd of the certain tokens plus the listed
     // uncertain ones in token order.
     double zt = mine ? bits_to_double(r[MemberRec::kZt]) : 0.0;
