@@ -650,7 +650,10 @@ __device__ __forceinline__ Partial wave_fold(const Params& P, const Item& it, It
   // order).
   float tmax = hv;
   int where = -1;
-  float k = -INFINITY;  // the wave's reference (uniform); -inf until a finite logit
+  // The wave's reference (uniform). It starts finite and below every scaled
+  // logit, so the first finite logit raises it, -inf logits add exactly 0
+  // before that, and neither check needs a test of its own.
+  float k = -FLT_MAX;
   float s = 0.0f;
   // Folds one group (values v, maximum gm) into the state.
   auto fold = [&](const auto& v, float gm, int place, bool in) {
@@ -658,16 +661,14 @@ __device__ __forceinline__ Partial wave_fold(const Params& P, const Item& it, It
     where = up ? place : where;
     tmax = up ? gm : tmax;
     if (kSampled) {
-      if (__ballot(gm != -INFINITY && fmaf(gm, c, -k) > 64.0f)) {
+      if (__ballot(fmaf(gm, c, -k) > 64.0f)) {
         // Rare: raise the reference to the wave's largest logit so far.
         const float k2 = scaled_max(wave_max(tmax), c);
-        s = s * fast_exp2(k - k2);  // 0 while k is -inf (s is 0 then)
+        s = s * fast_exp2(k - k2);  // s is 0 until the first raise
         k = k2;
       }
-      if (k != -INFINITY) {
-        const float e = group_exp_sum(v, c, k);
-        s += in ? e : 0.0f;
-      }
+      const float e = group_exp_sum(v, c, k);
+      s += in ? e : 0.0f;
     }
   };
   {
