@@ -1,21 +1,23 @@
-"""Print the table of 2^(j/64), j = 0..63, correctly rounded to fp64, as C++.
+"""Print the table of 2^(j/256), j = 0..255, correctly rounded to fp64, as C++.
 
 The values are computed with 60 significant decimal digits and rounded once
 (Python's float() of a decimal string rounds correctly), so each entry is
-within half an ulp of 2^(j/64). The output is pasted into specv_math.h.
+within half an ulp of 2^(j/256). The output is pasted into specv_math.h.
 """
 
 from decimal import Decimal, getcontext
 
+N = 256  # entries: 2^(j/N)
+
 
 def table():
     getcontext().prec = 60
-    return [float(str(Decimal(2) ** (Decimal(j) / Decimal(64)))) for j in range(64)]
+    return [float(str(Decimal(2) ** (Decimal(j) / Decimal(N)))) for j in range(N)]
 
 
 if __name__ == "__main__":
     vals = table()
-    print("constexpr double kExp2Table[64] = {")
-    for i in range(0, 64, 4):
+    print(f"constexpr double kExp2Table[{N}] = {{")
+    for i in range(0, N, 4):
         print("    " + ", ".join(v.hex() for v in vals[i:i + 4]) + ",")
     print("};")

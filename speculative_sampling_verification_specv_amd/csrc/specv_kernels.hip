@@ -796,9 +796,11 @@ struct DecideShared {
 static_assert(kStageParts == kThreads, "one staged row partial per thread");
 static_assert(int64_t(kMaxVocab) * 4 / kStatBytes <= kStageParts, "a row's partials fit one group");
 
+static_assert(sizeof(kExp2Table) == kThreads * sizeof(double), "the exp table is filled one entry per thread");
+
 struct DrawShared {
   double red[4 * kWaves];
-  double exp2_tab[64];  // kExp2Table, for exp_nonpos_tab (members and the finisher)
+  double exp2_tab[kThreads];  // kExp2Table, for exp_nonpos_tab (members and the finisher)
   union {
     struct {
       double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
@@ -1139,12 +1141,12 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   const int e = (c * kThreads + tid) * kPer;
   // The exp table first (a cached read that arrives before the rows), then
   // the rows.
-  const double tab_v = kExp2Table[tid & 63];
+  const double tab_v = kExp2Table[tid];  // one entry per thread
   uint4 xt[kG], xd[kG];
   load_packed(d.trow, e, P.vocab, P.vec_ok != 0, xt);
   if (residual) load_packed(d.drow, e, P.vocab, P.vec_ok != 0, xd);
   trace(0, 1);
-  if (tid < 64) ws.exp2_tab[tid] = tab_v;
+  ws.exp2_tab[tid] = tab_v;
   barrier();
   const double* tab = ws.exp2_tab;
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;

@@ -2,7 +2,7 @@
 // table form specv::exp_nonpos_tab) against long-double exp: prints, for each,
 // the largest relative error over a dense grid of [-708, 0], a few special
 // values and the error in the subnormal range; and the table's largest error
-// in ulps against long-double 2^(j/64).
+// in ulps against long-double 2^(j/256).
 #include <math.h>
 #include <stdio.h>
 
@@ -40,8 +40,9 @@ int main() {
   report("", [](double a) { return specv::exp_nonpos(a); });
   report("tab_", [](double a) { return specv::exp_nonpos_tab(a, specv::kExp2Table); });
   double worst_ulp = 0.0;
-  for (int j = 0; j < 64; ++j) {
-    const long double ref = powl(2.0L, static_cast<long double>(j) / 64.0L);
+  constexpr int n = sizeof(specv::kExp2Table) / sizeof(specv::kExp2Table[0]);
+  for (int j = 0; j < n; ++j) {
+    const long double ref = powl(2.0L, static_cast<long double>(j) / n);
     const double v = specv::kExp2Table[j];
     const double ulp = nextafter(v, 2.0 * v) - v;
     worst_ulp = fmax(worst_ulp, static_cast<double>(fabsl(static_cast<long double>(v) - ref)) / ulp);
