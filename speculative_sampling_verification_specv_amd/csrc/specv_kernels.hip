@@ -1156,6 +1156,7 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     const float inv_tf = float(d.inv_t);
     const float dmf = float(d.nmt - d.nmd);  // -(mt - md)/T
     const float hi = float(s.log_rho + kSignBand), lo = float(s.log_rho - kSignBand);
+    bool any_band = false;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const float ztk = Logit<T>::element(xt, k);
@@ -1172,7 +1173,16 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
       const double pos_d = pos ? 1.0 : 0.0;  // adds et and ed exactly, or nothing
       sa = fma(pos_d, et, sa);
       sb = fma(pos_d, ed, sb);
-      unc |= band ? (1u << k) : 0u;
+      any_band = any_band || band;
+    }
+    // Uncertain tokens are rare (a wave in tens holds one): their bits are
+    // taken in a second pass, with the same arithmetic, only where needed.
+    if (__ballot(any_band)) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const float lr = fmaf(Logit<T>::element(xt, k) - Logit<T>::element(xd, k), inv_tf, dmf);
+        unc |= (!(lr > hi) && lr >= lo) ? (1u << k) : 0u;
+      }
     }
   } else {
 #pragma unroll
