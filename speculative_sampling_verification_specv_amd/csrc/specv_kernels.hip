@@ -1185,8 +1185,17 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
       }
     }
   } else {
+    // A copy the compiler cannot see through: otherwise it computes the
+    // target row's kPer fp64 exp arguments once above both branches and
+    // keeps them all live (spills in the fp32 build).
+    uint4 yt[kG];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) st += exp_nonpos_tab(exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t), tab);
+    for (int u = 0; u < kG; ++u) {
+      yt[u] = xt[u];
+      asm volatile("" : "+v"(yt[u].x), "+v"(yt[u].y), "+v"(yt[u].z), "+v"(yt[u].w));
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) st += exp_nonpos_tab(exp_arg(Logit<T>::element(yt, k), d.nmt, d.inv_t), tab);
     sa = st;
   }
   trace(0, 2);
