@@ -50,11 +50,11 @@ extern "C" {
 /* Opaque handle; created by specv_create, released by specv_destroy. */
 typedef struct specv_ctx* specv_handle;
 
-/* Storage type of the logits. */
-enum specv_dtype {
+/* Storage type of the logits (passed as an int-sized enum). */
+typedef enum specv_dtype {
   SPECV_F32 = 0,  /* IEEE float32 */
   SPECV_BF16 = 1, /* bfloat16 (upper half of a float32) */
-};
+} specv_dtype;
 
 /* Return codes. Host-detectable errors return before anything is enqueued. */
 enum specv_status {
@@ -76,14 +76,18 @@ enum specv_status {
  * Create a handle for calls with batch <= max_batch, 1 <= n_draft <= max_draft,
  * vocabulary size `vocab` (V >= 1) and logits stored as `dtype`, on HIP device
  * `device`. Allocates the scratch workspace on that device (size grows with
- * max_batch * (2*max_draft+1) * ceil(V*dtype_bytes/32768) row partials plus
- * max_batch * ceil(V*dtype_bytes/16384) draw records). On success *out is set and
+ * max_batch * (2*max_draft+1) * ceil(V*dtype_bytes/65536) row partials plus
+ * max_batch * ceil(V/4096) draw records). On success *out is set and
  * SPECV_OK returned; on failure *out is NULL.
+ * If the environment variable SPECV_DEBUG is set (and not "0") when the handle
+ * is created, its calls also check on the device that every uniform lies in
+ * [0, 1): a sequence with one outside gets the invalid-input sentinel (-1).
  * Errors: SPECV_EINVAL (out NULL, max_batch < 1, max_draft outside
  * [1, SPECV_MAX_DRAFT], vocab < 1 or > SPECV_MAX_VOCAB, unknown dtype, bad device),
  * SPECV_ENOMEM, SPECV_EHIP.
  */
-SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int dtype, int device);
+SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, specv_dtype dtype,
+                           int device);
 
 /*
  * Verify one batch. All pointers are device pointers; layouts are row-major
@@ -103,9 +107,16 @@ SPECV_API int specv_create(specv_handle* out, int max_batch, int max_draft, int 
  * waiting; outputs are valid once the stream reaches this point.
  * Per-sequence input faults that only the device can see — a draft token
  * outside [0, V), a temperature that is negative, NaN, infinite or positive
- * below 2^-60 — make that
+ * below 2^-60 (and, with SPECV_DEBUG, a uniform outside [0, 1)) — make that
  * sequence's out_n_accepted = -1 and all its out_tokens = -1; other sequences
  * are unaffected.
+ * The workgroups of one call hand work to each other; every wait for another
+ * workgroup is bounded by the handle's wait limit (specv_set_wait_limit).
+ * A sequence whose wait gave up — not expected: it means the device did not
+ * run a workgroup of the call within the limit — gets out_n_accepted = -2,
+ * and its out_tokens are then unspecified (each is -2 or a value the call
+ * was writing). Nothing is left behind that a later call could take for its
+ * own (every hand-off word carries the number of the call that wrote it).
  * batch == 0 is a no-op returning SPECV_OK.
  * Errors (nothing enqueued): SPECV_EINVAL (null handle or pointer, batch < 0
  * or > max_batch, n_draft < 1 or > max_draft), SPECV_EALIGN (logits not
@@ -131,6 +142,16 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
  * verify yet), SPECV_EHIP.
  */
 SPECV_API int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream);
+
+/*
+ * Bound of every wait between the workgroups of one call, in microseconds
+ * (0 <= microseconds <= 3.6e9; default 100000). Applies to later calls on the
+ * handle. A wait normally lasts microseconds. 0 makes every wait give up at
+ * once, whether or not what it waits for is there, so every sequence of the
+ * call reports -2 (or -1 if its inputs are invalid): a way to exercise that
+ * path. Errors: SPECV_EINVAL (null handle, value out of range).
+ */
+SPECV_API int specv_set_wait_limit(specv_handle h, int64_t microseconds);
 
 /*
  * Kernel timing (diagnostic). With enable != 0, every later specv_verify on

@@ -40,13 +40,29 @@ Readings where the pages are silent (each also listed in the design notes):
   back to q_j.
 * One accept uniform per position (u_i) and one sample uniform per sequence are
   passed in; the accept test is strict.
-* The temperature domain is 0 or a finite T >= 2^-60; other values mark the
-  sequence invalid (n_accepted = -1, all tokens -1), as do draft tokens outside
-  [0, V).
+* The temperature domain is T = 0 (greedy) or any finite T > 0; a negative,
+  NaN or infinite T marks the sequence invalid (n_accepted = -1, all tokens
+  -1), as do draft tokens outside [0, V). With float32 logits (|z| < 2^128)
+  and a float32 T >= 2^-149, z / T stays finite in fp64, so every such T is
+  computed exactly as written.
 * Decision margins, the distance of a float decision from its boundary, are
   recorded so that a parity check can tell rounding ties from real errors:
-  |u_i - q_i(d_i)/p_i(d_i)| for each accept test made, and
-  min(u*S - C_{k-1}, C_k - u*S) (probability-mass units) for the draw.
+  |u_i - q_i(d_i)/p_i(d_i)| for each accept test made (decision_margin), and
+  the distance from u*S to the nearer edge of the chosen token's CDF interval
+  [C_{k-1}, C_k), in probability-mass units (cdf_margin).
+
+Beyond the verification itself (the steps around it on the pages):
+
+* sample_row: the draft-side draw of a token from softmax(z / T) (lesson,
+  "핵심 알고리즘(Core algorithm)" step 2 and Step 3's draft loop), by the same
+  inverse CDF; T = 0 takes the first argmax.
+* acceptance_rates: the per-position acceptance probability
+  alpha_i = sum_x min(p_i(x), q_i(x)) and the expected tokens per verifier
+  pass tau = sum_{k=0..N} prod_{i<k} alpha_i (lesson, "속도 향상을 결정하는 것";
+  guide, "몇 글자를 미리 쓰게 할까요").
+* kv_commit: the verifier's KV entries of the drafts, written to a scratch
+  area, are committed to the cache only up to the accepted prefix (lesson,
+  "KV 캐시 처리(KV cache dance)" and exercise 4).
 """
 
 from __future__ import annotations
@@ -58,16 +74,22 @@ import numpy as np
 
 __all__ = [
     "SequenceResult",
+    "SampleResult",
     "tempered_log_normaliser",
+    "tempered_probabilities",
     "first_argmax",
     "log_prob_of",
     "acceptance_ratio",
     "residual_weights",
     "bonus_weights",
     "inverse_cdf",
+    "decision_margin",
+    "cdf_margin",
     "verify_sequence",
-    "verify_batch",
     "verify_trials",
+    "sample_row",
+    "acceptance_rates",
+    "kv_commit",
 ]
 
 
@@ -90,6 +112,13 @@ def tempered_log_normaliser(z_rows: np.ndarray, T: float) -> np.ndarray:
     return (m + np.log(np.sum(np.exp(x - m), axis=-1, keepdims=True)))[..., 0]
 
 
+def tempered_probabilities(z_rows: np.ndarray, T: float) -> np.ndarray:
+    """softmax(z / T) of each row: exp(z / T - L) with L the row's log-normaliser."""
+    z = np.asarray(z_rows, dtype=np.float64)
+    L = tempered_log_normaliser(z, T)
+    return np.exp(z / T - L[..., None])
+
+
 def first_argmax(row: np.ndarray) -> int:
     """Index of the largest entry; the lowest index wins a tie (numpy's argmax
     returns the first occurrence of the maximum)."""
@@ -102,10 +131,12 @@ def log_prob_of(z_row: np.ndarray, token: int, T: float, L: float) -> float:
 
 
 def acceptance_ratio(log_q: float, log_p: float) -> float:
-    """q(d) / p(d); infinite when the draft gave d zero probability."""
+    """q(d) / p(d); infinite when the draft gave d zero probability, or when the
+    ratio is beyond the fp64 range (then it exceeds every uniform)."""
     if log_p == -math.inf:
         return math.inf
-    return math.exp(log_q - log_p)
+    x = log_q - log_p
+    return math.exp(x) if x < 709.0 else math.inf
 
 
 def residual_weights(q: np.ndarray, p: np.ndarray) -> np.ndarray:
@@ -118,13 +149,20 @@ def bonus_weights(q: np.ndarray) -> np.ndarray:
     return q
 
 
+def cdf_margin(target: float, lower: float, upper: float) -> float:
+    """Distance of ``target`` = u*S to the nearer edge of the chosen token's
+    interval [lower, upper) = [C_{k-1}, C_k): how far the draw is from picking
+    a neighbour."""
+    return min(abs(target - lower), abs(upper - target))
+
+
 def inverse_cdf(w: np.ndarray, u: float):
     """Draw a token from weights ``w`` with uniform ``u`` by an inverse CDF.
 
     Returns (token, margin, S): the smallest k with C_k > u*S, where
     C_k = sum_{x<=k} w_x in ascending token order and S = C_{V-1}; if rounding
-    leaves none, the last k with w_k > 0. ``margin`` is the distance of u*S to
-    the nearer edge of [C_{k-1}, C_k).
+    leaves none, the last k with w_k > 0. ``margin`` is cdf_margin of u*S in
+    [C_{k-1}, C_k).
     """
     C = np.cumsum(np.asarray(w, dtype=np.float64))
     S = float(C[-1])
@@ -135,18 +173,21 @@ def inverse_cdf(w: np.ndarray, u: float):
     else:
         k = int(np.nonzero(w > 0)[0][-1])
     lower = float(C[k - 1]) if k > 0 else 0.0
-    margin = min(target - lower, float(C[k]) - target)
-    return k, margin, S
+    return k, cdf_margin(target, lower, float(C[k])), S
 
 
-# Temperatures the verification contract accepts: 0 (greedy) or a finite
-# T >= 2^-60. Anything else (negative, NaN, infinite, or positive below 2^-60)
-# marks the sequence invalid.
-MIN_TEMPERATURE = 2.0 ** -60
+def decision_margin(u: float, ratio: float) -> float:
+    """Distance of an accept test u < ratio from its boundary: |u - ratio|
+    (infinite when the ratio is, i.e. the draft gave the token zero mass)."""
+    return abs(u - ratio)
+
+
+def _valid_temperature(T: float) -> bool:
+    return math.isfinite(T) and T >= 0.0
 
 
 def _valid(T: float, tokens: np.ndarray, V: int) -> bool:
-    if not math.isfinite(T) or T < 0.0 or 0.0 < T < MIN_TEMPERATURE:
+    if not _valid_temperature(T):
         return False
     return bool(np.all((tokens >= 0) & (tokens < V)))
 
@@ -181,7 +222,7 @@ def _verify_sampled(draft_z, target_z, tokens, ua, us, T, Ld, Lt) -> SequenceRes
         log_p = log_prob_of(draft_z[i], d, T, Ld[i])
         ratio = acceptance_ratio(log_q, log_p)
         u = float(ua[i])
-        margins.append(abs(u - ratio))
+        margins.append(decision_margin(u, ratio))
         if not u < ratio:
             j = i
             break
@@ -220,16 +261,6 @@ def verify_sequence(draft_z, target_z, tokens, accept_u, sample_u, T) -> Sequenc
     return _verify_sampled(draft_z, target_z, tokens, accept_u, sample_u, T, Ld, Lt)
 
 
-def verify_batch(draft_z, target_z, tokens, accept_u, sample_u, temperature, seqs=None) -> list:
-    """Verify sequences ``seqs`` (default: all) of a batch; float64 inputs as in verify_sequence."""
-    B = tokens.shape[0]
-    order = range(B) if seqs is None else seqs
-    return [
-        verify_sequence(draft_z[b], target_z[b], tokens[b], accept_u[b], sample_u[b], temperature[b])
-        for b in order
-    ]
-
-
 def verify_trials(draft_z, target_z, tokens, accept_u, sample_u, T) -> list:
     """Many sequences that share one set of logits (Monte-Carlo trials).
 
@@ -253,3 +284,108 @@ def verify_trials(draft_z, target_z, tokens, accept_u, sample_u, T) -> list:
         else:
             out.append(_verify_sampled(draft_z, target_z, tokens[n], accept_u[n], sample_u[n], T, Ld, Lt))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Around the verification: the draft-side draw, acceptance telemetry and the
+# KV-cache commit.
+
+
+@dataclass
+class SampleResult:
+    """One drawn token plus the oracle's margin (None at T = 0 or when invalid)."""
+
+    token: int  # -1 marks an invalid temperature
+    margin: float | None = None
+
+
+def sample_row(z_row, T: float, u: float) -> SampleResult:
+    """Draw a token from softmax(z / T) with uniform u (the draft model's step).
+
+    The lesson's draft loop draws each draft token from the draft model's
+    tempered distribution; the draw here is the same inverse CDF as every
+    other draw: the token is the smallest k with C_k > u * S over
+    q = softmax(z / T) in ascending token order. T = 0 takes the first argmax
+    (the low-temperature limit); a negative, NaN or infinite T gives -1.
+    """
+    z = np.asarray(z_row, dtype=np.float64)
+    T = float(T)
+    if not _valid_temperature(T):
+        return SampleResult(-1)
+    if T == 0.0:
+        return SampleResult(first_argmax(z))
+    q = tempered_probabilities(z, T)
+    k, margin, _ = inverse_cdf(q, float(u))
+    return SampleResult(k, margin)
+
+
+def acceptance_rates(draft_z, target_z, tokens, T: float):
+    """Per-position acceptance probability alpha_i and expected tokens per pass tau.
+
+    alpha_i = sum_x min(p_i(x), q_i(x)): the probability that draft i is
+    accepted given that position i is reached, when the draft token is drawn
+    from p_i (the acceptance rule accepts x with probability min(1, q/p)).
+    tau = sum_{k=0..N} prod_{i<k} alpha_i is the expected number of tokens one
+    verifier pass emits: position k is reached with probability
+    prod_{i<k} alpha_i and every reached position emits one token (the last
+    one the correction or the bonus). With alpha constant this is
+    (1 - alpha^(N+1)) / (1 - alpha), the lesson's closed form.
+    At T = 0 both distributions are point masses (the draft's greedy pick d_i
+    and the verifier's first argmax g_i), so alpha_i = 1 if d_i = g_i else 0.
+    Returns (alpha [N] list, tau); NaNs when the sequence is invalid.
+    """
+    draft_z = np.asarray(draft_z, dtype=np.float64)
+    target_z = np.asarray(target_z, dtype=np.float64)
+    tokens = np.asarray(tokens)
+    N, V = target_z.shape[0] - 1, target_z.shape[1]
+    T = float(T)
+    if not _valid(T, tokens, V):
+        return [math.nan] * N, math.nan
+    if T == 0.0:
+        alpha = [1.0 if int(tokens[i]) == first_argmax(target_z[i]) else 0.0 for i in range(N)]
+    else:
+        p = tempered_probabilities(draft_z, T)
+        q = tempered_probabilities(target_z[:N], T)
+        alpha = [float(np.sum(np.minimum(p[i], q[i]))) for i in range(N)]
+    tau = 0.0
+    reach = 1.0
+    for k in range(N + 1):
+        tau += reach
+        if k < N:
+            reach *= alpha[k]
+    return alpha, tau
+
+
+def kv_commit(cache, cache_len, scratch, n_accepted):
+    """Commit the accepted drafts' KV entries from a scratch area into the cache.
+
+    The verifier's pass over N drafts writes one KV entry per draft into a
+    scratch area; once n = n_accepted of them are accepted, entries 0..n-1 are
+    appended to the sequence's cache at its current length and the length
+    grows by n, so the next pass reads the prefix plus the accepted drafts and
+    nothing of the rejected ones (lesson, "KV 캐시 처리(KV cache dance)";
+    exercise 4 checks exactly this).
+
+    cache [P, B, L, E] and scratch [P, B, N, E] are byte arrays (P planes, e.g.
+    keys and values of every layer; E bytes per entry); cache_len and
+    n_accepted [B]. A sequence whose n_accepted is outside [0, N] (an invalid
+    verification) or whose entries would not fit (len + n > L, or len < 0) is
+    left as it is and reports length -1. Returns (new cache, new lengths);
+    the inputs are not modified.
+    """
+    out = np.array(cache, copy=True)
+    scratch = np.asarray(scratch)
+    P, B, L, E = out.shape
+    N = scratch.shape[2]
+    new_len = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        n = int(n_accepted[b])
+        start = int(cache_len[b])
+        if n < 0 or n > N or start < 0 or start + n > L:
+            new_len[b] = -1
+            continue
+        for p in range(P):
+            for t in range(n):
+                out[p, b, start + t, :] = scratch[p, b, t, :]
+        new_len[b] = start + n
+    return out, new_len

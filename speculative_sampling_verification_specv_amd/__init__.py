@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     specv_last_timings,
     specv_row_stats,
     specv_set_timing,
+    specv_set_wait_limit,
     specv_stage_name,
     specv_strerror,
     specv_verify,

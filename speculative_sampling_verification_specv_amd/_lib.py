@@ -33,6 +33,7 @@ _SIGNATURES = {
     "specv_destroy": (None, [ctypes.c_void_p]),
     "specv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "specv_set_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
+    "specv_set_wait_limit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
     "specv_last_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int)]),
     "specv_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -108,6 +109,10 @@ def specv_verify(handle: int, draft_logits, target_logits, draft_tokens, accept_
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:
     _check(load_library().specv_row_stats(handle, _ptr(out_lse), _ptr(out_argmax),
                                           _stream_ptr(stream, out_lse.device)), "specv_row_stats")
+
+
+def specv_set_wait_limit(handle: int, microseconds: int) -> None:
+    _check(load_library().specv_set_wait_limit(handle, int(microseconds)), "specv_set_wait_limit")
 
 
 def specv_set_timing(handle: int, enable: bool) -> None:
@@ -228,6 +233,9 @@ class Verifier:
 
     def set_timing(self, enable: bool) -> None:
         specv_set_timing(self.handle, enable)
+
+    def set_wait_limit(self, microseconds: int) -> None:
+        specv_set_wait_limit(self.handle, microseconds)
 
     def last_timings(self) -> dict:
         return specv_last_timings(self.handle)

@@ -25,6 +25,10 @@ struct specv_ctx {
   specv::Workspace ws;
   int last_batch;        // -1 until a verify succeeds
   int last_n_draft;
+  uint32_t next_tag;     // number of the next call (1, 2, ...; 0 is skipped)
+  uint32_t debug;        // SPECV_DEBUG was set at create: check the uniforms on the device
+  uint64_t wait_ticks;   // bound of every wait between workgroups, in wall-clock ticks
+  int clock_khz;         // the device's wall-clock rate
   bool timing;                               // record stage events on every verify
   bool timed_call;                           // the last verify recorded them
   int timed_stages;                          // stages the last timed verify launched
@@ -54,6 +58,11 @@ class DeviceGuard {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Default bound of a wait between the workgroups of one launch (a normal
+// wait lasts microseconds; the bound only matters if the device fails to run
+// a workgroup that another waits for).
+constexpr int64_t kDefaultWaitUs = 100000;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
@@ -72,7 +81,7 @@ const char* specv_strerror(int code) {
   }
 }
 
-int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int dtype, int device) {
+int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, specv_dtype dtype, int device) {
   if (out == nullptr) return SPECV_EINVAL;
   *out = nullptr;
   if (max_batch < 1 || max_draft < 1 || max_draft > SPECV_MAX_DRAFT) return SPECV_EINVAL;
@@ -136,6 +145,18 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, int
   }
   h->last_batch = -1;
   h->last_n_draft = 0;
+  h->next_tag = 1;
+  {
+    const char* dbg = getenv("SPECV_DEBUG");
+    h->debug = (dbg != nullptr && dbg[0] != '\0' && strcmp(dbg, "0") != 0) ? 1u : 0u;
+  }
+  if (hipDeviceGetAttribute(&h->clock_khz, hipDeviceAttributeWallClockRate, device) != hipSuccess ||
+      h->clock_khz <= 0) {
+    (void)hipFree(h->mem);
+    delete h;
+    return SPECV_EHIP;
+  }
+  h->wait_ticks = uint64_t(kDefaultWaitUs) * uint64_t(h->clock_khz) / 1000u;
   h->timing = false;
   h->timed_call = false;
   h->timed_stages = 0;
@@ -175,8 +196,12 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
+  a.tag = h->next_tag;
+  a.debug = h->debug;
+  a.wait_ticks = h->wait_ticks;
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, h->timing ? h->events : nullptr, &stages) != hipSuccess) return SPECV_EHIP;
+  h->next_tag = h->next_tag == UINT32_MAX ? 1u : h->next_tag + 1u;
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;
@@ -196,6 +221,12 @@ int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* s
     return SPECV_EHIP;
   if (hipMemcpyAsync(out_argmax, h->ws.row_argmax, n * sizeof(int), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return SPECV_EHIP;
+  return SPECV_OK;
+}
+
+int specv_set_wait_limit(specv_handle h, int64_t microseconds) {
+  if (h == nullptr || microseconds < 0 || microseconds > int64_t(3600) * 1000000) return SPECV_EINVAL;
+  h->wait_ticks = uint64_t(microseconds) * uint64_t(h->clock_khz) / 1000u;
   return SPECV_OK;
 }
 

@@ -30,7 +30,9 @@ inline int stat_chunk_elems(int dtype) { return kStatBytes / (dtype == 0 ? 4 : 2
 
 constexpr int kCounterStride = 64;
 
-enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+// What a sampled sequence's draw does: a residual or bonus draw, nothing because an
+// input is invalid (-1 outputs), or nothing because a wait gave up (-2 outputs).
+enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2, kModeInvalid = 3, kModeFailed = 4 };
 
 // Device workspace: records one launch writes and the next reads.
 struct Workspace {
@@ -63,6 +65,9 @@ struct VerifyArgs {
   const float* temperature;
   int* out_tokens;
   int* out_n;
+  uint32_t tag;         // the call's number (never 0), carried by every hand-off word
+  uint32_t debug;       // also check that the uniforms lie in [0, 1)
+  uint64_t wait_ticks;  // bound of every wait between workgroups, in wall-clock ticks
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

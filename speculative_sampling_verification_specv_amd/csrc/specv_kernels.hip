@@ -398,30 +398,36 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
   return uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
 }
 
-// Records written by one workgroup and read by another (or the next launch).
-// Row statistics of one item as two words, neither of them zero once written: w0 = (first argmax + 1) | max logit << 32, w1 = s | zg << 32
-// (s = sum of 2^(z*c - fl(max*c)), >= 1/2 when max is finite; stored as 1
-// when it is 0, i.e. for a greedy or skipped item, or an all -inf one, where no
-// merge uses it; zg = the logit at the row's draft token if the item holds it,
-// else 0). The decision zeroes both after reading them, so a zero word means
-// "not written yet in this call", and no word is read against another.
+// Records written by one workgroup and read by another within a launch. Every
+// word is a 32-bit payload in its low half and the call's tag in its high half
+// (the host numbers its calls 1, 2, ...; never 0), so a reader takes each word
+// on its own once its tag is the current call's, needs no order between the
+// words of a record, and never takes a word that an earlier call left behind.
+// Readers also zero what they take (so words read zero at every call's start,
+// also when a captured launch is replayed).
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) { return (uint64_t(tag) << 32) | payload; }
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return uint32_t(w >> 32) == tag; }
+
+// Row statistics of one item: the largest logit m, s = sum of
+// 2^(z*c - fl(m*c)) (>= 1/2 when m is finite; 1 for a greedy, skipped or
+// all -inf item, where no merge uses it), the first index of m plus one, and
+// the logit at the row's draft token if the item holds it (else 0).
 struct PartialRec {
-  uint64_t w0, w1;
+  uint64_t m, s, idx, zg;
 };
-// One sequence's decision, published for its draw members as three words that
-// each carry kPublished, so a reader takes each word once it is set and needs
-// no order between them; all three are zero between calls.
+// One sequence's decision, published for its draw members.
 struct SeqRec {
-  uint64_t w0;  // kPublished | j << 40 | mode << 32 | maximum of target row j (low half)
-  uint64_t w1;  // kPublished | temperature << 32 | maximum of draft row j (low half)
-  uint64_t w2;  // kPublished | log(Zt/Zd) of row j, from the fp32 row sums, as fp32 (low half)
+  uint64_t jm;      // j | mode << 8
+  uint64_t mt;      // largest logit of target row j
+  uint64_t md;      // largest logit of draft row j (residual draws)
+  uint64_t logrho;  // log(Zt/Zd) of row j from the fp32 row sums, as fp32 (residual draws)
 };
-constexpr uint64_t kPublished = uint64_t(1) << 63;
 // One draw member's fp64 sums as 64-bit words (written once each, read by
 // the finisher after the member has reported):
 struct MemberRec {
-  static constexpr int kZt = 0, kZd = 1;  // sums of the target and draft exps
-  static constexpr int kA = 2;            // + k: sub-chunk k's sum of et over certainly positive tokens
+  static constexpr int kStatus = 0;       // the call's tag << 32 | 1 if the member saw the decision
+  static constexpr int kZt = 1, kZd = 2;  // sums of the target and draft exps
+  static constexpr int kA = 3;            // + k: sub-chunk k's sum of et over certainly positive tokens
   static constexpr int kB = kA + kSubs;   // + k: the same sum of ed
   static constexpr int kNUnc = kB + kSubs;  // uncertain-sign tokens (kUncMax + 1: more than listed)
   static constexpr int kPos = kNUnc + 1;    // + i: their positions, ascending
@@ -457,8 +463,11 @@ struct Params {
   int nch;    // row-statistics chunks per row
   int chunk;  // logits per row-statistics chunk
   int nm;     // draw members per sequence
-  int vec_ok;  // rows start 16-byte aligned
+  uint32_t flags;       // kVecOk: rows start 16-byte aligned; kDebug: check that the uniforms lie in [0, 1)
+  uint32_t tag;         // this call's number (never 0): the high half of every hand-off word
+  uint32_t wait_ticks;  // bound of every wait, in ticks of the 100 MHz wall clock
 };
+constexpr uint32_t kVecOk = 1, kDebug = 2;
 
 // Partial of item (row r, chunk c) of sequence b.
 __device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r, int c) {
@@ -733,8 +742,10 @@ __device__ __forceinline__ void partial_write(const Params& P, const Item& it, c
         acc_merge<false>(a.m, a.s, a.idx, o.m, o.s, o.idx, 0.0f);
     }
     PartialRec* p = partial_at(P, it.b, it.r, it.c);
-    put_u64(&p->w0, uint64_t(uint32_t(a.idx + 1)) | (uint64_t(__float_as_uint(a.m)) << 32));
-    put_u64(&p->w1, pack2(a.s != 0.0f ? a.s : 1.0f, a.zg));
+    put_u64(&p->m, tagged(P.tag, __float_as_uint(a.m)));
+    put_u64(&p->s, tagged(P.tag, __float_as_uint(a.s != 0.0f ? a.s : 1.0f)));
+    put_u64(&p->idx, tagged(P.tag, uint32_t(a.idx + 1)));
+    put_u64(&p->zg, tagged(P.tag, __float_as_uint(a.zg)));
   }
 }
 
@@ -766,15 +777,13 @@ __device__ __forceinline__ bool last_arrival(int* count, int total) {
 
 // Publishes sequence b's decision for its draw members. Only sampled
 // sequences (T > 0) have draw members waiting; the last of them zeroes the
-// record again, so it reads zero at every call's start (also when a captured
-// launch is replayed).
-__device__ __forceinline__ void publish(const Params& P, int b, int mode, int j, float mt, float md,
-                                        double log_rho, float temp) {
+// record again.
+__device__ __forceinline__ void publish(const Params& P, int b, int mode, int j, float mt, float md, double log_rho) {
   SeqRec* q = P.seq + b;
-  put_u64(&q->w0, kPublished | (uint64_t(uint32_t(j)) << 40) | (uint64_t(uint32_t(mode)) << 32) | __float_as_uint(mt));
-  // A sampled sequence's temperature is positive: 31 bits hold it.
-  put_u64(&q->w1, kPublished | (uint64_t(__float_as_uint(temp)) << 32) | __float_as_uint(md));
-  put_u64(&q->w2, kPublished | __float_as_uint(float(log_rho)));
+  put_u64(&q->jm, tagged(P.tag, uint32_t(j) | (uint32_t(mode) << 8)));
+  put_u64(&q->mt, tagged(P.tag, __float_as_uint(mt)));
+  put_u64(&q->md, tagged(P.tag, __float_as_uint(md)));
+  put_u64(&q->logrho, tagged(P.tag, __float_as_uint(float(log_rho))));
 }
 
 // Whether sequence b's draw members wait for its decision: a positive valid
@@ -782,7 +791,10 @@ __device__ __forceinline__ void publish(const Params& P, int b, int mode, int j,
 __device__ __forceinline__ bool has_draw_members(float t) { return t > 0.0f && temperature_valid(t); }
 
 constexpr int kStageParts = 256;  // row partials the decision holds in LDS at once
-constexpr int kWaitPolls = 1 << 20;  // bound of every wait (about a second)
+
+// Wall-clock deadline of a wait that starts now (s_memrealtime: 100 MHz).
+__device__ __forceinline__ uint64_t deadline_after(uint64_t ticks) { return wall_clock64() + ticks; }
+__device__ __forceinline__ bool before(uint64_t deadline) { return wall_clock64() < deadline; }
 
 struct DecideShared {
   float row_m[kMaxRows];
@@ -815,6 +827,7 @@ struct DrawShared {
   double rem;
   double rt, rd, total;
   unsigned long long over;
+  unsigned long long fail;  // finisher: members that did not see this call's decision
 };
 
 struct Shared {
@@ -835,27 +848,36 @@ struct SeqInfo {
   double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
 };
 
-// Waits (bounded) until partial q of this call is written, then takes it and
-// zeroes its words for the next call. Returns false if it timed out.
-__device__ __forceinline__ bool take_partial(PartialRec* q, Partial& out) {
-  uint64_t w0 = get_u64(&q->w0), w1 = get_u64(&q->w1);
-  for (int i = 0; (w0 == 0 || w1 == 0) && i < kWaitPolls; ++i) {
+// Waits (until `deadline`) for partial q of this call, then takes it and
+// zeroes its words. Returns false if the wait gave up (always, when the wait
+// bound is 0: the host's way to exercise this path).
+__device__ __forceinline__ bool take_partial(const Params& P, PartialRec* q, uint64_t deadline, Partial& out) {
+  const uint32_t tag = P.tag;
+  uint64_t m = get_u64(&q->m), s = get_u64(&q->s), i = get_u64(&q->idx), z = get_u64(&q->zg);
+  auto ready = [&] { return has_tag(m, tag) && has_tag(s, tag) && has_tag(i, tag) && has_tag(z, tag); };
+  while (!ready() && before(deadline)) {
     __builtin_amdgcn_s_sleep(4);
-    if (w0 == 0) w0 = get_u64(&q->w0);
-    if (w1 == 0) w1 = get_u64(&q->w1);
+    if (!has_tag(m, tag)) m = get_u64(&q->m);
+    if (!has_tag(s, tag)) s = get_u64(&q->s);
+    if (!has_tag(i, tag)) i = get_u64(&q->idx);
+    if (!has_tag(z, tag)) z = get_u64(&q->zg);
   }
-  put_u64(&q->w0, 0);
-  put_u64(&q->w1, 0);
-  out = Partial{__uint_as_float(uint32_t(w0 >> 32)), __uint_as_float(uint32_t(w1)), __uint_as_float(uint32_t(w1 >> 32)),
-                int(uint32_t(w0) - 1u)};
-  return w0 != 0 && w1 != 0;
+  const bool ok = P.wait_ticks != 0 && ready();
+  put_u64(&q->m, 0);
+  put_u64(&q->s, 0);
+  put_u64(&q->idx, 0);
+  put_u64(&q->zg, 0);
+  out = Partial{__uint_as_float(uint32_t(m)), __uint_as_float(uint32_t(s)), __uint_as_float(uint32_t(z)),
+                int(uint32_t(i) - 1u)};
+  return ok;
 }
 
 // The decision for sequence b (whole workgroup, once per sequence): per-row
 // log-normalisers and argmaxes from the row partials, the N accept tests, the
-// first rejection. Writes the accepted prefix (and the token itself when
-// greedy), n_accepted, the row diagnostics and the sequence record the draw
-// reads.
+// first rejection. Writes the row diagnostics and the accepted prefix; a
+// greedy sequence's emitted token and n_accepted too, while a sampled
+// sequence's are written by its draw's finisher, from the record published
+// here.
 //
 // The normalisers come from fp32 row sums (relative error ~1e-6); logs and
 // the ratio are taken in fp64, so a decision can only differ from exact
@@ -874,8 +896,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   int* amax = P.row_argmax + int64_t(b) * R;
   // Every row partial of the sequence is taken (and zeroed) whatever the
   // outcome, a group of rows at a time (thread i takes partial i of the
-  // group); the draft tokens, accept uniforms and temperature are requested
-  // alongside the first group.
+  // group).
   const int pr = P.nch;  // partials per row
   const int rows_per_group = max(1, kStageParts / pr);
   PartialRec* part_b = P.partials + int64_t(b) * R * pr;
@@ -883,9 +904,13 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const int d = tok[ti];
   const float ua = P.accept_u[int64_t(b) * N + ti];
   const float t = load_uniform(P.temperature + b);
+  const float us = load_uniform(P.sample_u + b);
   if (tid < N) ds.tok[tid] = d;
-  const bool bad = !temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab));
+  bool bad = !temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab));
+  if (P.flags & kDebug) bad = bad || (tid < N && !(ua >= 0.0f && ua < 1.0f)) || (t > 0.0f && !(us >= 0.0f && us < 1.0f));
+  const bool any_bad = block_any(bad);
   const bool greedy = (t == 0.0f);
+  const bool draws = has_draw_members(t);  // draw members wait for this decision
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
@@ -894,23 +919,21 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   constexpr int cs = 4;
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
-  bool timed_out = false, any_bad = false;
+  const uint64_t deadline = deadline_after(P.wait_ticks);
+  bool timed_out = false;
   for (int rg = 0; rg < R; rg += rows_per_group) {
     const int nr = min(rows_per_group, R - rg);
     const int np = nr * pr;
+    bool late = false;
     if (tid < np) {
       Partial q;
-      timed_out = !take_partial(part_b + int64_t(rg) * pr + tid, q) || timed_out;
+      late = !take_partial(P, part_b + int64_t(rg) * pr + tid, deadline, q);
       ds.part[tid] = q;
     }
-    if (rg == 0) {
-      any_bad = block_any(bad || timed_out);
-      if (any_bad) continue;
-      trace(2, 4);
-    } else {
-      barrier();
-    }
-    if (any_bad) continue;
+    // (also the barrier that makes the group's partials visible)
+    timed_out = block_any(late) || timed_out;
+    if (any_bad || timed_out) continue;
+    if (rg == 0) trace(2, 4);
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
       const int rr = r0 + seg;
       const int r = rg + rr;
@@ -951,17 +974,20 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     }
     barrier();
   }
-  if (any_bad) {
-    // Invalid inputs (or, not expected, a partial that never came): sentinels.
-    const bool late = block_any(timed_out);
-    for (int i = tid; i <= N; i += kThreads) otok[i] = late ? -2 : -1;
+  if (any_bad || timed_out) {
+    // Invalid inputs give -1 everywhere; a partial that never came (not
+    // expected: a workgroup that was not dispatched in time) gives -2.
+    const int code = any_bad ? -1 : -2;
     for (int r = tid; r < R; r += kThreads) {
       lse[r] = NAN;
       amax[r] = -1;
     }
-    if (tid == 0) {
-      P.out_n[b] = late ? -2 : -1;
-      if (has_draw_members(t)) publish(P, b, kModeNone, 0, 0.0f, 0.0f, 0.0, t);
+    if (draws) {
+      // The finisher writes the sentinels.
+      if (tid == 0) publish(P, b, any_bad ? kModeInvalid : kModeFailed, 0, 0.0f, 0.0f, 0.0);
+    } else {
+      for (int i = tid; i <= N; i += kThreads) otok[i] = code;
+      if (tid == 0) P.out_n[b] = code;
     }
     return;
   }
@@ -1003,7 +1029,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   if (tid == 0 && !greedy) {
     const float md = j < N ? ds.row_m[j] : 0.0f;
     const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho, t);
+    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
   }
   for (int i = tid; i <= N; i += kThreads) {
     if (i < j)
@@ -1013,7 +1039,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     else if (greedy)
       otok[i] = ds.row_idx[N + j];
   }
-  if (tid == 0) P.out_n[b] = j;
+  if (tid == 0 && greedy) P.out_n[b] = j;
 }
 
 // ---------------------------------------------------------------------------
@@ -1118,7 +1144,8 @@ __device__ __forceinline__ void block_inverse_cdf(DrawShared& ws, const double (
 //   w_x = max(0, et_x/Zt - ed_x/Zd) = max(0, et_x - rho*ed_x)/Zt,  rho = Zt/Zd,
 // (et, ed: exps relative to the row maxima), so its sign only depends on
 // whether log(et_x/ed_x) exceeds log(rho). The decision knows log(rho) from
-// the fp32 row sums to a few 1e-6; a member treats tokens more than
+// the fp32 row sums to a few 1e-6, and log(et_x/ed_x) is the difference of
+// the two exps' fp64 arguments; a member treats tokens more than
 // kSignBand away from it as certain and sums their exps into A and B per
 // sub-chunk, so a sub-chunk's weight is A/Zt - B/Zd plus the exact terms of
 // its few uncertain tokens, which the record lists. One pass over the rows
@@ -1143,8 +1170,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   // the rows.
   const double tab_v = kExp2Table[tid];  // one entry per thread
   uint4 xt[kG], xd[kG];
-  load_packed(d.trow, e, P.vocab, P.vec_ok != 0, xt);
-  if (residual) load_packed(d.drow, e, P.vocab, P.vec_ok != 0, xd);
+  load_packed(d.trow, e, P.vocab, (P.flags & kVecOk) != 0, xt);
+  if (residual) load_packed(d.drow, e, P.vocab, (P.flags & kVecOk) != 0, xd);
   trace(0, 1);
   ws.exp2_tab[tid] = tab_v;
   barrier();
@@ -1152,22 +1179,21 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;
   uint32_t unc = 0;  // bit k: token k of this thread has an uncertain sign
   if (residual) {
-    // The sign of w_x follows (zt - zd)/T - (mt - md)/T against log(rho).
-    const float inv_tf = float(d.inv_t);
-    const float dmf = float(d.nmt - d.nmd);  // -(mt - md)/T
-    const float hi = float(s.log_rho + kSignBand), lo = float(s.log_rho - kSignBand);
+    // The sign of w_x follows log(et/ed) = at - ad (the exps' fp64 arguments,
+    // exact to about 1e-16 of their size) against log(rho).
+    const double hi = s.log_rho + kSignBand, lo = s.log_rho - kSignBand;
     bool any_band = false;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const float ztk = Logit<T>::element(xt, k);
-      const float zdk = Logit<T>::element(xd, k);
-      const double et = exp_nonpos_tab(exp_arg(ztk, d.nmt, d.inv_t), tab);
-      const double ed = exp_nonpos_tab(exp_arg(zdk, d.nmd, d.inv_t), tab);
+      const double at = exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t);
+      const double ad = exp_arg(Logit<T>::element(xd, k), d.nmd, d.inv_t);
+      const double et = exp_nonpos_tab(at, tab);
+      const double ed = exp_nonpos_tab(ad, tab);
       st += et;
       sd += ed;
       // +inf when the draft gives the token zero mass, NaN (neither class)
       // when both rows do: such a token adds nothing wherever it goes.
-      const float lr = fmaf(ztk - zdk, inv_tf, dmf);
+      const double lr = at - ad;
       const bool pos = lr > hi;
       const bool band = !pos && lr >= lo;
       const double pos_d = pos ? 1.0 : 0.0;  // adds et and ed exactly, or nothing
@@ -1178,9 +1204,18 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     // Uncertain tokens are rare (a wave in tens holds one): their bits are
     // taken in a second pass, with the same arithmetic, only where needed.
     if (__ballot(any_band)) {
+      // The logits pass through an empty asm the compiler cannot see
+      // through: otherwise it keeps the first pass's kPer fp64 differences
+      // live until here instead of recomputing them.
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        asm volatile("" : "+v"(xt[u].x), "+v"(xt[u].y), "+v"(xt[u].z), "+v"(xt[u].w));
+        asm volatile("" : "+v"(xd[u].x), "+v"(xd[u].y), "+v"(xd[u].z), "+v"(xd[u].w));
+      }
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const float lr = fmaf(Logit<T>::element(xt, k) - Logit<T>::element(xd, k), inv_tf, dmf);
+        const double lr = exp_arg(Logit<T>::element(xt, k), d.nmt, d.inv_t) -
+                          exp_arg(Logit<T>::element(xd, k), d.nmd, d.inv_t);
         unc |= (!(lr > hi) && lr >= lo) ? (1u << k) : 0u;
       }
     }
@@ -1392,6 +1427,21 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (tid + u * kThreads < n_words) ws.stage[tid + u * kThreads] = words[u];
   barrier();
   trace_at(1, b, 1);
+  // Every member must have seen this call's decision, and the decision must
+  // call for a draw; otherwise the sequence gets its sentinels here.
+  if (tid < 64) {
+    const unsigned long long bad =
+        __ballot(lane < nm && ws.stage[lane * kW + MemberRec::kStatus] != tagged(P.tag, 1u));
+    if (lane == 0) ws.fail = bad;
+  }
+  barrier();
+  if (ws.fail != 0ull || !(s.mode == kModeResidual || s.mode == kModeBonus)) {
+    const int code = s.mode == kModeInvalid ? -1 : -2;
+    int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
+    for (int i = tid; i <= P.n_draft; i += kThreads) otok[i] = code;
+    if (tid == 0) P.out_n[b] = code;
+    return;
+  }
   const DrawRows<T> d = draw_rows<T>(P, b, s);
   double w[kSubs];
 #pragma unroll
@@ -1483,6 +1533,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (lane == 0) {
       const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
       P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
+      P.out_n[b] = s.j;
     }
   }
 }
@@ -1526,30 +1577,36 @@ __device__ __forceinline__ void decision_role(const Params& P, Shared& sh, int b
   trace(2, 3);
 }
 
-// Waits (bounded) for sequence b's decision. A draw member only waits for
-// the decision workgroup, which precedes it in the launch order and waits only
-// for row-statistics workgroups that precede it and never wait, so the wait
-// ends. Returns false if it timed out.
+// Waits (until the call's wait bound) for sequence b's decision. A draw
+// member only waits for the decision workgroup, which precedes it in the
+// launch order and waits only for row-statistics workgroups that precede it
+// and never wait. Returns false if the wait gave up (s.mode is then
+// kModeFailed).
 
 __shared__ SeqInfo g_seq;
 __shared__ int g_seq_ok;
 
-__device__ __forceinline__ bool wait_decision(const Params& P, int b, SeqInfo& s) {
+__device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp, SeqInfo& s) {
   if (threadIdx.x == 0) {
     const SeqRec* q = P.seq + b;
-    uint64_t w0 = get_u64(&q->w0), w1 = get_u64(&q->w1), w2 = get_u64(&q->w2);
-    for (int i = 0; !(w0 & w1 & w2 & kPublished) && i < kWaitPolls; ++i) {
-      __builtin_amdgcn_s_sleep(8);
-      if (!(w0 & kPublished)) w0 = get_u64(&q->w0);
-      if (!(w1 & kPublished)) w1 = get_u64(&q->w1);
-      if (!(w2 & kPublished)) w2 = get_u64(&q->w2);
+    const uint32_t tag = P.tag;
+    uint64_t jm = get_u64(&q->jm), mt = get_u64(&q->mt), md = get_u64(&q->md), lr = get_u64(&q->logrho);
+    auto ready = [&] { return has_tag(jm, tag) && has_tag(mt, tag) && has_tag(md, tag) && has_tag(lr, tag); };
+    if (!ready()) {
+      const uint64_t deadline = deadline_after(P.wait_ticks);
+      while (!ready() && before(deadline)) {
+        __builtin_amdgcn_s_sleep(8);
+        if (!has_tag(jm, tag)) jm = get_u64(&q->jm);
+        if (!has_tag(mt, tag)) mt = get_u64(&q->mt);
+        if (!has_tag(md, tag)) md = get_u64(&q->md);
+        if (!has_tag(lr, tag)) lr = get_u64(&q->logrho);
+      }
     }
-    const bool ok = (w0 & w1 & w2 & kPublished) != 0;
+    const bool ok = P.wait_ticks != 0 && ready();
     g_seq_ok = ok;
-    g_seq = ok ? SeqInfo{__uint_as_float(uint32_t(w1 >> 32) & 0x7fffffffu), int((w0 >> 32) & 0xff),
-                         int((w0 >> 40) & 0xffff), __uint_as_float(uint32_t(w0)), __uint_as_float(uint32_t(w1)),
-                         double(__uint_as_float(uint32_t(w2)))}
-               : SeqInfo{0.0f, kModeNone, 0, 0.0f, 0.0f, 0.0};
+    g_seq = ok ? SeqInfo{temp, int((jm >> 8) & 0xff), int(jm & 0xff), __uint_as_float(uint32_t(mt)),
+                         __uint_as_float(uint32_t(md)), double(__uint_as_float(uint32_t(lr)))}
+               : SeqInfo{temp, kModeFailed, 0, 0.0f, 0.0f, 0.0};
   }
   barrier();
   s = g_seq;
@@ -1557,36 +1614,34 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, SeqInfo& s
 }
 
 // Draw member c of sequence b. Every member of a sampled sequence reports
-// when done; the last one clears the decision's flag and, if there is a draw,
-// draws the token.
+// (with whether it saw this call's decision) when done; the last one clears
+// the decision's record and finishes the sequence: its token and n_accepted,
+// or its sentinels.
 template <typename T>
 __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
-  if (!has_draw_members(load_uniform(P.temperature + b))) return;
+  const float temp = load_uniform(P.temperature + b);
+  if (!has_draw_members(temp)) return;
   trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
   SeqInfo s;
-  if (!wait_decision(P, b, s)) {
-    // Not expected: the decision did not come within the bound. The sequence
-    // is reported as failed rather than the device left waiting.
-    if (threadIdx.x == 0) P.out_n[b] = -2;
-  }
+  const bool saw = wait_decision(P, b, temp, s);
   trace(0, 5);
-  if (s.mode != kModeNone) member_record<T>(P, sh, b, c, s);
+  if (s.mode == kModeResidual || s.mode == kModeBonus) member_record<T>(P, sh, b, c, s);
+  if (threadIdx.x == 0) put_u64(&P.records[int64_t(b) * P.nm + c].w[MemberRec::kStatus], tagged(P.tag, saw ? 1u : 0u));
   trace(0, 3);
   const bool last = last_arrival(P.draw_done + b * kCounterStride, P.nm);
   trace(0, 4);
   if (last) {
     if (threadIdx.x == 0) {
-      put_u64(&P.seq[b].w0, 0);
-      put_u64(&P.seq[b].w1, 0);
-      put_u64(&P.seq[b].w2, 0);
+      put_u64(&P.seq[b].jm, 0);
+      put_u64(&P.seq[b].mt, 0);
+      put_u64(&P.seq[b].md, 0);
+      put_u64(&P.seq[b].logrho, 0);
     }
-    if (s.mode != kModeNone) {
-      critical_path();
-      trace_at(1, b, 0);
-      finish<T>(P, sh, b, s);
-      trace_at(1, b, 4);
-    }
+    critical_path();
+    trace_at(1, b, 0);
+    finish<T>(P, sh, b, s);
+    trace_at(1, b, 4);
   }
 }
 
@@ -1677,7 +1732,10 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   // statistics, draw) pairs, so a sequence's decision is normally out before
   // its draw members start.
   p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + 1 + p.nm)));
-  p.vec_ok = (int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0;
+  p.flags = ((int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0 ? kVecOk : 0u) | (a.debug ? kDebug : 0u);
+  p.tag = a.tag;
+  // (not min(): on the host it takes ints)
+  p.wait_ticks = a.wait_ticks > uint64_t(UINT32_MAX) ? UINT32_MAX : uint32_t(a.wait_ticks);
   const int64_t blocks = int64_t(a.batch) * (p.items_per_seq + 1 + p.nm);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);

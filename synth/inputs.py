@@ -38,6 +38,7 @@ __all__ = [
     "workload",
     "make_batch",
     "make_trials",
+    "resample",
     "widen",
     "to_bf16_bits",
     "gumbel_max_tokens",
@@ -229,3 +230,23 @@ def make_trials(wl: Workload, seed: int, n_trials: int) -> Batch:
         grid_uniforms(rng, (n_trials,)),
         np.full((n_trials,), base.temperature[0], dtype=np.float32),
     )
+
+
+def resample(batch: Batch, wl: Workload, seed: int, variant: int) -> Batch:
+    """The same logits with fresh draft tokens and uniforms.
+
+    Variant 0 is ``batch`` itself; variant v > 0 draws every sequence's draft
+    tokens again from its tempered draft distribution (Gumbel-max) and new
+    accept and sample uniforms, from a seed of its own. Many verification
+    cases then share one set of logits (one upload, one set of row
+    normalisers) while their decisions and draws differ.
+    """
+    if variant == 0:
+        return batch
+    rng = np.random.default_rng(np.random.SeedSequence([wl.index, int(seed), 1000 + int(variant)]))
+    B, N = batch.batch, batch.n_draft
+    tokens = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        tokens[b] = gumbel_max_tokens(widen(batch.draft_logits[b], batch.dtype), float(batch.temperature[b]), rng)
+    return Batch(batch.dtype, batch.draft_logits, batch.target_logits, tokens, grid_uniforms(rng, (B, N)),
+                 grid_uniforms(rng, (B,)), batch.temperature)

@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
-                                          "specv_stage_name"}
+                                          "specv_stage_name", "specv_set_wait_limit"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,6 +74,7 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
     lib.specv_destroy(None)  # no-op
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
+    assert lib.specv_set_wait_limit(None, 10) == _lib.SPECV_EINVAL
     n = ctypes.c_int()
     assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
     assert specv.specv_stage_name(0) == "verify"

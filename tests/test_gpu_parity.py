@@ -14,8 +14,8 @@ from scipy import special, stats
 
 import oracle
 import synth
-from parity import (MARGIN, GpuResult, Tally, check_row_stats, compare, require_gpu, run_gpu, run_oracle,
-                    to_device)
+from parity import (MARGIN, GpuResult, Tally, check_row_stats, compare, full_size_parity, require_gpu, run_gpu,
+                    run_oracle, to_device)
 from speculative_sampling_verification_specv_amd import SpecvError, Verifier, _lib
 
 pytestmark = pytest.mark.gpu
@@ -93,32 +93,25 @@ def test_scaled_parity(name, batch, vocab):
     total.check(name)
 
 
-FULL = ["b1_n5_v32000_f32", "b64_n5_v128256_bf16", "b256_n7_v151936_bf16_mixed", "b32_n16_v128256_f32"]
+# Full sizes: every sequence of several seeded calls (each batch of logits
+# with resampled draft tokens and uniforms), at least 10^3 cases per
+# workload; tokens and n_accepted by the parity rules, lse and argmax of every
+# row read.
+FULL = [
+    ("b1_n5_v32000_f32", list(range(7, 57)), 20),
+    ("b64_n5_v128256_bf16", [7, 8, 9, 10], 4),
+    ("b256_n7_v151936_bf16_mixed", [7, 8], 2),
+    ("b32_n16_v128256_f32", [7, 8, 9, 10], 8),
+]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size(name):
-    """Full workload sizes: oracle on sampled sequences (all greedy ones), properties on all."""
+@pytest.mark.parametrize("name,seeds,n_var", FULL, ids=[f[0] for f in FULL])
+def test_full_size(name, seeds, n_var):
     require_gpu()
-    wl = W[name]
-    b = synth.make_batch(wl, seed=7)
-    gpu = run_gpu(b)
-    B, N = wl.batch, wl.n_draft
-    rng = np.random.default_rng(17)
-    seqs = sorted(set(rng.choice(B, size=min(B, 12), replace=False).tolist())
-                  | {s for s in range(B) if b.temperature[s] == 0.0})
-    res = run_oracle(b, seqs)
-    tally = compare(b, gpu, res, seqs)
-    check_row_stats(b, gpu, [s for s in seqs if b.temperature[s] > 0][:6])
-    _say(f"[parity] {name} full: sampled={len(seqs)} exact={tally.exact} excused={tally.excused}")
-    tally.check(name)
-    # Properties of every sequence.
-    assert np.all((gpu.n_accepted >= 0) & (gpu.n_accepted <= N))
-    for s in range(B):
-        j = gpu.n_accepted[s]
-        assert np.array_equal(gpu.tokens[s, :j], b.draft_tokens[s, :j])
-        assert 0 <= gpu.tokens[s, j] < wl.vocab
-        assert np.all(gpu.tokens[s, j + 1:] == -1)
+    total = full_size_parity(name, seeds, n_var, say=_say)
+    _say(f"[parity] {name} full size: cases={total.cases} exact={total.exact} excused={total.excused}")
+    assert total.cases >= 1000
+    total.check(name)
 
 
 def test_invalid_inputs_give_sentinels():
@@ -346,6 +339,7 @@ def test_uncertain_sign_overflow(dtype):
     res = run_oracle(b)
     check_row_stats(b, gpu)
     exact = 0
+    excused = 0
     for s_, r in enumerate(res):
         assert r.n_accepted == 0 and gpu.n_accepted[s_] == 0
         # The residual mass S is ~5e-5 here, so the margin is judged relative to it.
@@ -358,8 +352,75 @@ def test_uncertain_sign_overflow(dtype):
         if int(gpu.tokens[s_, 0]) == r.tokens[0]:
             exact += 1
         else:
+            excused += 1
             assert r.sample_margin / S < 1e-8, (s_, int(gpu.tokens[s_, 0]), r.tokens[0], r.sample_margin / S)
-    _say(f"[parity] uncertain overflow {dtype}: cases={len(res)} exact={exact}")
+    _say(f"[parity] uncertain overflow {dtype}: cases={len(res)} exact={exact} excused={excused}")
+    # A mismatch needs u*S within 1e-8*S of a CDF edge: at most one in the batch.
+    assert excused <= 1
+
+
+@pytest.mark.parametrize("T", [0.01, 0.05])
+def test_temperature_with_logit_offset(T):
+    """Draft logits = target + noise + a constant offset (the softmax ignores
+    it, the arithmetic does not): at a low temperature the differences of the
+    tempered logits are large, and the residual's sign must still be taken
+    right for every token. Every sequence against the oracle."""
+    require_gpu()
+    total = Tally()
+    for dtype, offset in (("f32", 30.0), ("bf16", 30.0), ("f32", -45.0)):
+        wl = synth.Workload("offset", 13, 12, 4, 3 * 4096 + 77, dtype, 0.2, 0.0, (0.001, 0.004), (T, T))
+        b = synth.make_batch(wl, seed=100 + int(T * 1000) + int(abs(offset)))
+        d64 = synth.widen(b.draft_logits, dtype) + offset
+        b.draft_logits = (d64.astype(np.float32) if dtype == "f32"
+                          else synth.to_bf16_bits(d64.astype(np.float32)))
+        rng = np.random.default_rng(5)
+        for s_ in range(wl.batch):
+            b.draft_tokens[s_] = synth.gumbel_max_tokens(synth.widen(b.draft_logits[s_], dtype), T, rng)
+        gpu, t = _parity(b, label=f"T={T} offset={offset} {dtype}")
+        total = total.merge(t)
+    total.check(f"offset T={T}")
+
+
+def test_wait_limit_zero_then_normal_call():
+    """A wait bound of 0 makes every wait between workgroups give up: every
+    sequence reports -2 and every workgroup exits, leaving words behind that
+    their producers wrote after the give-up. Then calls on the same handle with
+    the default bound match the oracle exactly: nothing a gave-up call left
+    behind is taken."""
+    require_gpu()
+    wl = _scaled("b256_n7_v151936_bf16_mixed", 24, 2 * 32768 + 4099)
+    b = synth.make_batch(wl, seed=77)
+    res = run_oracle(b)
+    with Verifier(wl.batch, wl.n_draft, wl.vocab, wl.dtype) as v:
+        v.set_wait_limit(0)
+        gave_up_runs = [run_gpu(b, v) for _ in range(3)]
+        v.set_wait_limit(100000)
+        normal = [run_gpu(b, v) for _ in range(2)]
+    for gpu in normal:
+        compare(b, gpu, res).check("after wait 0")
+        check_row_stats(b, gpu)
+    for gpu in gave_up_runs:
+        assert np.all(gpu.n_accepted == -2), gpu.n_accepted
+    _say(f"[wait 0] all {3 * wl.batch} sequences of 3 calls gave up; the next 2 calls matched the oracle")
+
+
+def test_debug_checks_uniforms(monkeypatch):
+    """With SPECV_DEBUG set when the handle is created, a uniform outside
+    [0, 1) makes its sequence invalid (-1); the others match the oracle."""
+    require_gpu()
+    monkeypatch.setenv("SPECV_DEBUG", "1")
+    wl = W["b1_n5_v32000_f32"].with_sizes(batch=8, vocab=3000)
+    b = synth.make_batch(wl, seed=19)
+    b.accept_uniforms[1, 2] = np.float32(1.0)
+    b.accept_uniforms[2, 0] = np.float32(-0.25)
+    b.accept_uniforms[3, 4] = np.float32(np.nan)
+    b.sample_uniforms[4] = np.float32(1.5)
+    with Verifier(wl.batch, wl.n_draft, wl.vocab, wl.dtype) as v:
+        gpu = run_gpu(b, v)
+    for s_ in (1, 2, 3, 4):
+        assert gpu.n_accepted[s_] == -1 and np.all(gpu.tokens[s_] == -1), s_
+    good = [0, 5, 6, 7]
+    compare(b, gpu, run_oracle(b, good), good).check("debug")
 
 
 def test_reuse_with_smaller_batch_and_draft():

@@ -352,11 +352,33 @@ def test_greedy_first_argmax_with_ties():
 def test_invalid_inputs_give_sentinel():
     draft = np.zeros((2, 4))
     target = np.zeros((3, 4))
-    for T, toks in ((float("nan"), [0, 1]), (-1.0, [0, 1]), (float("inf"), [0, 1]), (1.0, [0, 4]),
-                    (1.0, [-1, 0]), (0.0, [7, 0]), (1e-30, [0, 1]), (2.0 ** -61, [0, 1])):
+    for T, toks in ((float("nan"), [0, 1]), (-1.0, [0, 1]), (float("inf"), [0, 1]), (-0.5, [0, 1]),
+                    (1.0, [0, 4]), (1.0, [-1, 0]), (0.0, [7, 0])):
         r = oracle.verify_sequence(draft, target, toks, [0.5, 0.5], 0.5, T)
         assert r.n_accepted == -1 and r.tokens == [-1, -1, -1]
-    assert oracle.verify_sequence(draft, target, [0, 1], [0.5, 0.5], 0.5, 2.0 ** -60).n_accepted >= 0
+
+
+def test_every_finite_positive_temperature_is_computed():
+    """Tiny temperatures are inside the rule's domain: as T -> 0 the tempered
+    distributions tend to point masses, so away from ties the result is the
+    greedy one (the oracle's fp64 keeps z / T finite down to the smallest
+    float32 T)."""
+    wl = synth.workload("b1_n5_v32000_f32").with_sizes(batch=6, vocab=3000)
+    b = synth.make_batch(wl, seed=31)
+    d64 = synth.widen(b.draft_logits, b.dtype)
+    t64 = synth.widen(b.target_logits, b.dtype)
+    for T in (2.0 ** -61, 1e-30, float(np.float32(2.0 ** -149))):
+        for s in range(wl.batch):
+            toks = np.argmax(d64[s], axis=-1)
+            g = oracle.verify_sequence(d64[s], t64[s], toks, np.full(5, 0.5), 0.5, 0.0)
+            r = oracle.verify_sequence(d64[s], t64[s], toks, np.full(5, 0.5), 0.5, T)
+            assert r.n_accepted >= 0 and all(np.isfinite(r.lse))
+            assert (r.n_accepted, r.tokens) == (g.n_accepted, g.tokens), (T, s)
+    # A ratio beyond the fp64 range (q(d) > p(d) at a tiny T) exceeds every uniform: accepted.
+    d = np.array([[1.0, 0.0]])
+    t = np.array([[0.0, 1.0], [0.0, 1.0]])
+    r = oracle.verify_sequence(d, t, [1], [1.0 - 2 ** -24], 0.5, 1e-30)
+    assert r.n_accepted == 1 and r.tokens == [1, 1]
 
 
 # ------------------------------------------------------ planted mistakes
@@ -404,3 +426,257 @@ def test_planted_temperature_mistake_is_caught(monkeypatch):
                                case["draft_tokens"], np.asarray(case["accept_uniforms"]),
                                case["sample_uniform"], T)
     assert (r.n_accepted, r.tokens) != (case["n_accepted"], case["tokens"])
+
+
+# ------------------------------------------------------------ margins
+
+def _hand_result(case):
+    T = case["temperature"]
+    ua = np.asarray(case["accept_uniforms"], dtype=np.float32).astype(np.float64)
+    us = float(np.float32(case["sample_uniform"]))
+    return oracle.verify_sequence(_logits(case["draft_probs"], T), _logits(case["target_probs"], T),
+                                  case["draft_tokens"], ua, us, T)
+
+
+def _hand_margins_hold() -> bool:
+    for case in _load("hand_examples.json")["cases"]:
+        r = _hand_result(case)
+        want = [float(m) for m in case["decision_margins"]]
+        if len(r.decision_margins) != len(want):
+            return False
+        for got, w in zip(r.decision_margins, want):
+            if math.isinf(w):
+                if not math.isinf(got):
+                    return False
+            elif not abs(got - w) <= 2e-7:
+                return False
+        if not abs(r.sample_margin - case["sample_margin"]) <= 2e-7:
+            return False
+    return True
+
+
+def _brute_force_margins_hold(seed=3) -> bool:
+    """V = 16 brute force: the draw margin is the distance from u*S to the
+    nearest CDF edge (every edge 0, C_0, ..., C_15 examined), and each decision
+    margin is |u_i - r_i| with r_i = q_i(d_i)/p_i(d_i) from scipy's softmax."""
+    rng = np.random.default_rng(seed)
+    for trial in range(200):
+        w = rng.random(16)
+        w[rng.random(16) < 0.3] = 0.0
+        if w.sum() == 0:
+            continue
+        u = float(synth.grid_uniforms(rng, ()))
+        k, margin, S = oracle.inverse_cdf(w, u)
+        edges = np.concatenate([[0.0], np.cumsum(w)])
+        if not abs(margin - np.min(np.abs(u * S - edges))) <= 1e-15:
+            return False
+    for trial in range(60):
+        N, V = 4, 16
+        d = rng.normal(size=(N, V))
+        t = np.concatenate([d, rng.normal(size=(1, V))]) + rng.normal(scale=1.5, size=(N + 1, V))
+        T = float(np.float32(rng.choice([0.5, 1.0, 2.0])))
+        p = special.softmax(d / T, axis=-1)
+        q = special.softmax(t / T, axis=-1)
+        toks = np.array([rng.choice(V, p=p[i]) for i in range(N)])
+        ua = synth.grid_uniforms(rng, (N,)).astype(np.float64)
+        r = oracle.verify_sequence(d, t, toks, ua, 0.5, T)
+        tested = min(r.n_accepted + 1, N)
+        if len(r.decision_margins) != tested:
+            return False
+        for i in range(tested):
+            want = abs(ua[i] - q[i, toks[i]] / p[i, toks[i]])
+            if not abs(r.decision_margins[i] - want) <= 1e-12 * max(1.0, want):
+                return False
+    return True
+
+
+def test_margins_of_hand_cases():
+    assert _hand_margins_hold()
+
+
+def test_margins_by_brute_force():
+    assert _brute_force_margins_hold()
+
+
+@pytest.mark.parametrize("attr,bad", [
+    ("decision_margin", lambda u, r: 0.0),                          # no margin at all
+    ("decision_margin", lambda u, r: abs(u - 1.0 / r) if r else math.inf),  # inverted ratio
+    ("cdf_margin", lambda t, lo, up: 0.0),
+    ("cdf_margin", lambda t, lo, up: abs(up - t)),                  # upper edge only
+    ("cdf_margin", lambda t, lo, up: abs(t - lo)),                  # lower edge only
+])
+def test_planted_margin_mistakes_are_caught(monkeypatch, attr, bad):
+    monkeypatch.setattr(specv_oracle, attr, bad)
+    assert not (_hand_margins_hold() and _brute_force_margins_hold())
+
+
+# ------------------------------------------------------- draft-side sampler
+
+def _sampler_frequencies_hold(T, n=100_000, seed=8) -> bool:
+    wl = synth.workload("tiny_b1_n4_v16_f32")
+    b = synth.make_batch(wl, seed=2)
+    z = synth.widen(b.draft_logits[0, 0], b.dtype)
+    rng = np.random.default_rng(seed)
+    us = synth.grid_uniforms(rng, (n,)).astype(np.float64)
+    toks = np.array([oracle.sample_row(z, T, u).token for u in us])
+    q = special.softmax(z / T)
+    return stats.chisquare(np.bincount(toks, minlength=z.size), n * q).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("T", [1.0, float(np.float32(0.7)), 2.5])
+def test_sampler_follows_tempered_softmax(T):
+    """Drawn tokens follow softmax(z / T) (chi-square against scipy's softmax)."""
+    assert _sampler_frequencies_hold(T)
+
+
+def test_sampler_brute_force_cdf():
+    """V = 16: over a fine grid of u the token is the smallest k with C_k > u*S,
+    each token drawn for a share q_k of the grid, monotone in u."""
+    rng = np.random.default_rng(4)
+    for trial in range(5):
+        z = rng.normal(scale=2.0, size=16)
+        z[rng.random(16) < 0.2] = -np.inf
+        z[5] = 1.0
+        q = special.softmax(z)
+        grid = np.arange(1 << 13) / float(1 << 13)
+        drawn = np.array([oracle.sample_row(z, 1.0, u).token for u in grid])
+        assert np.all(np.diff(drawn) >= 0) and np.all(q[drawn] > 0)
+        freq = np.bincount(drawn, minlength=16) / grid.size
+        assert np.max(np.abs(freq - q)) <= 2.0 / grid.size + 1e-12
+
+
+def test_sampler_greedy_and_invalid():
+    row = np.array([0.0, 2.0, -1.0, 2.0])
+    assert oracle.sample_row(row, 0.0, 0.9).token == 1
+    for T in (float("nan"), -1.0, float("inf")):
+        assert oracle.sample_row(row, T, 0.5).token == -1
+    # Tiny T tends to the argmax.
+    assert oracle.sample_row(np.array([0.0, 2.0, 1.999]), 1e-30, 0.99).token == 1
+
+
+def test_planted_sampler_temperature_mistake_is_caught(monkeypatch):
+    orig = specv_oracle.tempered_probabilities
+    monkeypatch.setattr(specv_oracle, "tempered_probabilities", lambda z, T: orig(z, 1.0))  # T dropped
+    assert not _sampler_frequencies_hold(2.5)
+
+
+# ------------------------------------------------------- acceptance telemetry
+
+@pytest.mark.parametrize("case", _load("hand_examples.json")["acceptance_rate_cases"], ids=lambda c: c["name"])
+def test_acceptance_rates_hand_cases(case):
+    T = case["temperature"]
+    alpha, tau = oracle.acceptance_rates(_logits(case["draft_probs"], T), _logits(case["target_probs"], T),
+                                         case["draft_tokens"], T)
+    assert np.allclose(alpha, case["alpha"], rtol=0, atol=1e-12)
+    assert abs(tau - case["tau"]) < 1e-12
+
+
+@pytest.mark.parametrize("case", _load("hand_examples.json")["greedy_acceptance_cases"], ids=lambda c: c["name"])
+def test_acceptance_rates_greedy(case):
+    target = np.asarray(case["target_logits"])
+    N = len(case["draft_tokens"])
+    alpha, tau = oracle.acceptance_rates(np.zeros((N, target.shape[1])), target, case["draft_tokens"], 0.0)
+    assert alpha == case["alpha"] and tau == case["tau"]
+
+
+def test_tau_closed_form_and_page_values():
+    """Constant alpha at every position: tau = (1 - a^(N+1)) / (1 - a) (lesson);
+    the page's rule of thumb a = 0.75, N = 5 gives about 3, and a = 0.7 with
+    ten drafts leaves 3 to 4 tokens per pass (guide)."""
+    g = _load("page_values.json")["tokens_per_verify"]
+    for a, N in ((0.75, 5), (0.7, 10), (0.4, 3), (0.4, 7), (0.9, 16)):
+        p0, q0 = 0.95, 0.95 - (1.0 - a)  # sum min(p, q) = q0 + (1 - p0) = a
+        d = np.tile(_logits([p0, 1 - p0], 1.0), (N, 1))
+        t = np.tile(_logits([q0, 1 - q0], 1.0), (N + 1, 1))
+        alpha, tau = oracle.acceptance_rates(d, t, np.zeros(N, int), 1.0)
+        assert np.allclose(alpha, a, atol=1e-12)
+        assert abs(tau - (1 - a ** (N + 1)) / (1 - a)) < 1e-12
+    rt = g["rule_of_thumb"]
+    d = np.tile(_logits([0.95, 0.05], 1.0), (rt["n_draft"], 1))
+    t = np.tile(_logits([0.7, 0.3], 1.0), (rt["n_draft"] + 1, 1))
+    assert abs(oracle.acceptance_rates(d, t, np.zeros(rt["n_draft"], int), 1.0)[1] - rt["about"]) <= rt["band"]
+
+
+def test_acceptance_rate_is_the_monte_carlo_frequency(tiny_mc):
+    """alpha_i from the formula against the oracle's own accept decisions over
+    10^5 trials (the acceptance rule and sum min(p, q) are two independent
+    routes to the same number), and alpha_i = 1 - sum_x (q_i - p_i)_+."""
+    d64, t64, T, tr, res = tiny_mc
+    alpha, tau = oracle.acceptance_rates(d64, t64, tr.draft_tokens[0], T)
+    nacc = np.array([r.n_accepted for r in res])
+    q = special.softmax(t64 / T, axis=-1)
+    p = special.softmax(d64 / T, axis=-1)
+    for i in range(d64.shape[0]):
+        reached = nacc >= i
+        f = (nacc[reached] > i).mean()
+        a = alpha[i]
+        assert abs(f - a) < 4 * math.sqrt(a * (1 - a) / reached.sum())
+        assert abs(a - (1.0 - np.clip(q[i] - p[i], 0, None).sum())) < 1e-12
+    emitted = nacc + 1
+    assert abs(emitted.mean() - tau) < 4 * emitted.std() / math.sqrt(len(res))
+
+
+def test_planted_acceptance_mistake_is_caught(monkeypatch):
+    case = [c for c in _load("hand_examples.json")["acceptance_rate_cases"] if c["name"] == "temperature_two"][0]
+    T = case["temperature"]
+    orig = specv_oracle.tempered_probabilities
+    monkeypatch.setattr(specv_oracle, "tempered_probabilities", lambda z, T: orig(z, 1.0))  # T dropped
+    alpha, _ = oracle.acceptance_rates(_logits(case["draft_probs"], T), _logits(case["target_probs"], T),
+                                       case["draft_tokens"], T)
+    assert not np.allclose(alpha, case["alpha"], atol=1e-6)
+
+
+# ------------------------------------------------------- KV-cache commit
+
+def _kv_exercise_holds(commit) -> bool:
+    g = _load("kv_rollback_exercise.json")
+    P, E, L = 4, 6, 32
+    N, prefix = g["n_draft"], g["prefix_len"]
+    rng = np.random.default_rng(9)
+    cache = rng.integers(0, 256, size=(P, 1, L, E), dtype=np.uint8)
+    scratch = rng.integers(0, 256, size=(P, 1, N, E), dtype=np.uint8)
+    n_acc = g["rejected_position_counting_from_1"] - 1
+    if n_acc != g["n_accepted"]:
+        return False
+    new, new_len = commit(cache, np.array([prefix]), scratch, np.array([n_acc]))
+    if int(new_len[0]) != g["expected_len"]:
+        return False
+    want = []
+    for kind, idx in zip(g["expected_read"][0::2], g["expected_read"][1::2]):
+        want.append(cache[:, 0, idx, :] if kind == "prefix" else scratch[:, 0, idx, :])
+    read = new[:, 0, :int(new_len[0]), :]
+    return np.array_equal(read, np.stack(want, axis=1)) and np.array_equal(new[:, 0, int(new_len[0]):], cache[:, 0, int(new_len[0]):])
+
+
+def test_kv_rollback_exercise():
+    """The lesson's exercise 4: a 10-token prefix, 5 drafts, rejection at the
+    third; the next read is the prefix plus the first 2 drafts, exactly."""
+    assert _kv_exercise_holds(oracle.kv_commit)
+
+
+def test_kv_commit_edge_cases():
+    rng = np.random.default_rng(10)
+    P, B, L, N, E = 2, 6, 12, 5, 8
+    cache = rng.integers(0, 256, size=(P, B, L, E), dtype=np.uint8)
+    scratch = rng.integers(0, 256, size=(P, B, N, E), dtype=np.uint8)
+    lens = np.array([0, 3, 7, 9, 2, 12])
+    nacc = np.array([0, 5, 5, 4, -1, 1])   # nothing, all, exactly full, overflow, invalid, overflow
+    new, nl = oracle.kv_commit(cache, lens, scratch, nacc)
+    assert nl.tolist() == [0, 8, 12, -1, -1, -1]
+    assert np.array_equal(new[:, 0], cache[:, 0])
+    assert np.array_equal(new[:, 1, 3:8], scratch[:, 1, :5]) and np.array_equal(new[:, 1, :3], cache[:, 1, :3])
+    assert np.array_equal(new[:, 2, 7:12], scratch[:, 2])
+    for b in (3, 4, 5):
+        assert np.array_equal(new[:, b], cache[:, b])
+    assert np.array_equal(new[:, 1, 8:], cache[:, 1, 8:])
+
+
+def test_planted_kv_mistakes_are_caught():
+    def keeps_rejected(cache, lens, scratch, nacc):  # commits the rejected draft too
+        return oracle.kv_commit(cache, lens, scratch, np.minimum(np.asarray(nacc) + 1, scratch.shape[2]))
+
+    def wrong_offset(cache, lens, scratch, nacc):  # overwrites the prefix's last entry
+        return oracle.kv_commit(cache, np.asarray(lens) - 1, scratch, nacc)
+
+    assert not _kv_exercise_holds(keeps_rejected)
+    assert not _kv_exercise_holds(wrong_offset)
