@@ -63,6 +63,16 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // a workgroup that another waits for).
 constexpr int64_t kDefaultWaitUs = 100000;
 
+// Number of the call after `tag`: never one whose low 17 bits are all zero
+// (0 included), which the kernels' row-statistics records could not tell
+// from a zeroed word.
+uint32_t next_call_tag(uint32_t tag) {
+  do {
+    ++tag;
+  } while ((tag & 0x1ffffu) == 0u);
+  return tag;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
@@ -201,7 +211,7 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.wait_ticks = h->wait_ticks;
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, h->timing ? h->events : nullptr, &stages) != hipSuccess) return SPECV_EHIP;
-  h->next_tag = h->next_tag == UINT32_MAX ? 1u : h->next_tag + 1u;
+  h->next_tag = next_call_tag(h->next_tag);
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;

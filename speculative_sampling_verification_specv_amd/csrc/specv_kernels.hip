@@ -94,6 +94,19 @@ __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 
 __shared__ int g_vote[kThreads / 64];
 
+// Uniform ORs of two per-thread flags over the workgroup (bit 0: a, bit 1: b).
+__shared__ int g_vote2[kThreads / 64];
+__device__ __forceinline__ int block_any2(bool a, bool b) {
+  const unsigned long long ma = __ballot(a), mb = __ballot(b);
+  if ((threadIdx.x & 63) == 0) g_vote2[threadIdx.x >> 6] = (ma != 0ull ? 1 : 0) | (mb != 0ull ? 2 : 0);
+  barrier();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) r |= g_vote2[w];
+  barrier();
+  return r;
+}
+
 // Uniform OR of a per-thread flag over the workgroup.
 __device__ __forceinline__ bool block_any(bool v) {
   const unsigned long long m = __ballot(v);
@@ -408,13 +421,22 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) { return (uint64_t(tag) << 32) | payload; }
 __device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return uint32_t(w >> 32) == tag; }
 
-// Row statistics of one item: the largest logit m, s = sum of
-// 2^(z*c - fl(m*c)) (>= 1/2 when m is finite; 1 for a greedy, skipped or
-// all -inf item, where no merge uses it), the first index of m plus one, and
-// the logit at the row's draft token if the item holds it (else 0).
+// Row statistics of one item in two words: the largest logit m with the
+// call's tag, and sx = s | v << 31 | (tag & kTag17) << 47, where
+// s = sum of 2^(z*c - fl(m*c)) (>= 1/2 when m is finite; 1 for a greedy,
+// skipped or all -inf item, where no merge uses it; positive, so its sign bit
+// is left out) and v = 1 + the first index of m within the item (0: none).
+// The host never numbers a call with tag & kTag17 == 0, so a zeroed sx never
+// looks current. (Fewer words per item matter: each is a device-coherent
+// store, and with 3 words a B = 256 call took 5 us longer.)
 struct PartialRec {
-  uint64_t m, s, idx, zg;
+  uint64_t m, sx;
 };
+constexpr uint32_t kTag17 = 0x1ffffu;
+__device__ __forceinline__ uint64_t pack_sx(float s, uint32_t v, uint32_t tag) {
+  return uint64_t(__float_as_uint(s) & 0x7fffffffu) | (uint64_t(v) << 31) | (uint64_t(tag & kTag17) << 47);
+}
+__device__ __forceinline__ bool sx_current(uint64_t w, uint32_t tag) { return uint32_t(w >> 47) == (tag & kTag17); }
 // One sequence's decision, published for its draw members.
 struct SeqRec {
   uint64_t jm;      // j | mode << 8
@@ -535,7 +557,7 @@ __device__ __forceinline__ const T* item_row(const Params& P, const Item& it) {
 // the compiler wait for every load in flight where the branches join.
 struct ItemRegs {
   uint4 x[kStatVecs];
-  uint32_t head, tail, zg;
+  uint32_t head, tail;
 };
 
 // A 16-byte load marked non-temporal (streamed through the caches). The
@@ -567,8 +589,6 @@ __device__ __forceinline__ void item_load(const Params& P, const Item& it, ItemR
     g.head = 0u;
     g.tail = 0u;
   }
-  // The draft token's logit: one scalar (read-only) load.
-  g.zg = (it.tok >= it.e0 && it.tok < it.e1) ? load_uniform_bits(row + it.tok) : 0u;
 }
 
 // Largest of three floats in one instruction. The logits are finite or
@@ -607,7 +627,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // A folded item: thread 0 holds the merged state.
 struct Partial {
-  float m, s, zg;
+  float m, s;
   int idx;
 };
 
@@ -712,9 +732,7 @@ __device__ __forceinline__ Partial wave_fold(const Params& P, const Item& it, It
     idx = it.ea + (tid + where * kThreads) * kVec + first;
   }
   if (mw != -INFINITY) idx = wave_min(idx);
-  // The logit at the row's draft token if this chunk holds it.
-  const float zg = (it.tok >= it.e0 && it.tok < it.e1) ? Logit<T>::from_bits(g.zg) : 0.0f;
-  return Partial{mw, s, zg, idx};
+  return Partial{mw, s, idx};
 }
 
 template <typename T>
@@ -742,10 +760,9 @@ __device__ __forceinline__ void partial_write(const Params& P, const Item& it, c
         acc_merge<false>(a.m, a.s, a.idx, o.m, o.s, o.idx, 0.0f);
     }
     PartialRec* p = partial_at(P, it.b, it.r, it.c);
+    const uint32_t v = (it.live && a.idx >= it.e0 && a.idx < it.e1) ? uint32_t(a.idx - it.e0 + 1) : 0u;
     put_u64(&p->m, tagged(P.tag, __float_as_uint(a.m)));
-    put_u64(&p->s, tagged(P.tag, __float_as_uint(a.s != 0.0f ? a.s : 1.0f)));
-    put_u64(&p->idx, tagged(P.tag, uint32_t(a.idx + 1)));
-    put_u64(&p->zg, tagged(P.tag, __float_as_uint(a.zg)));
+    put_u64(&p->sx, pack_sx(a.s != 0.0f ? a.s : 1.0f, v, P.tag));
   }
 }
 
@@ -800,7 +817,6 @@ struct DecideShared {
   float row_m[kMaxRows];
   double row_logz[kMaxRows];
   int row_idx[kMaxRows];
-  float row_zg[kMaxRows];
   Partial part[kStageParts];
   int tok[kMaxRows / 2];
   unsigned long long rej_mask;
@@ -848,27 +864,25 @@ struct SeqInfo {
   double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
 };
 
-// Waits (until `deadline`) for partial q of this call, then takes it and
-// zeroes its words. Returns false if the wait gave up (always, when the wait
-// bound is 0: the host's way to exercise this path).
-__device__ __forceinline__ bool take_partial(const Params& P, PartialRec* q, uint64_t deadline, Partial& out) {
+// Waits (until `deadline`) for partial q of this call (its item starts at
+// element e0 of the row), then takes it and zeroes its words. Returns false
+// if the wait gave up (always, when the wait bound is 0: the host's way to
+// exercise this path).
+__device__ __forceinline__ bool take_partial(const Params& P, PartialRec* q, int e0, uint64_t deadline,
+                                             Partial& out) {
   const uint32_t tag = P.tag;
-  uint64_t m = get_u64(&q->m), s = get_u64(&q->s), i = get_u64(&q->idx), z = get_u64(&q->zg);
-  auto ready = [&] { return has_tag(m, tag) && has_tag(s, tag) && has_tag(i, tag) && has_tag(z, tag); };
+  uint64_t m = get_u64(&q->m), x = get_u64(&q->sx);
+  auto ready = [&] { return has_tag(m, tag) && sx_current(x, tag); };
   while (!ready() && before(deadline)) {
     __builtin_amdgcn_s_sleep(4);
     if (!has_tag(m, tag)) m = get_u64(&q->m);
-    if (!has_tag(s, tag)) s = get_u64(&q->s);
-    if (!has_tag(i, tag)) i = get_u64(&q->idx);
-    if (!has_tag(z, tag)) z = get_u64(&q->zg);
+    if (!sx_current(x, tag)) x = get_u64(&q->sx);
   }
   const bool ok = P.wait_ticks != 0 && ready();
   put_u64(&q->m, 0);
-  put_u64(&q->s, 0);
-  put_u64(&q->idx, 0);
-  put_u64(&q->zg, 0);
-  out = Partial{__uint_as_float(uint32_t(m)), __uint_as_float(uint32_t(s)), __uint_as_float(uint32_t(z)),
-                int(uint32_t(i) - 1u)};
+  put_u64(&q->sx, 0);
+  const uint32_t v = uint32_t(x >> 31) & 0xffffu;
+  out = Partial{__uint_as_float(uint32_t(m)), __uint_as_float(uint32_t(x) & 0x7fffffffu), v ? e0 + int(v) - 1 : INT_MAX};
   return ok;
 }
 
@@ -908,8 +922,14 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   if (tid < N) ds.tok[tid] = d;
   bool bad = !temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab));
   if (P.flags & kDebug) bad = bad || (tid < N && !(ua >= 0.0f && ua < 1.0f)) || (t > 0.0f && !(us >= 0.0f && us < 1.0f));
-  const bool any_bad = block_any(bad);
   const bool greedy = (t == 0.0f);
+  // Thread i < N: the logits of draft token d_i in draft row i and target
+  // row i (requested now; used by the accept test).
+  float zt = 0.0f, zd = 0.0f;
+  if (tid < N && !greedy && d >= 0 && d < P.vocab) {
+    zt = Logit<T>::at(static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + tid) * P.vocab, d);
+    zd = Logit<T>::at(static_cast<const T*>(P.draft) + (int64_t(b) * N + tid) * P.vocab, d);
+  }
   const bool draws = has_draw_members(t);  // draw members wait for this decision
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
@@ -920,18 +940,22 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
   const uint64_t deadline = deadline_after(P.wait_ticks);
-  bool timed_out = false;
+  bool timed_out = false, any_bad = false;
   for (int rg = 0; rg < R; rg += rows_per_group) {
     const int nr = min(rows_per_group, R - rg);
     const int np = nr * pr;
     bool late = false;
     if (tid < np) {
       Partial q;
-      late = !take_partial(P, part_b + int64_t(rg) * pr + tid, deadline, q);
+      late = !take_partial(P, part_b + int64_t(rg) * pr + tid, (tid % pr) * P.chunk, deadline, q);
       ds.part[tid] = q;
     }
-    // (also the barrier that makes the group's partials visible)
-    timed_out = block_any(late) || timed_out;
+    // (also the barrier that makes the group's partials visible); the input
+    // checks join the first group's vote, so the partials are requested
+    // before anything waits for the draft tokens.
+    const int vote = block_any2(rg == 0 && bad, late);
+    any_bad = any_bad || (vote & 1);
+    timed_out = timed_out || (vote & 2);
     if (any_bad || timed_out) continue;
     if (rg == 0) trace(2, 4);
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
@@ -966,8 +990,6 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        // The item holding the draft token carries its logit.
-        ds.row_zg[r] = (r < 2 * N) ? ds.part[rr * pr + ds.tok[r < N ? r : r - N] / P.chunk].zg : 0.0f;
         lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
         amax[r] = idx;
       }
@@ -1001,8 +1023,6 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
 
   bool accept = true;
   if (tid < N) {
-    const float zt = ds.row_zg[N + tid];
-    const float zd = ds.row_zg[tid];
     if (greedy) {
       accept = (d == ds.row_idx[N + tid]);
     } else if (zd == -INFINITY) {
@@ -1553,7 +1573,7 @@ __device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
   trace_set(unsigned(b) * unsigned(P.items_per_seq + 1) + unsigned(idx));
   trace(2, 0);
   const Item it = item_at<T>(P, int64_t(b) * P.items_per_seq + idx);
-  Partial q{-INFINITY, 0.0f, 0.0f, INT_MAX - 1};
+  Partial q{-INFINITY, 0.0f, INT_MAX - 1};
   if (it.live) {
     ItemRegs g;
     item_load<T>(P, it, g);
