@@ -64,6 +64,7 @@ enum specv_status {
   SPECV_EHIP = -3,   /* a HIP runtime call or kernel launch failed */
   SPECV_EALIGN = -4, /* a device pointer is not aligned as required */
   SPECV_ESTATE = -5, /* specv_row_stats before any successful specv_verify */
+  SPECV_ERANGE = -6, /* specv_verify_static: a size beyond its static workspace */
 };
 
 /* Largest n_draft a handle accepts (one 64-lane wavefront holds a sequence's decisions). */
@@ -167,6 +168,31 @@ SPECV_API int specv_set_wait_limit(specv_handle h, int64_t microseconds);
 SPECV_API int specv_set_timing(specv_handle h, int enable);
 SPECV_API int specv_last_timings(specv_handle h, float* ms, int capacity, int* count);
 SPECV_API const char* specv_stage_name(int stage);
+
+/*
+ * specv_verify without a handle and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Arguments, layouts and results are
+ * those of specv_verify, on the current HIP device; `vocab` and `dtype` are
+ * passed per call.
+ * Its workspace is a fixed device array inside the library (about 8 MB on
+ * each GPU it runs on, held until the process ends), cleared by a kernel on
+ * `stream` before the first call on each device; the first call also looks up
+ * that array's device address. Limits: batch <= 256, n_draft <= 16,
+ * vocab <= SPECV_MAX_VOCAB; beyond them it returns SPECV_ERANGE. Every call on
+ * one GPU shares that array: calls that overlap on one GPU (on different
+ * streams, or from several host threads) race and must not be issued;
+ * successive calls on one stream are fine. Waits use the default bound
+ * (specv_set_wait_limit has no effect here); SPECV_DEBUG is read at the first
+ * call on each device.
+ * Errors (nothing enqueued): SPECV_EINVAL (batch < 0, n_draft < 1, vocab < 1,
+ * bad dtype, null pointer), SPECV_ERANGE, SPECV_EALIGN, SPECV_EHIP.
+ */
+SPECV_API int specv_verify_static(int batch, int n_draft, int vocab, specv_dtype dtype, const void* draft_logits,
+                                  const void* target_logits, const int32_t* draft_tokens,
+                                  const float* accept_uniforms, const float* sample_uniforms,
+                                  const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted,
+                                  void* stream);
 
 /* Release the handle and its workspace (synchronises the handle's device first). NULL is ignored. */
 SPECV_API void specv_destroy(specv_handle h);

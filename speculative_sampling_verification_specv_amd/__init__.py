@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     SPECV_EHIP,
     SPECV_EINVAL,
     SPECV_ENOMEM,
+    SPECV_ERANGE,
     SPECV_ESTATE,
     SPECV_F32,
     SPECV_MAX_DRAFT,
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     specv_stage_name,
     specv_strerror,
     specv_verify,
+    specv_verify_static,
 )
 
 __all__ = [
@@ -34,6 +36,7 @@ __all__ = [
     "load_library",
     "specv_create",
     "specv_verify",
+    "specv_verify_static",
     "specv_row_stats",
     "specv_destroy",
     "specv_strerror",

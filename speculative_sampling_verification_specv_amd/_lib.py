@@ -21,6 +21,7 @@ SPECV_ENOMEM = -2
 SPECV_EHIP = -3
 SPECV_EALIGN = -4
 SPECV_ESTATE = -5
+SPECV_ERANGE = -6
 SPECV_MAX_DRAFT = 64
 SPECV_MAX_VOCAB = 1 << 18
 
@@ -29,6 +30,8 @@ _SIGNATURES = {
     "specv_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int]),
     "specv_verify": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 9),
+    "specv_verify_static": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                            + [ctypes.c_void_p] * 9),
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "specv_destroy": (None, [ctypes.c_void_p]),
     "specv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -104,6 +107,24 @@ def specv_verify(handle: int, draft_logits, target_logits, draft_tokens, accept_
         handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
         _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device)), "specv_verify")
+
+
+def specv_verify_static(draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms, temperature,
+                        out_tokens, out_n_accepted, stream=None) -> None:
+    """Enqueue one verification through the allocation-free entry point (no handle).
+
+    batch and n_draft come from draft_tokens' shape, the vocabulary from the
+    logits' last dimension and the dtype from theirs; the tensors' layouts are
+    those of specv_verify (the caller checks them)."""
+    import torch
+
+    B, N = draft_tokens.shape
+    V = int(target_logits.shape[-1])
+    dtype = SPECV_F32 if target_logits.dtype == torch.float32 else SPECV_BF16
+    _check(load_library().specv_verify_static(
+        int(B), int(N), V, dtype, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
+        _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
+        _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device)), "specv_verify_static")
 
 
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:

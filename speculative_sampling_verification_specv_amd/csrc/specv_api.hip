@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -75,39 +77,14 @@ uint32_t next_call_tag(uint32_t tag) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-const char* specv_strerror(int code) {
-  switch (code) {
-    case SPECV_OK: return "success";
-    case SPECV_EINVAL: return "invalid argument";
-    case SPECV_ENOMEM: return "device memory allocation failed";
-    case SPECV_EHIP: return "HIP runtime error or kernel launch failure";
-    case SPECV_EALIGN: return "device pointer misaligned";
-    case SPECV_ESTATE: return "no successful specv_verify on this handle yet";
-    default: return "unknown specv status code";
-  }
-}
-
-int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, specv_dtype dtype, int device) {
-  if (out == nullptr) return SPECV_EINVAL;
-  *out = nullptr;
-  if (max_batch < 1 || max_draft < 1 || max_draft > SPECV_MAX_DRAFT) return SPECV_EINVAL;
-  if (vocab < 1 || vocab > specv::kMaxVocab) return SPECV_EINVAL;
-  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
-  int n_dev = 0;
-  if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
-  if (device < 0 || device >= n_dev) return SPECV_EINVAL;
-
+// Lays out a workspace for calls up to (max_batch, max_draft) at `vocab` and
+// `dtype` from `base` (which may be null to only size it); returns its size
+// in bytes. The regions are 256-byte aligned if `base` is.
+size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char* base, specv::Workspace* ws) {
   const int chunk = specv::stat_chunk_elems(dtype);
   const int nch = specv::ceil_div(vocab, chunk);
   const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
   const size_t rows = size_t(max_batch) * size_t(2 * max_draft + 1);
-  // Grid: one workgroup per row-statistics item, per decision and per draw member.
-  if (int64_t(rows) * nch + int64_t(max_batch) * (nm + 1) >= (int64_t(1) << 31)) return SPECV_EINVAL;
-
   size_t off = 0;
   const size_t off_partials = off;
   off = align_up(off + rows * nch * specv::partial_bytes(), 256);
@@ -121,6 +98,57 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, spe
   off = align_up(off + rows * sizeof(int), 256);
   const size_t off_counters = off;
   off = align_up(off + size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
+  if (ws != nullptr) {
+    ws->partials = base + off_partials;
+    ws->seq = base + off_seq;
+    ws->records = base + off_records;
+    ws->row_lse = reinterpret_cast<float*>(base + off_lse);
+    ws->row_argmax = reinterpret_cast<int*>(base + off_argmax);
+    ws->draw_done = reinterpret_cast<int*>(base + off_counters);
+    ws->n_stat_chunks = nch;
+    ws->n_members = nm;
+    ws->stat_chunk = chunk;
+  }
+  return off;
+}
+
+// Whether a launch of (batch, n_draft) at `vocab` and `dtype` has a grid the
+// runtime takes (one workgroup per row-statistics item, decision and draw
+// member, below 2^31).
+bool grid_fits(int batch, int n_draft, int vocab, int dtype) {
+  const int64_t nch = specv::ceil_div(vocab, specv::stat_chunk_elems(dtype));
+  const int64_t nm = specv::ceil_div(vocab, specv::member_elems(dtype));
+  return int64_t(batch) * (2 * n_draft + 1) * nch + int64_t(batch) * (nm + 1) < (int64_t(1) << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* specv_strerror(int code) {
+  switch (code) {
+    case SPECV_OK: return "success";
+    case SPECV_EINVAL: return "invalid argument";
+    case SPECV_ENOMEM: return "device memory allocation failed";
+    case SPECV_EHIP: return "HIP runtime error or kernel launch failure";
+    case SPECV_EALIGN: return "device pointer misaligned";
+    case SPECV_ESTATE: return "no successful specv_verify on this handle yet";
+    case SPECV_ERANGE: return "size beyond the static workspace of specv_verify_static (batch <= 256, n_draft <= 16)";
+    default: return "unknown specv status code";
+  }
+}
+
+int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, specv_dtype dtype, int device) {
+  if (out == nullptr) return SPECV_EINVAL;
+  *out = nullptr;
+  if (max_batch < 1 || max_draft < 1 || max_draft > SPECV_MAX_DRAFT) return SPECV_EINVAL;
+  if (vocab < 1 || vocab > specv::kMaxVocab) return SPECV_EINVAL;
+  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
+  int n_dev = 0;
+  if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
+  if (device < 0 || device >= n_dev) return SPECV_EINVAL;
+  if (!grid_fits(max_batch, max_draft, vocab, dtype)) return SPECV_EINVAL;
+  const size_t off = layout_workspace(max_batch, max_draft, vocab, dtype, nullptr, nullptr);
 
   DeviceGuard guard(device);
   if (!guard.ok()) return SPECV_EHIP;
@@ -131,22 +159,13 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, spe
     delete h;
     return SPECV_ENOMEM;
   }
-  char* base = static_cast<char*>(h->mem);
   h->device = device;
   h->max_batch = max_batch;
   h->max_draft = max_draft;
   h->vocab = vocab;
   h->dtype = dtype;
   h->mem_bytes = off;
-  h->ws.partials = base + off_partials;
-  h->ws.seq = base + off_seq;
-  h->ws.records = base + off_records;
-  h->ws.row_lse = reinterpret_cast<float*>(base + off_lse);
-  h->ws.row_argmax = reinterpret_cast<int*>(base + off_argmax);
-  h->ws.draw_done = reinterpret_cast<int*>(base + off_counters);
-  h->ws.n_stat_chunks = nch;
-  h->ws.n_members = nm;
-  h->ws.stat_chunk = chunk;
+  layout_workspace(max_batch, max_draft, vocab, dtype, static_cast<char*>(h->mem), &h->ws);
   h->ws.resident_blocks = specv::max_resident_blocks(dtype);
   if (h->ws.resident_blocks < 1 || hipMemset(h->mem, 0, off) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->mem);
@@ -290,3 +309,132 @@ void specv_destroy(specv_handle h) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// specv_verify_static: the same verification with no handle and no
+// allocation. Its workspace is `scratch`, a device array of this file (one
+// copy per GPU, held until the process ends), laid out once for the largest
+// call it takes; the kernels receive its device address as they receive a
+// handle's workspace.
+
+namespace {
+
+constexpr int kStaticMaxBatch = 256;
+constexpr int kStaticMaxDraft = 16;
+// layout_workspace(256, 16, 2^18, float32) = 8071168 bytes; checked at set-up.
+constexpr size_t kStaticBytes = size_t(8) << 20;
+constexpr int kStaticMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+namespace {
+
+// Fills n 16-byte words with zeros (once per device, before the first call).
+__global__ void zero_words(uint4* p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct StaticDevice {
+  std::atomic<int> ready{0};
+  char* ptr = nullptr;  // device address of `scratch` on this device
+  int resident[2] = {0, 0};
+  uint64_t wait_ticks = 0;
+  uint32_t debug = 0;
+  std::atomic<uint32_t> tag{1};
+};
+StaticDevice g_static[kStaticMaxDevices];
+std::mutex g_static_mu;
+
+uint32_t take_tag(std::atomic<uint32_t>& t) {
+  uint32_t cur = t.load(std::memory_order_relaxed);
+  while (!t.compare_exchange_weak(cur, next_call_tag(cur), std::memory_order_relaxed)) {
+  }
+  return cur;
+}
+
+// Once per device, with that device current: the array's device address, the
+// launch parameters, and the array cleared on `stream` (ahead of the call
+// that set it up).
+int static_setup(int dev, hipStream_t stream) {
+  StaticDevice& sd = g_static[dev];
+  if (sd.ready.load(std::memory_order_acquire)) return SPECV_OK;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (sd.ready.load(std::memory_order_relaxed)) return SPECV_OK;
+  if (layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, nullptr, nullptr) >
+      kStaticBytes)
+    return SPECV_EHIP;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return SPECV_EHIP;
+  }
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return SPECV_EHIP;
+  const int r0 = specv::max_resident_blocks(SPECV_F32), r1 = specv::max_resident_blocks(SPECV_BF16);
+  if (r0 < 1 || r1 < 1) return SPECV_EHIP;
+  hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, static_cast<uint4*>(ptr), kStaticBytes / 16);
+  if (hipGetLastError() != hipSuccess) return SPECV_EHIP;
+  sd.ptr = static_cast<char*>(ptr);
+  sd.resident[SPECV_F32] = r0;
+  sd.resident[SPECV_BF16] = r1;
+  sd.wait_ticks = uint64_t(kDefaultWaitUs) * uint64_t(khz) / 1000u;
+  const char* dbg = getenv("SPECV_DEBUG");
+  sd.debug = (dbg != nullptr && dbg[0] != '\0' && strcmp(dbg, "0") != 0) ? 1u : 0u;
+  sd.ready.store(1, std::memory_order_release);
+  return SPECV_OK;
+}
+
+}  // namespace
+
+extern "C" int specv_verify_static(int batch, int n_draft, int vocab, specv_dtype dtype, const void* draft_logits,
+                                   const void* target_logits, const int32_t* draft_tokens,
+                                   const float* accept_uniforms, const float* sample_uniforms,
+                                   const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted,
+                                   void* stream) {
+  if (batch < 0 || n_draft < 1 || vocab < 1) return SPECV_EINVAL;
+  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_EINVAL;
+  if (batch > kStaticMaxBatch || n_draft > kStaticMaxDraft || vocab > specv::kMaxVocab) return SPECV_ERANGE;
+  if (batch == 0) return SPECV_OK;
+  if (!draft_logits || !target_logits || !draft_tokens || !accept_uniforms || !sample_uniforms || !temperature ||
+      !out_tokens || !out_n_accepted)
+    return SPECV_EINVAL;
+  if (!aligned(draft_logits, 16) || !aligned(target_logits, 16)) return SPECV_EALIGN;
+  if (!aligned(draft_tokens, 4) || !aligned(accept_uniforms, 4) || !aligned(sample_uniforms, 4) ||
+      !aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(out_n_accepted, 4))
+    return SPECV_EALIGN;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) return SPECV_EHIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rc = static_setup(dev, s);
+  if (rc != SPECV_OK) return rc;
+  StaticDevice& sd = g_static[dev];
+  // Every region at the offset of the largest layout, whatever this call's
+  // vocabulary, so the counters always sit where the last call left them at 0.
+  specv::Workspace ws;
+  layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, sd.ptr, &ws);
+  ws.stat_chunk = specv::stat_chunk_elems(dtype);
+  ws.n_stat_chunks = specv::ceil_div(vocab, ws.stat_chunk);
+  ws.n_members = specv::ceil_div(vocab, specv::member_elems(dtype));
+  ws.resident_blocks = sd.resident[dtype];
+  specv::VerifyArgs a;
+  a.batch = batch;
+  a.n_draft = n_draft;
+  a.vocab = vocab;
+  a.dtype = dtype;
+  a.draft = draft_logits;
+  a.target = target_logits;
+  a.tokens = draft_tokens;
+  a.accept_u = accept_uniforms;
+  a.sample_u = sample_uniforms;
+  a.temperature = temperature;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n_accepted;
+  a.tag = take_tag(sd.tag);
+  a.debug = sd.debug;
+  a.wait_ticks = sd.wait_ticks;
+  int stages = 0;
+  return specv::launch_verify(a, ws, s, nullptr, &stages) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}

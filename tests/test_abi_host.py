@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
-                                          "specv_stage_name", "specv_set_wait_limit"}
+                                          "specv_stage_name", "specv_set_wait_limit",
+                                          "specv_verify_static"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_codes_match_header():
     text = _header_text()
-    for name in ("SPECV_OK", "SPECV_EINVAL", "SPECV_ENOMEM", "SPECV_EHIP", "SPECV_EALIGN", "SPECV_ESTATE",
+    for name in ("SPECV_OK", "SPECV_EINVAL", "SPECV_ENOMEM", "SPECV_EHIP", "SPECV_EALIGN", "SPECV_ESTATE", "SPECV_ERANGE",
                  "SPECV_F32", "SPECV_BF16"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m, name
@@ -54,7 +55,7 @@ def test_status_codes_match_header():
 
 def test_strerror_covers_codes():
     seen = set()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = specv.specv_strerror(code)
         assert s and s not in seen
         seen.add(s)
@@ -75,6 +76,16 @@ def test_argument_errors_before_any_device_call():
     lib.specv_destroy(None)  # no-op
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
     assert lib.specv_set_wait_limit(None, 10) == _lib.SPECV_EINVAL
+    # The allocation-free entry point checks sizes before touching a device.
+    nine = [None] * 9
+    assert lib.specv_verify_static(-1, 1, 16, 0, *nine) == _lib.SPECV_EINVAL
+    assert lib.specv_verify_static(1, 0, 16, 0, *nine) == _lib.SPECV_EINVAL
+    assert lib.specv_verify_static(1, 1, 16, 2, *nine) == _lib.SPECV_EINVAL
+    assert lib.specv_verify_static(257, 1, 16, 0, *nine) == _lib.SPECV_ERANGE
+    assert lib.specv_verify_static(1, 17, 16, 0, *nine) == _lib.SPECV_ERANGE
+    assert lib.specv_verify_static(1, 1, _lib.SPECV_MAX_VOCAB + 1, 1, *nine) == _lib.SPECV_ERANGE
+    assert lib.specv_verify_static(0, 1, 16, 0, *nine) == _lib.SPECV_OK
+    assert lib.specv_verify_static(1, 1, 16, 0, *nine) == _lib.SPECV_EINVAL  # null pointers
     n = ctypes.c_int()
     assert lib.specv_last_timings(None, (ctypes.c_float * 4)(), 4, ctypes.byref(n)) == _lib.SPECV_EINVAL
     assert specv.specv_stage_name(0) == "verify"
