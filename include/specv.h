@@ -130,7 +130,28 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
                  int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
 
 /*
- * Diagnostics of the most recent specv_verify on this handle: for every
+ * Draw one token from each of n_rows rows of logits (the draft model's step
+ * before verification: lesson "추측 디코딩 — 초안 작성, 검증, 반복",
+ * section "핵심 알고리즘(Core algorithm)" step 2, and the draft loop of its
+ * "Step 3"): token r ~ softmax(logits[r] / temperature[r]) by the same inverse
+ * CDF as every other draw (the smallest k with C_k > uniforms[r] * S, fp64
+ * weights), or the first argmax where temperature[r] = 0.
+ *   logits       [n_rows][V]  the handle's dtype; 16-byte aligned (device)
+ *   temperature  [n_rows]     float32, as for specv_verify (device)
+ *   uniforms     [n_rows]     float32 in [0, 1) (device)
+ *   out_tokens   [n_rows]     int32, written: the drawn token, or -1 where the
+ *                             temperature is invalid (-2 as for specv_verify)
+ * 0 <= n_rows <= the handle's max_batch; V is the handle's vocabulary.
+ * Asynchronous on `stream` like specv_verify; specv_row_stats afterwards
+ * gives each row's log-normaliser and argmax ([n_rows][1]).
+ * Errors (nothing enqueued): SPECV_EINVAL, SPECV_EALIGN, SPECV_EHIP.
+ */
+SPECV_API int specv_sample(specv_handle h, int n_rows, const void* logits, const float* temperature,
+                           const float* uniforms, int32_t* out_tokens, void* stream);
+
+/*
+ * Diagnostics of the most recent specv_verify (or specv_sample, with
+ * n_draft = 0) on this handle: for every
  * sequence b and row r (draft rows 0..n_draft-1, then target rows 0..n_draft),
  *   out_lse    [batch][2*n_draft+1] float32: log sum_x exp(z_x / T), the row's
  *              tempered log-normaliser (lesson, "Core algorithm" step 2-3

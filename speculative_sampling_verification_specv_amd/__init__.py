@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     specv_destroy,
     specv_last_timings,
     specv_row_stats,
+    specv_sample,
     specv_set_timing,
     specv_set_wait_limit,
     specv_stage_name,
@@ -38,6 +39,7 @@ __all__ = [
     "specv_verify",
     "specv_verify_static",
     "specv_row_stats",
+    "specv_sample",
     "specv_destroy",
     "specv_strerror",
 ]

@@ -33,6 +33,7 @@ _SIGNATURES = {
     "specv_verify_static": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
                             + [ctypes.c_void_p] * 9),
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "specv_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
     "specv_destroy": (None, [ctypes.c_void_p]),
     "specv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "specv_set_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -125,6 +126,13 @@ def specv_verify_static(draft_logits, target_logits, draft_tokens, accept_unifor
         int(B), int(N), V, dtype, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
         _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device)), "specv_verify_static")
+
+
+def specv_sample(handle: int, logits, temperature, uniforms, out_tokens, stream=None) -> None:
+    """Enqueue one draw per row of logits [n_rows, V]."""
+    n = int(logits.shape[0])
+    _check(load_library().specv_sample(handle, n, _ptr(logits), _ptr(temperature), _ptr(uniforms), _ptr(out_tokens),
+                                       _stream_ptr(stream, logits.device)), "specv_sample")
 
 
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:
@@ -251,6 +259,21 @@ class Verifier:
                 raise SpecvError(rc, "specv_verify")
 
         return call
+
+    def sample(self, logits, temperature, uniforms, out_tokens=None, stream=None):
+        """Draw one token per row of logits [n_rows, V]; returns out_tokens [n_rows] int32."""
+        import torch
+
+        n = int(logits.shape[0])
+        self._expect(logits, "logits", (n, self.vocab), self.torch_dtype)
+        self._expect(temperature, "temperature", (n,), torch.float32)
+        self._expect(uniforms, "uniforms", (n,), torch.float32)
+        if out_tokens is None:
+            out_tokens = torch.empty((n,), dtype=torch.int32, device=self.device)
+        self._expect(out_tokens, "out_tokens", (n,), torch.int32)
+        specv_sample(self.handle, logits, temperature, uniforms, out_tokens, stream)
+        self._last = (n, 0)
+        return out_tokens
 
     def set_timing(self, enable: bool) -> None:
         specv_set_timing(self.handle, enable)

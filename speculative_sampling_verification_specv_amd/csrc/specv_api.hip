@@ -238,6 +238,47 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   return SPECV_OK;
 }
 
+int specv_sample(specv_handle h, int n_rows, const void* logits, const float* temperature, const float* uniforms,
+                 int32_t* out_tokens, void* stream) {
+  if (h == nullptr) return SPECV_EINVAL;
+  if (n_rows < 0 || n_rows > h->max_batch) return SPECV_EINVAL;
+  if (n_rows == 0) return SPECV_OK;
+  if (!logits || !temperature || !uniforms || !out_tokens) return SPECV_EINVAL;
+  if (!aligned(logits, 16)) return SPECV_EALIGN;
+  if (!aligned(temperature, 4) || !aligned(uniforms, 4) || !aligned(out_tokens, 4)) return SPECV_EALIGN;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return SPECV_EHIP;
+  // The verification with no drafts: each row is a sequence's only verifier
+  // row, so its draw is the bonus draw from softmax(row / T) (the argmax at
+  // T = 0); nothing reads drafts, draft tokens or accept uniforms.
+  specv::VerifyArgs a;
+  a.batch = n_rows;
+  a.n_draft = 0;
+  a.vocab = h->vocab;
+  a.dtype = h->dtype;
+  a.draft = logits;
+  a.target = logits;
+  a.tokens = nullptr;
+  a.accept_u = nullptr;
+  a.sample_u = uniforms;
+  a.temperature = temperature;
+  a.out_tokens = out_tokens;
+  a.out_n = nullptr;
+  a.tag = h->next_tag;
+  a.debug = h->debug;
+  a.wait_ticks = h->wait_ticks;
+  int stages = 0;
+  if (specv::launch_verify(a, h->ws, static_cast<hipStream_t>(stream), h->timing ? h->events : nullptr, &stages) !=
+      hipSuccess)
+    return SPECV_EHIP;
+  h->next_tag = next_call_tag(h->next_tag);
+  h->last_batch = n_rows;
+  h->last_n_draft = 0;
+  h->timed_call = h->timing;
+  h->timed_stages = stages;
+  return SPECV_OK;
+}
+
 int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream) {
   if (h == nullptr || out_lse == nullptr || out_argmax == nullptr) return SPECV_EINVAL;
   if (!aligned(out_lse, 4) || !aligned(out_argmax, 4)) return SPECV_EALIGN;

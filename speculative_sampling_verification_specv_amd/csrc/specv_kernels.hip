@@ -914,9 +914,10 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const int pr = P.nch;  // partials per row
   const int rows_per_group = max(1, kStageParts / pr);
   PartialRec* part_b = P.partials + int64_t(b) * R * pr;
-  const int ti = min(tid, N - 1);
-  const int d = tok[ti];
-  const float ua = P.accept_u[int64_t(b) * N + ti];
+  // (n_draft = 0 is the plain draw from one row: no draft tokens, no uniforms to test)
+  const int ti = min(tid, max(N - 1, 0));
+  const int d = N > 0 ? tok[ti] : 0;
+  const float ua = N > 0 ? P.accept_u[int64_t(b) * N + ti] : 0.0f;
   const float t = load_uniform(P.temperature + b);
   const float us = load_uniform(P.sample_u + b);
   if (tid < N) ds.tok[tid] = d;
@@ -1009,7 +1010,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
       if (tid == 0) publish(P, b, any_bad ? kModeInvalid : kModeFailed, 0, 0.0f, 0.0f, 0.0);
     } else {
       for (int i = tid; i <= N; i += kThreads) otok[i] = code;
-      if (tid == 0) P.out_n[b] = code;
+      if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
     }
     return;
   }
@@ -1059,7 +1060,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     else if (greedy)
       otok[i] = ds.row_idx[N + j];
   }
-  if (tid == 0 && greedy) P.out_n[b] = j;
+  if (tid == 0 && greedy && P.out_n != nullptr) P.out_n[b] = j;
 }
 
 // ---------------------------------------------------------------------------
@@ -1078,7 +1079,7 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params& P, int b, const S
   const int N = P.n_draft;
   DrawRows<T> d;
   d.trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + s.j) * P.vocab;
-  d.drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab;
+  d.drow = N > 0 ? static_cast<const T*>(P.draft) + (int64_t(b) * N + min(s.j, N - 1)) * P.vocab : d.trow;
   d.inv_t = 1.0 / double(s.temp);
   d.nmt = -double(s.m_target) * d.inv_t;
   d.nmd = -double(s.m_draft) * d.inv_t;
@@ -1459,7 +1460,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     const int code = s.mode == kModeInvalid ? -1 : -2;
     int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
     for (int i = tid; i <= P.n_draft; i += kThreads) otok[i] = code;
-    if (tid == 0) P.out_n[b] = code;
+    if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
     return;
   }
   const DrawRows<T> d = draw_rows<T>(P, b, s);
@@ -1553,7 +1554,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (lane == 0) {
       const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
       P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
-      P.out_n[b] = s.j;
+      if (P.out_n != nullptr) P.out_n[b] = s.j;
     }
   }
 }

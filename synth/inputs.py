@@ -39,6 +39,8 @@ __all__ = [
     "make_batch",
     "make_trials",
     "resample",
+    "SampleRows",
+    "make_sample_rows",
     "widen",
     "to_bf16_bits",
     "gumbel_max_tokens",
@@ -250,3 +252,25 @@ def resample(batch: Batch, wl: Workload, seed: int, variant: int) -> Batch:
         tokens[b] = gumbel_max_tokens(widen(batch.draft_logits[b], batch.dtype), float(batch.temperature[b]), rng)
     return Batch(batch.dtype, batch.draft_logits, batch.target_logits, tokens, grid_uniforms(rng, (B, N)),
                  grid_uniforms(rng, (B,)), batch.temperature)
+
+
+@dataclass
+class SampleRows:
+    """Host arrays of one draft-side draw: rows of logits, a temperature and a uniform per row."""
+
+    dtype: str
+    logits: np.ndarray  # [n, V] float32 or uint16 bfloat16 bits
+    temperature: np.ndarray  # [n] float32
+    uniforms: np.ndarray  # [n] float32 in [0, 1)
+
+
+def make_sample_rows(wl: Workload, seed: int, n_rows: int) -> SampleRows:
+    """``n_rows`` draft-model rows of workload ``wl`` (its draft logits, position
+    after position, sequence after sequence) with the sequences' temperatures
+    and fresh uniforms."""
+    rng = np.random.default_rng(np.random.SeedSequence([wl.index, int(seed), 2]))
+    B = -(-n_rows // wl.n_draft)
+    b = make_batch(wl.with_sizes(batch=B), seed)
+    logits = np.ascontiguousarray(b.draft_logits.reshape(B * wl.n_draft, wl.vocab)[:n_rows])
+    temps = np.repeat(b.temperature, wl.n_draft)[:n_rows].astype(np.float32)
+    return SampleRows(wl.dtype, logits, temps, grid_uniforms(rng, (n_rows,)))

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
                                           "specv_stage_name", "specv_set_wait_limit",
-                                          "specv_verify_static"}
+                                          "specv_verify_static", "specv_sample"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,6 +73,7 @@ def test_argument_errors_before_any_device_call():
     null = [None] * 9
     assert lib.specv_verify(None, 1, 1, *null) == _lib.SPECV_EINVAL
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
+    assert lib.specv_sample(None, 1, None, None, None, None, None) == _lib.SPECV_EINVAL
     lib.specv_destroy(None)  # no-op
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
     assert lib.specv_set_wait_limit(None, 10) == _lib.SPECV_EINVAL
