@@ -215,6 +215,36 @@ SPECV_API int specv_verify_static(int batch, int n_draft, int vocab, specv_dtype
                                   const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted,
                                   void* stream);
 
+/*
+ * Commit the accepted drafts' KV entries after a verification (lesson
+ * "추측 디코딩 — 초안 작성, 검증, 반복", section "KV 캐시 처리(KV cache dance)"
+ * and exercise 4): the verifier's pass wrote one entry per draft into a
+ * scratch area; for each sequence b with n = n_accepted[b] in [0, n_draft] and
+ * cache_len[b] + n <= max_len, scratch entries 0..n-1 of every plane are copied
+ * to cache entries cache_len[b] .. cache_len[b]+n-1 and out_cache_len[b] =
+ * cache_len[b] + n; any other sequence (n_accepted -1 or -2 from an invalid or
+ * failed verification, or entries that would not fit) is left as it is and
+ * gets out_cache_len[b] = -1. Cache entries past the new length are not
+ * touched. Needs no handle and allocates nothing.
+ *   cache    device bytes: entry (p, b, t) at cache + p*cache_plane_stride
+ *            + b*cache_seq_stride + t*entry_bytes, for t < max_len
+ *   scratch  device bytes: entry (p, b, t) at scratch + p*scratch_plane_stride
+ *            + b*scratch_seq_stride + t*entry_bytes, for t < n_draft
+ *   n_accepted, cache_len, out_cache_len: device int32 [batch]
+ * A plane is one contiguous [len][entry] array, e.g. the keys or the values
+ * of one layer; an entry is entry_bytes bytes (heads * head_dim * element
+ * size). n_planes = 0 only computes the new lengths (caches the verifier
+ * wrote in place need nothing else). entry_bytes, the strides and the cache
+ * and scratch bases must be multiples of 16 bytes; the two areas must not
+ * overlap, and out_cache_len must not alias cache_len. Asynchronous on
+ * `stream`. Errors (nothing enqueued): SPECV_EINVAL (negative sizes,
+ * n_draft < 1, entry_bytes < 16, null pointers), SPECV_EALIGN, SPECV_EHIP.
+ */
+SPECV_API int specv_kv_commit(int n_planes, int batch, int n_draft, int max_len, int64_t entry_bytes, void* cache,
+                              int64_t cache_plane_stride, int64_t cache_seq_stride, const void* scratch,
+                              int64_t scratch_plane_stride, int64_t scratch_seq_stride, const int32_t* n_accepted,
+                              const int32_t* cache_len, int32_t* out_cache_len, void* stream);
+
 /* Release the handle and its workspace (synchronises the handle's device first). NULL is ignored. */
 SPECV_API void specv_destroy(specv_handle h);
 

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     load_library,
     specv_create,
     specv_destroy,
+    specv_kv_commit,
     specv_last_timings,
     specv_row_stats,
     specv_sample,
@@ -41,5 +42,6 @@ __all__ = [
     "specv_row_stats",
     "specv_sample",
     "specv_destroy",
+    "specv_kv_commit",
     "specv_strerror",
 ]

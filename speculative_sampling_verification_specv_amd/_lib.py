@@ -34,6 +34,10 @@ _SIGNATURES = {
                             + [ctypes.c_void_p] * 9),
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "specv_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
+    "specv_kv_commit": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "specv_destroy": (None, [ctypes.c_void_p]),
     "specv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "specv_set_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -133,6 +137,35 @@ def specv_sample(handle: int, logits, temperature, uniforms, out_tokens, stream=
     n = int(logits.shape[0])
     _check(load_library().specv_sample(handle, n, _ptr(logits), _ptr(temperature), _ptr(uniforms), _ptr(out_tokens),
                                        _stream_ptr(stream, logits.device)), "specv_sample")
+
+
+def specv_kv_commit(cache, cache_len, scratch, n_accepted, out_cache_len, stream=None) -> None:
+    """Enqueue the KV-cache commit of the accepted drafts.
+
+    cache [P, B, L, ...] and scratch [P, B, N, ...] are device tensors of one
+    dtype whose trailing dimensions (one entry) match; each (plane, sequence)
+    slice must be contiguous. cache_len, n_accepted, out_cache_len: int32 [B].
+    """
+    if cache.dtype != scratch.dtype or tuple(cache.shape[3:]) != tuple(scratch.shape[3:]):
+        raise ValueError("cache and scratch entries differ in dtype or shape")
+    if tuple(cache.shape[:2]) != tuple(scratch.shape[:2]):
+        raise ValueError("cache and scratch differ in planes or batch")
+    P, B, L = (int(x) for x in cache.shape[:3])
+    N = int(scratch.shape[2])
+    entry_elems = 1
+    for x in cache.shape[3:]:
+        entry_elems *= int(x)
+    es = cache.element_size()
+    for t, name in ((cache, "cache"), (scratch, "scratch")):
+        inner = 1
+        for d in range(t.dim() - 1, 1, -1):
+            if t.stride(d) != inner:
+                raise ValueError(f"{name}: each (plane, sequence) slice must be contiguous")
+            inner *= int(t.shape[d])
+    _check(load_library().specv_kv_commit(
+        P, B, N, L, entry_elems * es, _ptr(cache), cache.stride(0) * es, cache.stride(1) * es,
+        _ptr(scratch), scratch.stride(0) * es, scratch.stride(1) * es, _ptr(n_accepted), _ptr(cache_len),
+        _ptr(out_cache_len), _stream_ptr(stream, cache.device)), "specv_kv_commit")
 
 
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:

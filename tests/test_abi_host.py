@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
                                           "specv_stage_name", "specv_set_wait_limit",
-                                          "specv_verify_static", "specv_sample"}
+                                          "specv_verify_static", "specv_sample", "specv_kv_commit"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,6 +74,18 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_verify(None, 1, 1, *null) == _lib.SPECV_EINVAL
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
     assert lib.specv_sample(None, 1, None, None, None, None, None) == _lib.SPECV_EINVAL
+    # KV commit: sizes and alignment are checked before any device call.
+    kv = lambda *a: lib.specv_kv_commit(*a)  # noqa: E731
+    p16 = ctypes.c_void_p(4096)
+    p4 = ctypes.c_void_p(4100)
+    assert kv(-1, 1, 1, 8, 16, p16, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EINVAL
+    assert kv(1, 1, 0, 8, 16, p16, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EINVAL
+    assert kv(1, 1, 1, 8, 8, p16, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EINVAL
+    assert kv(1, 1, 1, 8, 24, p16, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EALIGN
+    assert kv(1, 1, 1, 8, 16, p4, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EALIGN
+    assert kv(1, 1, 1, 8, 16, p16, 8, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EALIGN
+    assert kv(1, 1, 1, 8, 16, None, 0, 0, p16, 0, 0, p4, p4, p4, None) == _lib.SPECV_EINVAL
+    assert kv(1, 0, 1, 8, 16, None, 0, 0, None, 0, 0, None, None, None, None) == _lib.SPECV_OK
     lib.specv_destroy(None)  # no-op
     assert lib.specv_set_timing(None, 1) == _lib.SPECV_EINVAL
     assert lib.specv_set_wait_limit(None, 10) == _lib.SPECV_EINVAL
