@@ -166,6 +166,30 @@ SPECV_API int specv_sample(specv_handle h, int n_rows, const void* logits, const
 SPECV_API int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream);
 
 /*
+ * Acceptance telemetry of the most recent specv_verify on this handle, which
+ * must have been called with this batch and n_draft and with these same
+ * buffers (their contents unchanged since): for every sequence b and position
+ * i < n_draft,
+ *   out_alpha [batch][n_draft] float32: alpha_i = sum_x min(p_i(x), q_i(x)),
+ *     the probability that draft i is accepted once position i is reached
+ *     (lesson "추측 디코딩 — 초안 작성, 검증, 반복", section "속도 향상을
+ *     결정하는 것"); at T = 0, 1 if d_i is the verifier's first argmax, else 0;
+ *   out_tau [batch] float32: tau = sum_{k=0..n_draft} prod_{i<k} alpha_i, the
+ *     expected number of tokens one verifier pass emits (with alpha held
+ *     fixed, (1 - alpha^(N+1)) / (1 - alpha)).
+ * NaN for sequences the verification found invalid. p and q come from the
+ * fp64 row log-normalisers the verification left in the handle; one more
+ * pass reads the 2*n_draft draft and target rows (about 1e-6 absolute error
+ * on alpha: fp64 arguments, fp32 exps). Asynchronous on `stream`.
+ * Errors (nothing enqueued): SPECV_EINVAL, SPECV_EALIGN, SPECV_ESTATE (the
+ * last call on the handle had another batch or n_draft, or was specv_sample),
+ * SPECV_EHIP.
+ */
+SPECV_API int specv_acceptance_rates(specv_handle h, int batch, int n_draft, const void* draft_logits,
+                                     const void* target_logits, const int32_t* draft_tokens, const float* temperature,
+                                     float* out_alpha, float* out_tau, void* stream);
+
+/*
  * Bound of every wait between the workgroups of one call, in microseconds
  * (0 <= microseconds <= 3.6e9; default 100000). Applies to later calls on the
  * handle. A wait normally lasts microseconds. 0 makes every wait give up at

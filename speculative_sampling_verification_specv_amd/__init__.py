@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     SpecvError,
     Verifier,
     load_library,
+    specv_acceptance_rates,
     specv_create,
     specv_destroy,
     specv_kv_commit,
@@ -37,6 +38,7 @@ __all__ = [
     "SpecvError",
     "load_library",
     "specv_create",
+    "specv_acceptance_rates",
     "specv_verify",
     "specv_verify_static",
     "specv_row_stats",

@@ -34,6 +34,7 @@ _SIGNATURES = {
                             + [ctypes.c_void_p] * 9),
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "specv_sample": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
+    "specv_acceptance_rates": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 7),
     "specv_kv_commit": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
@@ -166,6 +167,14 @@ def specv_kv_commit(cache, cache_len, scratch, n_accepted, out_cache_len, stream
         P, B, N, L, entry_elems * es, _ptr(cache), cache.stride(0) * es, cache.stride(1) * es,
         _ptr(scratch), scratch.stride(0) * es, scratch.stride(1) * es, _ptr(n_accepted), _ptr(cache_len),
         _ptr(out_cache_len), _stream_ptr(stream, cache.device)), "specv_kv_commit")
+
+
+def specv_acceptance_rates(handle: int, draft_logits, target_logits, draft_tokens, temperature, out_alpha, out_tau,
+                           stream=None) -> None:
+    B, N = draft_tokens.shape
+    _check(load_library().specv_acceptance_rates(
+        handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(temperature),
+        _ptr(out_alpha), _ptr(out_tau), _stream_ptr(stream, draft_tokens.device)), "specv_acceptance_rates")
 
 
 def specv_row_stats(handle: int, out_lse, out_argmax, stream=None) -> None:
@@ -307,6 +316,16 @@ class Verifier:
         specv_sample(self.handle, logits, temperature, uniforms, out_tokens, stream)
         self._last = (n, 0)
         return out_tokens
+
+    def acceptance_rates(self, draft_logits, target_logits, draft_tokens, temperature, stream=None):
+        """(alpha [B, N], tau [B]) float32 of the last verify (same tensors, unchanged)."""
+        import torch
+
+        B, N = draft_tokens.shape
+        alpha = torch.empty((B, N), dtype=torch.float32, device=self.device)
+        tau = torch.empty((B,), dtype=torch.float32, device=self.device)
+        specv_acceptance_rates(self.handle, draft_logits, target_logits, draft_tokens, temperature, alpha, tau, stream)
+        return alpha, tau
 
     def set_timing(self, enable: bool) -> None:
         specv_set_timing(self.handle, enable)

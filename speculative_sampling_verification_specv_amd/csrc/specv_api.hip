@@ -77,10 +77,18 @@ uint32_t next_call_tag(uint32_t tag) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// out[i] = float(in[i]) for the row diagnostics.
+__global__ void narrow_to_float(const double* in, float* out, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    out[i] = float(in[i]);
+}
+
 // Lays out a workspace for calls up to (max_batch, max_draft) at `vocab` and
 // `dtype` from `base` (which may be null to only size it); returns its size
-// in bytes. The regions are 256-byte aligned if `base` is.
-size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char* base, specv::Workspace* ws) {
+// in bytes. The regions are 256-byte aligned if `base` is. `rates`: also the
+// acceptance-rate partials (handles only).
+size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char* base, specv::Workspace* ws,
+                        bool rates) {
   const int chunk = specv::stat_chunk_elems(dtype);
   const int nch = specv::ceil_div(vocab, chunk);
   const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
@@ -93,18 +101,21 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
   const size_t off_records = off;
   off = align_up(off + size_t(max_batch) * nm * specv::member_bytes(), 256);
   const size_t off_lse = off;
-  off = align_up(off + rows * sizeof(float), 256);
+  off = align_up(off + rows * sizeof(double), 256);
   const size_t off_argmax = off;
   off = align_up(off + rows * sizeof(int), 256);
   const size_t off_counters = off;
   off = align_up(off + size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
+  const size_t off_rates = off;
+  if (rates) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nch * sizeof(double), 256);
   if (ws != nullptr) {
     ws->partials = base + off_partials;
     ws->seq = base + off_seq;
     ws->records = base + off_records;
-    ws->row_lse = reinterpret_cast<float*>(base + off_lse);
+    ws->row_lse = reinterpret_cast<double*>(base + off_lse);
     ws->row_argmax = reinterpret_cast<int*>(base + off_argmax);
     ws->draw_done = reinterpret_cast<int*>(base + off_counters);
+    ws->rate_parts = rates ? reinterpret_cast<double*>(base + off_rates) : nullptr;
     ws->n_stat_chunks = nch;
     ws->n_members = nm;
     ws->stat_chunk = chunk;
@@ -148,7 +159,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, spe
   if (hipGetDeviceCount(&n_dev) != hipSuccess) return SPECV_EHIP;
   if (device < 0 || device >= n_dev) return SPECV_EINVAL;
   if (!grid_fits(max_batch, max_draft, vocab, dtype)) return SPECV_EINVAL;
-  const size_t off = layout_workspace(max_batch, max_draft, vocab, dtype, nullptr, nullptr);
+  const size_t off = layout_workspace(max_batch, max_draft, vocab, dtype, nullptr, nullptr, true);
 
   DeviceGuard guard(device);
   if (!guard.ok()) return SPECV_EHIP;
@@ -165,7 +176,7 @@ int specv_create(specv_handle* out, int max_batch, int max_draft, int vocab, spe
   h->vocab = vocab;
   h->dtype = dtype;
   h->mem_bytes = off;
-  layout_workspace(max_batch, max_draft, vocab, dtype, static_cast<char*>(h->mem), &h->ws);
+  layout_workspace(max_batch, max_draft, vocab, dtype, static_cast<char*>(h->mem), &h->ws, true);
   h->ws.resident_blocks = specv::max_resident_blocks(dtype);
   if (h->ws.resident_blocks < 1 || hipMemset(h->mem, 0, off) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->mem);
@@ -279,6 +290,33 @@ int specv_sample(specv_handle h, int n_rows, const void* logits, const float* te
   return SPECV_OK;
 }
 
+int specv_acceptance_rates(specv_handle h, int batch, int n_draft, const void* draft_logits, const void* target_logits,
+                           const int32_t* draft_tokens, const float* temperature, float* out_alpha, float* out_tau,
+                           void* stream) {
+  if (h == nullptr) return SPECV_EINVAL;
+  if (batch < 0 || batch > h->max_batch || n_draft < 1 || n_draft > h->max_draft) return SPECV_EINVAL;
+  if (batch == 0) return SPECV_OK;
+  if (!draft_logits || !target_logits || !draft_tokens || !temperature || !out_alpha || !out_tau) return SPECV_EINVAL;
+  if (!aligned(draft_logits, 16) || !aligned(target_logits, 16)) return SPECV_EALIGN;
+  if (!aligned(draft_tokens, 4) || !aligned(temperature, 4) || !aligned(out_alpha, 4) || !aligned(out_tau, 4))
+    return SPECV_EALIGN;
+  if (h->last_batch != batch || h->last_n_draft != n_draft) return SPECV_ESTATE;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return SPECV_EHIP;
+  specv::RatesArgs a;
+  a.batch = batch;
+  a.n_draft = n_draft;
+  a.vocab = h->vocab;
+  a.dtype = h->dtype;
+  a.draft = draft_logits;
+  a.target = target_logits;
+  a.tokens = draft_tokens;
+  a.temperature = temperature;
+  a.out_alpha = out_alpha;
+  a.out_tau = out_tau;
+  return specv::launch_rates(a, h->ws, static_cast<hipStream_t>(stream)) == hipSuccess ? SPECV_OK : SPECV_EHIP;
+}
+
 int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* stream) {
   if (h == nullptr || out_lse == nullptr || out_argmax == nullptr) return SPECV_EINVAL;
   if (!aligned(out_lse, 4) || !aligned(out_argmax, 4)) return SPECV_EALIGN;
@@ -287,8 +325,9 @@ int specv_row_stats(specv_handle h, float* out_lse, int32_t* out_argmax, void* s
   if (!guard.ok()) return SPECV_EHIP;
   const size_t n = size_t(h->last_batch) * size_t(2 * h->last_n_draft + 1);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(out_lse, h->ws.row_lse, n * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
-    return SPECV_EHIP;
+  hipLaunchKernelGGL(narrow_to_float, dim3(unsigned(std::min<size_t>((n + 255) / 256, 4096))), dim3(256), 0, s,
+                     h->ws.row_lse, out_lse, n);
+  if (hipGetLastError() != hipSuccess) return SPECV_EHIP;
   if (hipMemcpyAsync(out_argmax, h->ws.row_argmax, n * sizeof(int), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return SPECV_EHIP;
   return SPECV_OK;
@@ -362,7 +401,7 @@ namespace {
 
 constexpr int kStaticMaxBatch = 256;
 constexpr int kStaticMaxDraft = 16;
-// layout_workspace(256, 16, 2^18, float32) = 8071168 bytes; checked at set-up.
+// layout_workspace(256, 16, 2^18, float32) = 8104960 bytes; checked at set-up.
 constexpr size_t kStaticBytes = size_t(8) << 20;
 constexpr int kStaticMaxDevices = 64;
 
@@ -404,7 +443,7 @@ int static_setup(int dev, hipStream_t stream) {
   if (sd.ready.load(std::memory_order_acquire)) return SPECV_OK;
   std::lock_guard<std::mutex> lock(g_static_mu);
   if (sd.ready.load(std::memory_order_relaxed)) return SPECV_OK;
-  if (layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, nullptr, nullptr) >
+  if (layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, nullptr, nullptr, false) >
       kStaticBytes)
     return SPECV_EHIP;
   void* ptr = nullptr;
@@ -455,7 +494,7 @@ extern "C" int specv_verify_static(int batch, int n_draft, int vocab, specv_dtyp
   // Every region at the offset of the largest layout, whatever this call's
   // vocabulary, so the counters always sit where the last call left them at 0.
   specv::Workspace ws;
-  layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, sd.ptr, &ws);
+  layout_workspace(kStaticMaxBatch, kStaticMaxDraft, specv::kMaxVocab, SPECV_F32, sd.ptr, &ws, false);
   ws.stat_chunk = specv::stat_chunk_elems(dtype);
   ws.n_stat_chunks = specv::ceil_div(vocab, ws.stat_chunk);
   ws.n_members = specv::ceil_div(vocab, specv::member_elems(dtype));

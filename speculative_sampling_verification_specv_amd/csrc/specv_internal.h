@@ -39,13 +39,14 @@ struct Workspace {
   void* partials;    // [max_batch][2*max_draft+1][n_stat_chunks] row-statistics partials
   void* seq;         // [max_batch] decisions
   void* records;     // [max_batch][n_members] draw-member records
-  float* row_lse;    // [batch][2N+1] of the last call
+  double* row_lse;   // [batch][2N+1] of the last call (fp64; NaN for rows not read)
   int* row_argmax;   // [batch][2N+1] of the last call
   // Per sequence, how many draw members of a launch are done with it; the
   // last one resets its count to zero. Zero between calls. One counter per
   // kCounterStride ints (its own 256-byte line), so that atomics on different
   // sequences' counters never contend for a line.
   int* draw_done;    // [max_batch * kCounterStride]
+  double* rate_parts;  // [max_batch][max_draft][n_stat_chunks] acceptance-rate partial sums (handles only)
   int n_stat_chunks;
   int resident_blocks;  // workgroups of the verification kernel the device holds at once
   int n_members;     // draw members per sequence
@@ -87,6 +88,23 @@ const char* stage_name(int stage);
 size_t partial_bytes();
 size_t seq_bytes();
 size_t member_bytes();
+
+struct RatesArgs {
+  int batch;
+  int n_draft;
+  int vocab;
+  int dtype;  // specv_dtype
+  const void* draft;
+  const void* target;
+  const int* tokens;
+  const float* temperature;
+  float* out_alpha;  // [batch][n_draft]
+  float* out_tau;    // [batch]
+};
+
+// Enqueue the acceptance-rate passes on `stream`; they read the row
+// log-normalisers and argmaxes the last verification left in `w`.
+hipError_t launch_rates(const RatesArgs& a, const Workspace& w, hipStream_t stream);
 
 // Enqueue the whole verification on `stream`. If `events` is non-null it holds
 // kMaxStages + 1 events: events[k] is recorded before stage k and

@@ -471,7 +471,7 @@ struct Params {
   const float* temperature;
   int* out_tokens;
   int* out_n;
-  float* row_lse;
+  double* row_lse;
   int* row_argmax;
   PartialRec* partials;  // [batch][2N+1][nch], one per item
   SeqRec* seq;           // [batch]
@@ -906,7 +906,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const int wave = tid >> 6;
   const int* tok = P.tokens + int64_t(b) * N;
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
-  float* lse = P.row_lse + int64_t(b) * R;
+  double* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
   // Every row partial of the sequence is taken (and zeroed) whatever the
   // outcome, a group of rows at a time (thread i takes partial i of the
@@ -991,7 +991,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
         ds.row_m[r] = m;
         ds.row_logz[r] = logz;
         ds.row_idx[r] = idx;
-        lse[r] = greedy ? NAN : float(double(m) * inv_t + logz);
+        lse[r] = greedy ? double(NAN) : double(m) * inv_t + logz;
         amax[r] = idx;
       }
     }

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     assert set(_declared_functions()) == {"specv_create", "specv_verify", "specv_row_stats", "specv_destroy",
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
                                           "specv_stage_name", "specv_set_wait_limit",
-                                          "specv_verify_static", "specv_sample", "specv_kv_commit"}
+                                          "specv_verify_static", "specv_sample", "specv_kv_commit",
+                                          "specv_acceptance_rates"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,6 +75,7 @@ def test_argument_errors_before_any_device_call():
     assert lib.specv_verify(None, 1, 1, *null) == _lib.SPECV_EINVAL
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
     assert lib.specv_sample(None, 1, None, None, None, None, None) == _lib.SPECV_EINVAL
+    assert lib.specv_acceptance_rates(None, 1, 1, *([None] * 7)) == _lib.SPECV_EINVAL
     # KV commit: sizes and alignment are checked before any device call.
     kv = lambda *a: lib.specv_kv_commit(*a)  # noqa: E731
     p16 = ctypes.c_void_p(4096)
