@@ -130,6 +130,28 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
                  int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
 
 /*
+ * specv_verify with the same arguments and results, reading each sequence's
+ * rows only as far as its first rejection (guide "친구가 먼저 쓰고 선생님이
+ * 채점합니다", section "몇 글자를 미리 쓰게 할까요": position k is reached with
+ * probability alpha^k, so most rows past an early rejection need never be
+ * read). The positions go in stages [0,1), [1,2), [2,4), [4,8), ... up to
+ * n_draft, each a kernel launch of its own on `stream` over the sequences
+ * still alive at its first position; the row statistics, the accept tests
+ * and the draw are those of specv_verify, so tokens and n_accepted are
+ * identical to its. Bytes read fall from 2N+1 rows per sequence toward the
+ * rows up to the first rejection (plus the draw's re-read), at the cost of
+ * one launch per stage (ceil(log2 n_draft) + 1 of them). Afterwards
+ * specv_row_stats reports NaN / -1 for the rows not read, and
+ * specv_acceptance_rates NaN for the positions not reached.
+ * Errors: as specv_verify.
+ */
+SPECV_API int specv_verify_lazy(specv_handle h, int batch, int n_draft, const void* draft_logits,
+                                const void* target_logits, const int32_t* draft_tokens,
+                                const float* accept_uniforms, const float* sample_uniforms,
+                                const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted,
+                                void* stream);
+
+/*
  * Draw one token from each of n_rows rows of logits (the draft model's step
  * before verification: lesson "추측 디코딩 — 초안 작성, 검증, 반복",
  * section "핵심 알고리즘(Core algorithm)" step 2, and the draft loop of its

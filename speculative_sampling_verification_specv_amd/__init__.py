@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     specv_stage_name,
     specv_strerror,
     specv_verify,
+    specv_verify_lazy,
     specv_verify_static,
 )
 
@@ -40,6 +41,7 @@ __all__ = [
     "specv_create",
     "specv_acceptance_rates",
     "specv_verify",
+    "specv_verify_lazy",
     "specv_verify_static",
     "specv_row_stats",
     "specv_sample",

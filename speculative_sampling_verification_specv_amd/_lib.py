@@ -30,6 +30,7 @@ _SIGNATURES = {
     "specv_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int]),
     "specv_verify": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 9),
+    "specv_verify_lazy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 9),
     "specv_verify_static": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
                             + [ctypes.c_void_p] * 9),
     "specv_row_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -113,6 +114,16 @@ def specv_verify(handle: int, draft_logits, target_logits, draft_tokens, accept_
         handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
         _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
         _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device)), "specv_verify")
+
+
+def specv_verify_lazy(handle: int, draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms,
+                      temperature, out_tokens, out_n_accepted, stream=None) -> None:
+    """Enqueue one lazy verification (rows read up to each sequence's first rejection)."""
+    B, N = draft_tokens.shape
+    _check(load_library().specv_verify_lazy(
+        handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
+        _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
+        _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device)), "specv_verify_lazy")
 
 
 def specv_verify_static(draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms, temperature,
@@ -268,8 +279,32 @@ class Verifier:
         self._last = (B, N)
         return out_tokens, out_n_accepted
 
+    def verify_lazy(self, draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms, temperature,
+                    out_tokens=None, out_n_accepted=None, stream=None):
+        """verify() that reads each sequence's rows only up to its first rejection (same results)."""
+        import torch
+
+        B, N = draft_tokens.shape
+        V = self.vocab
+        self._expect(draft_logits, "draft_logits", (B, N, V), self.torch_dtype)
+        self._expect(target_logits, "target_logits", (B, N + 1, V), self.torch_dtype)
+        self._expect(draft_tokens, "draft_tokens", (B, N), torch.int32)
+        self._expect(accept_uniforms, "accept_uniforms", (B, N), torch.float32)
+        self._expect(sample_uniforms, "sample_uniforms", (B,), torch.float32)
+        self._expect(temperature, "temperature", (B,), torch.float32)
+        if out_tokens is None:
+            out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=self.device)
+        if out_n_accepted is None:
+            out_n_accepted = torch.empty((B,), dtype=torch.int32, device=self.device)
+        self._expect(out_tokens, "out_tokens", (B, N + 1), torch.int32)
+        self._expect(out_n_accepted, "out_n_accepted", (B,), torch.int32)
+        specv_verify_lazy(self.handle, draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms,
+                          temperature, out_tokens, out_n_accepted, stream)
+        self._last = (B, N)
+        return out_tokens, out_n_accepted
+
     def bind(self, draft_logits, target_logits, draft_tokens, accept_uniforms, sample_uniforms, temperature,
-             out_tokens, out_n_accepted, stream=None):
+             out_tokens, out_n_accepted, stream=None, lazy: bool = False):
         """Check one call's arguments once; return a function that enqueues exactly that call.
 
         The returned function re-issues specv_verify with the same buffers and
@@ -289,7 +324,7 @@ class Verifier:
         self._expect(temperature, "temperature", (B,), torch.float32)
         self._expect(out_tokens, "out_tokens", (B, N + 1), torch.int32)
         self._expect(out_n_accepted, "out_n_accepted", (B,), torch.int32)
-        fn = load_library().specv_verify
+        fn = load_library().specv_verify_lazy if lazy else load_library().specv_verify
         args = (self.handle, int(B), int(N), _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens),
                 _ptr(accept_uniforms), _ptr(sample_uniforms), _ptr(temperature), _ptr(out_tokens),
                 _ptr(out_n_accepted), _stream_ptr(stream, draft_tokens.device))

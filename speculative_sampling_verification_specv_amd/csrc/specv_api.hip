@@ -106,6 +106,8 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
   off = align_up(off + rows * sizeof(int), 256);
   const size_t off_counters = off;
   off = align_up(off + size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
+  const size_t off_state = off;
+  off = align_up(off + size_t(2) * max_batch * sizeof(int), 256);
   const size_t off_rates = off;
   if (rates) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nch * sizeof(double), 256);
   if (ws != nullptr) {
@@ -116,6 +118,7 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
     ws->row_argmax = reinterpret_cast<int*>(base + off_argmax);
     ws->draw_done = reinterpret_cast<int*>(base + off_counters);
     ws->rate_parts = rates ? reinterpret_cast<double*>(base + off_rates) : nullptr;
+    ws->lazy_state = reinterpret_cast<int*>(base + off_state);
     ws->n_stat_chunks = nch;
     ws->n_members = nm;
     ws->stat_chunk = chunk;
@@ -239,6 +242,8 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.tag = h->next_tag;
   a.debug = h->debug;
   a.wait_ticks = h->wait_ticks;
+  a.pos_lo = 0;
+  a.pos_hi = n_draft;
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, h->timing ? h->events : nullptr, &stages) != hipSuccess) return SPECV_EHIP;
   h->next_tag = next_call_tag(h->next_tag);
@@ -246,6 +251,60 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   h->last_n_draft = n_draft;
   h->timed_call = h->timing;
   h->timed_stages = stages;
+  return SPECV_OK;
+}
+
+int specv_verify_lazy(specv_handle h, int batch, int n_draft, const void* draft_logits, const void* target_logits,
+                      const int32_t* draft_tokens, const float* accept_uniforms, const float* sample_uniforms,
+                      const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted, void* stream) {
+  if (h == nullptr) return SPECV_EINVAL;
+  if (batch < 0 || batch > h->max_batch) return SPECV_EINVAL;
+  if (n_draft < 1 || n_draft > h->max_draft) return SPECV_EINVAL;
+  if (batch == 0) return SPECV_OK;
+  if (!draft_logits || !target_logits || !draft_tokens || !accept_uniforms || !sample_uniforms || !temperature ||
+      !out_tokens || !out_n_accepted)
+    return SPECV_EINVAL;
+  if (!aligned(draft_logits, 16) || !aligned(target_logits, 16)) return SPECV_EALIGN;
+  if (!aligned(draft_tokens, 4) || !aligned(accept_uniforms, 4) || !aligned(sample_uniforms, 4) ||
+      !aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(out_n_accepted, 4))
+    return SPECV_EALIGN;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return SPECV_EHIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  specv::VerifyArgs a;
+  a.batch = batch;
+  a.n_draft = n_draft;
+  a.vocab = h->vocab;
+  a.dtype = h->dtype;
+  a.draft = draft_logits;
+  a.target = target_logits;
+  a.tokens = draft_tokens;
+  a.accept_u = accept_uniforms;
+  a.sample_u = sample_uniforms;
+  a.temperature = temperature;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n_accepted;
+  a.debug = h->debug;
+  a.wait_ticks = h->wait_ticks;
+  a.lazy = 1;
+  a.state = h->ws.lazy_state;
+  // Stages [0,1), [1,2), [2,4), [4,8), ...: each a launch of its own, over the
+  // sequences still alive at its first position.
+  int k = 0;
+  for (int lo = 0; lo < n_draft; ++k) {
+    const int hi = lo == 0 ? 1 : std::min(n_draft, 2 * lo);
+    a.pos_lo = lo;
+    a.pos_hi = hi;
+    a.parity = k & 1;
+    a.tag = h->next_tag;
+    int stages = 0;
+    if (specv::launch_verify(a, h->ws, s, nullptr, &stages) != hipSuccess) return SPECV_EHIP;
+    h->next_tag = next_call_tag(h->next_tag);
+    lo = hi;
+  }
+  h->last_batch = batch;
+  h->last_n_draft = n_draft;
+  h->timed_call = false;
   return SPECV_OK;
 }
 
@@ -275,6 +334,8 @@ int specv_sample(specv_handle h, int n_rows, const void* logits, const float* te
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = nullptr;
+  a.pos_lo = 0;
+  a.pos_hi = 0;
   a.tag = h->next_tag;
   a.debug = h->debug;
   a.wait_ticks = h->wait_ticks;
@@ -401,7 +462,7 @@ namespace {
 
 constexpr int kStaticMaxBatch = 256;
 constexpr int kStaticMaxDraft = 16;
-// layout_workspace(256, 16, 2^18, float32) = 8104960 bytes; checked at set-up.
+// layout_workspace(256, 16, 2^18, float32) = 8107008 bytes; checked at set-up.
 constexpr size_t kStaticBytes = size_t(8) << 20;
 constexpr int kStaticMaxDevices = 64;
 
@@ -515,6 +576,8 @@ extern "C" int specv_verify_static(int batch, int n_draft, int vocab, specv_dtyp
   a.tag = take_tag(sd.tag);
   a.debug = sd.debug;
   a.wait_ticks = sd.wait_ticks;
+  a.pos_lo = 0;
+  a.pos_hi = n_draft;
   int stages = 0;
   return specv::launch_verify(a, ws, s, nullptr, &stages) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }

@@ -32,7 +32,15 @@ constexpr int kCounterStride = 64;
 
 // What a sampled sequence's draw does: a residual or bonus draw, nothing because an
 // input is invalid (-1 outputs), or nothing because a wait gave up (-2 outputs).
-enum SeqMode : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2, kModeInvalid = 3, kModeFailed = 4 };
+// A lazy stage's sequence whose drafts so far are all accepted continues in the next stage (no draw yet).
+enum SeqMode : int {
+  kModeNone = 0,
+  kModeResidual = 1,
+  kModeBonus = 2,
+  kModeInvalid = 3,
+  kModeFailed = 4,
+  kModeContinue = 5
+};
 
 // Device workspace: records one launch writes and the next reads.
 struct Workspace {
@@ -47,6 +55,7 @@ struct Workspace {
   // sequences' counters never contend for a line.
   int* draw_done;    // [max_batch * kCounterStride]
   double* rate_parts;  // [max_batch][max_draft][n_stat_chunks] acceptance-rate partial sums (handles only)
+  int* lazy_state;     // [2][max_batch] lazy stages' per-sequence states
   int n_stat_chunks;
   int resident_blocks;  // workgroups of the verification kernel the device holds at once
   int n_members;     // draw members per sequence
@@ -69,6 +78,11 @@ struct VerifyArgs {
   uint32_t tag;         // the call's number (never 0), carried by every hand-off word
   uint32_t debug;       // also check that the uniforms lie in [0, 1)
   uint64_t wait_ticks;  // bound of every wait between workgroups, in wall-clock ticks
+  // Positions [pos_lo, pos_hi) of this launch ([0, n_draft) for a whole
+  // call); a lazy stage (lazy != 0) reads and writes per-sequence states in
+  // `state` ([2][batch] ints, read half `parity`).
+  int pos_lo = 0, pos_hi = 0, lazy = 0, parity = 0;
+  int* state = nullptr;
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -488,6 +488,14 @@ struct Params {
   uint32_t flags;       // kVecOk: rows start 16-byte aligned; kDebug: check that the uniforms lie in [0, 1)
   uint32_t tag;         // this call's number (never 0): the high half of every hand-off word
   uint32_t wait_ticks;  // bound of every wait, in ticks of the 100 MHz wall clock
+  // The positions [lo, hi) this launch verifies: bits 0-7 lo, 8-15 hi, bit 16
+  // the parity of a lazy stage, bit 17 set for a lazy stage. A whole call is
+  // [0, N) and not lazy. A lazy call runs stages [0,1), [1,2), [2,4), ... as
+  // launches of their own; stage k reads each sequence's state from
+  // state[parity * batch + b] (the position it is alive at, -1 when done) and
+  // writes the next stage's to state[(1 - parity) * batch + b].
+  uint32_t stage;
+  int* state;
 };
 constexpr uint32_t kVecOk = 1, kDebug = 2;
 
@@ -496,11 +504,30 @@ __device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r,
   return P.partials + (int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c;
 }
 
-// The draft token of row r (draft row i or target row i: d_i), or -1 for target row N.
-__device__ __forceinline__ int row_token(const Params& P, int b, int r) {
-  const int N = P.n_draft;
-  const int pos = r < N ? r : r - N;
-  return pos < N ? load_uniform(P.tokens + int64_t(b) * N + pos) : -1;
+__device__ __forceinline__ int stage_lo(const Params& P) { return int(P.stage & 0xffu); }
+__device__ __forceinline__ int stage_hi(const Params& P) { return int((P.stage >> 8) & 0xffu); }
+__device__ __forceinline__ bool stage_lazy(const Params& P) { return (P.stage >> 17) & 1u; }
+__device__ __forceinline__ int stage_parity(const Params& P) { return int((P.stage >> 16) & 1u); }
+// Rows a sequence reads in this launch: draft and target rows lo..hi-1, and
+// target row N if hi = N.
+__device__ __forceinline__ int stage_rows(const Params& P) {
+  return 2 * (stage_hi(P) - stage_lo(P)) + (stage_hi(P) == P.n_draft ? 1 : 0);
+}
+// Row lr of this launch's rows as a row of the sequence (draft rows 0..N-1,
+// then target rows 0..N).
+__device__ __forceinline__ int global_row(const Params& P, int lr) {
+  const int lo = stage_lo(P), n = stage_hi(P) - lo;
+  return lr < n ? lo + lr : (lr < 2 * n ? P.n_draft + lo + (lr - n) : 2 * P.n_draft);
+}
+// Whether sequence b is verified in this launch (every sequence, except in a
+// lazy stage after the first: those still alive at its first position).
+__device__ __forceinline__ bool seq_alive(const Params& P, int b) {
+  if (!stage_lazy(P) || stage_lo(P) == 0) return true;
+  return load_uniform(P.state + stage_parity(P) * P.batch + b) == stage_lo(P);
+}
+// A lazy stage records where sequence b goes on (-1: done).
+__device__ __forceinline__ void set_next_state(const Params& P, int b, int v) {
+  if (stage_lazy(P)) P.state[(1 - stage_parity(P)) * P.batch + b] = v;
 }
 
 // One row-statistics item: chunk c of row r of sequence b.
@@ -513,7 +540,6 @@ struct Item {
   int e0, e1;  // chunk [e0, e1) of the row
   int ea, nv;  // first 16-byte aligned element, whole vectors from there
   int et;      // first element after the vectors
-  int tok;     // the row's draft token, or -1
 };
 
 template <typename T>
@@ -522,13 +548,13 @@ __device__ __forceinline__ Item item_at(const Params& P, int64_t t) {
   Item it;
   it.live = false;
   const int N = P.n_draft;
-  const int R = 2 * N + 1;
+  const int Rs = stage_rows(P);
   const int64_t rc = t / P.nch;
   it.c = int(t - rc * P.nch);
-  it.b = int(rc / R);
-  it.r = int(rc - int64_t(it.b) * R);
+  it.b = int(rc / Rs);
+  it.r = global_row(P, int(rc - int64_t(it.b) * Rs));
   const float temp = load_uniform(P.temperature + it.b);
-  if (!temperature_valid(temp) || (temp == 0.0f && it.r < N)) return it;
+  if (!temperature_valid(temp) || (temp == 0.0f && it.r < N) || !seq_alive(P, it.b)) return it;
   it.live = true;
   it.sampled = temp != 0.0f;
   it.coef = it.sampled ? exp2_coef(temp) : 0.0f;
@@ -541,7 +567,6 @@ __device__ __forceinline__ Item item_at(const Params& P, int64_t t) {
   it.ea = min(it.e1, it.e0 + (kVec - mis) % kVec);
   it.nv = (it.e1 - it.ea) / kVec;
   it.et = it.ea + it.nv * kVec;
-  it.tok = row_token(P, it.b, it.r);
   return it;
 }
 
@@ -886,12 +911,14 @@ __device__ __forceinline__ bool take_partial(const Params& P, PartialRec* q, int
   return ok;
 }
 
-// The decision for sequence b (whole workgroup, once per sequence): per-row
-// log-normalisers and argmaxes from the row partials, the N accept tests, the
-// first rejection. Writes the row diagnostics and the accepted prefix; a
-// greedy sequence's emitted token and n_accepted too, while a sampled
-// sequence's are written by its draw's finisher, from the record published
-// here.
+// The decision for sequence b (whole workgroup, once per sequence and
+// launch): per-row log-normalisers and argmaxes from the row partials of the
+// launch's rows, the accept tests of its positions [lo, hi), the first
+// rejection. Writes the row diagnostics and the accepted prefix; a greedy
+// sequence's emitted token and n_accepted too, while a sampled sequence's are
+// written by its draw's finisher, from the record published here. In a lazy
+// stage a sequence whose drafts lo..hi-1 are all accepted (hi < N) goes on to
+// the next stage: its drafts so far are written and nothing is drawn.
 //
 // The normalisers come from fp32 row sums (relative error ~1e-6); logs and
 // the ratio are taken in fp64, so a decision can only differ from exact
@@ -901,6 +928,9 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   DecideShared& ds = sh.u.dec;
   const int N = P.n_draft;
   const int R = 2 * N + 1;
+  const int lo = stage_lo(P), hi = stage_hi(P), ns = hi - lo;
+  const bool last = hi == N;
+  const int Rs = stage_rows(P);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -908,33 +938,54 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   double* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  // Every row partial of the sequence is taken (and zeroed) whatever the
+  const bool alive = seq_alive(P, b);
+  // Every row partial of the launch's rows is taken (and zeroed) whatever the
   // outcome, a group of rows at a time (thread i takes partial i of the
   // group).
   const int pr = P.nch;  // partials per row
   const int rows_per_group = max(1, kStageParts / pr);
   PartialRec* part_b = P.partials + int64_t(b) * R * pr;
-  // (n_draft = 0 is the plain draw from one row: no draft tokens, no uniforms to test)
-  const int ti = min(tid, max(N - 1, 0));
-  const int d = N > 0 ? tok[ti] : 0;
-  const float ua = N > 0 ? P.accept_u[int64_t(b) * N + ti] : 0.0f;
+  // The inputs are checked where a sequence starts (lo = 0), all N positions
+  // at once; thread i < ns tests position lo + i. (n_draft = 0 is the plain
+  // draw from one row: no draft tokens, no uniforms to test.)
+  const int tv = min(tid, max(N - 1, 0));
+  const int dv = N > 0 ? tok[tv] : 0;
+  const float uv = N > 0 ? P.accept_u[int64_t(b) * N + tv] : 0.0f;
+  const int pos = lo + min(tid, max(ns - 1, 0));
+  const int d = ns > 0 ? tok[pos] : 0;
+  const float ua = ns > 0 ? P.accept_u[int64_t(b) * N + pos] : 0.0f;
   const float t = load_uniform(P.temperature + b);
   const float us = load_uniform(P.sample_u + b);
-  if (tid < N) ds.tok[tid] = d;
-  bool bad = !temperature_valid(t) || (tid < N && (d < 0 || d >= P.vocab));
-  if (P.flags & kDebug) bad = bad || (tid < N && !(ua >= 0.0f && ua < 1.0f)) || (t > 0.0f && !(us >= 0.0f && us < 1.0f));
+  if (tid < ns) ds.tok[lo + tid] = d;
+  bool bad = false;
+  if (lo == 0) {
+    bad = !temperature_valid(t) || (tid < N && (dv < 0 || dv >= P.vocab));
+    if (P.flags & kDebug)
+      bad = bad || (tid < N && !(uv >= 0.0f && uv < 1.0f)) || (t > 0.0f && !(us >= 0.0f && us < 1.0f));
+  }
   const bool greedy = (t == 0.0f);
-  // Thread i < N: the logits of draft token d_i in draft row i and target
-  // row i (requested now; used by the accept test).
+  // Thread i < ns: the logits of draft token d at position lo + i in its draft
+  // and target rows (requested now; used by the accept test).
   float zt = 0.0f, zd = 0.0f;
-  if (tid < N && !greedy && d >= 0 && d < P.vocab) {
-    zt = Logit<T>::at(static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + tid) * P.vocab, d);
-    zd = Logit<T>::at(static_cast<const T*>(P.draft) + (int64_t(b) * N + tid) * P.vocab, d);
+  if (tid < ns && alive && !greedy && d >= 0 && d < P.vocab) {
+    zt = Logit<T>::at(static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + pos) * P.vocab, d);
+    zd = Logit<T>::at(static_cast<const T*>(P.draft) + (int64_t(b) * N + pos) * P.vocab, d);
   }
   const bool draws = has_draw_members(t);  // draw members wait for this decision
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
+  // The first stage of a lazy call marks the rows it does not read; later
+  // stages fill in the ones they read.
+  if (stage_lazy(P) && lo == 0) {
+    for (int r = tid; r < R; r += kThreads) {
+      const bool in_stage = r < N ? (r >= lo && r < hi) : (r < 2 * N ? (r - N >= lo && r - N < hi) : last);
+      if (!in_stage) {
+        lse[r] = NAN;
+        amax[r] = -1;
+      }
+    }
+  }
   // Quads of lanes each merge one row: lane k of a quad folds partials k,
   // k + 4, ... of the row in order, then two exchange steps within the quad.
   constexpr int cs = 4;
@@ -942,13 +993,14 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
   const uint64_t deadline = deadline_after(P.wait_ticks);
   bool timed_out = false, any_bad = false;
-  for (int rg = 0; rg < R; rg += rows_per_group) {
-    const int nr = min(rows_per_group, R - rg);
+  for (int rg = 0; rg < Rs; rg += rows_per_group) {
+    const int nr = min(rows_per_group, Rs - rg);
     const int np = nr * pr;
     bool late = false;
     if (tid < np) {
       Partial q;
-      late = !take_partial(P, part_b + int64_t(rg) * pr + tid, (tid % pr) * P.chunk, deadline, q);
+      const int kc = tid % pr;
+      late = !take_partial(P, part_b + int64_t(global_row(P, rg + tid / pr)) * pr + kc, kc * P.chunk, deadline, q);
       ds.part[tid] = q;
     }
     // (also the barrier that makes the group's partials visible); the input
@@ -957,11 +1009,11 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     const int vote = block_any2(rg == 0 && bad, late);
     any_bad = any_bad || (vote & 1);
     timed_out = timed_out || (vote & 2);
-    if (any_bad || timed_out) continue;
+    if (any_bad || timed_out || !alive) continue;
     if (rg == 0) trace(2, 4);
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
       const int rr = r0 + seg;
-      const int r = rg + rr;
+      const int r = global_row(P, rg + min(rr, nr - 1));
       const bool row_ok = rr < nr && r >= r_first;
       float m = -INFINITY, s = 0.0f;
       int idx = INT_MAX;
@@ -997,6 +1049,11 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     }
     barrier();
   }
+  if (!alive) {
+    // Done in an earlier stage: its partials are cleared, nothing else.
+    if (tid == 0) set_next_state(P, b, -1);
+    return;
+  }
   if (any_bad || timed_out) {
     // Invalid inputs give -1 everywhere; a partial that never came (not
     // expected: a workgroup that was not dispatched in time) gives -2.
@@ -1005,6 +1062,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
       lse[r] = NAN;
       amax[r] = -1;
     }
+    if (tid == 0) set_next_state(P, b, -1);
     if (draws) {
       // The finisher writes the sentinels.
       if (tid == 0) publish(P, b, any_bad ? kModeInvalid : kModeFailed, 0, 0.0f, 0.0f, 0.0);
@@ -1016,51 +1074,56 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   }
   trace(2, 5);
   if (greedy) {
-    for (int r = tid; r < N; r += kThreads) {
+    for (int r = lo + tid; r < hi; r += kThreads) {
       lse[r] = NAN;
       amax[r] = -1;
     }
   }
 
   bool accept = true;
-  if (tid < N) {
+  if (tid < ns) {
+    const int i = lo + tid;
     if (greedy) {
-      accept = (d == ds.row_idx[N + tid]);
+      accept = (d == ds.row_idx[N + i]);
     } else if (zd == -INFINITY) {
       accept = true;  // p(d) == 0: the ratio is infinite
     } else {
       // log(q(d)/p(d)); the test is u < exp of it.
-      const double lr = ((double(zt) - double(ds.row_m[N + tid])) - (double(zd) - double(ds.row_m[tid]))) * inv_t -
-                        (ds.row_logz[N + tid] - ds.row_logz[tid]);
+      const double lr = ((double(zt) - double(ds.row_m[N + i])) - (double(zd) - double(ds.row_m[i]))) * inv_t -
+                        (ds.row_logz[N + i] - ds.row_logz[i]);
       // u < 1 <= exp(lr) when lr >= 0; the library exp only where the local one underflows.
       accept = lr >= 0.0 || double(ua) < (lr >= -708.0 ? exp_nonpos(lr) : exp(lr));
     }
   }
   // N <= 64: every decision lives in wave 0.
   if (wave == 0) {
-    const unsigned long long rej = __ballot(tid < N && !accept);
+    const unsigned long long rej = __ballot(tid < ns && !accept);
     if (lane == 0) ds.rej_mask = rej;
   }
   barrier();
   trace(2, 6);
   const unsigned long long rej = ds.rej_mask;
-  const int j = rej ? (__ffsll(rej) - 1) : N;
-  const int mode = greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus);
+  const int j = rej ? lo + (__ffsll(rej) - 1) : hi;
+  const bool go_on = j == hi && !last;  // a lazy stage's sequence that continues
+  const int mode = go_on ? kModeContinue : (greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus));
   // The draw's record first: the draw members wait for it.
   if (tid == 0 && !greedy) {
-    const float md = j < N ? ds.row_m[j] : 0.0f;
-    const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-    publish(P, b, mode, j, ds.row_m[N + j], md, log_rho);
+    const float md = (j < N && !go_on) ? ds.row_m[j] : 0.0f;
+    const double log_rho = (j < N && !go_on) ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
+    publish(P, b, mode, j, go_on ? 0.0f : ds.row_m[N + j], md, log_rho);
   }
-  for (int i = tid; i <= N; i += kThreads) {
+  if (tid == 0) set_next_state(P, b, go_on ? hi : -1);
+  for (int i = lo + tid; i <= N; i += kThreads) {
     if (i < j)
       otok[i] = ds.tok[i];
+    else if (go_on)
+      break;
     else if (i > j)
       otok[i] = -1;
     else if (greedy)
       otok[i] = ds.row_idx[N + j];
   }
-  if (tid == 0 && greedy && P.out_n != nullptr) P.out_n[b] = j;
+  if (tid == 0 && greedy && !go_on && P.out_n != nullptr) P.out_n[b] = j;
 }
 
 // ---------------------------------------------------------------------------
@@ -1456,11 +1519,15 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (lane == 0) ws.fail = bad;
   }
   barrier();
+  if (ws.fail == 0ull && s.mode == kModeContinue) return;  // a lazy stage's sequence goes on
   if (ws.fail != 0ull || !(s.mode == kModeResidual || s.mode == kModeBonus)) {
     const int code = s.mode == kModeInvalid ? -1 : -2;
     int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
     for (int i = tid; i <= P.n_draft; i += kThreads) otok[i] = code;
-    if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
+    if (tid == 0) {
+      if (P.out_n != nullptr) P.out_n[b] = code;
+      set_next_state(P, b, -1);
+    }
     return;
   }
   const DrawRows<T> d = draw_rows<T>(P, b, s);
@@ -1641,7 +1708,9 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp
 template <typename T>
 __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
   const float temp = load_uniform(P.temperature + b);
-  if (!has_draw_members(temp)) return;
+  // (a lazy stage's sequence that is already done has no decision here: its
+  // members all leave at once, so its counter stays at zero)
+  if (!has_draw_members(temp) || !seq_alive(P, b)) return;
   trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
   SeqInfo s;
@@ -1748,7 +1817,11 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.nch = w.n_stat_chunks;
   p.chunk = w.stat_chunk;
   p.nm = w.n_members;
-  p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
+  p.stage = uint32_t(a.pos_lo) | (uint32_t(a.pos_hi) << 8) | (uint32_t(a.parity & 1) << 16) |
+            (a.lazy ? (1u << 17) : 0u);
+  p.state = a.state;
+  const int rows = 2 * (a.pos_hi - a.pos_lo) + (a.pos_hi == a.n_draft ? 1 : 0);
+  p.items_per_seq = rows * w.n_stat_chunks;
   // The lag: about three chip-fulls of resident workgroups of (row
   // statistics, draw) pairs, so a sequence's decision is normally out before
   // its draw members start.

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                                           "specv_strerror", "specv_set_timing", "specv_last_timings",
                                           "specv_stage_name", "specv_set_wait_limit",
                                           "specv_verify_static", "specv_sample", "specv_kv_commit",
-                                          "specv_acceptance_rates"}
+                                          "specv_acceptance_rates", "specv_verify_lazy"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,6 +73,7 @@ def test_argument_errors_before_any_device_call():
         assert h.value is None
     null = [None] * 9
     assert lib.specv_verify(None, 1, 1, *null) == _lib.SPECV_EINVAL
+    assert lib.specv_verify_lazy(None, 1, 1, *null) == _lib.SPECV_EINVAL
     assert lib.specv_row_stats(None, None, None, None) == _lib.SPECV_EINVAL
     assert lib.specv_sample(None, 1, None, None, None, None, None) == _lib.SPECV_EINVAL
     assert lib.specv_acceptance_rates(None, 1, 1, *([None] * 7)) == _lib.SPECV_EINVAL

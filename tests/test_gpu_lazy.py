@@ -1,0 +1,164 @@
+"""GPU parity of the lazy verification (specv_verify_lazy).
+
+Its tokens and n_accepted must equal specv_verify's bit for bit on the same
+inputs (and so the oracle's, by the parity rules); the rows it read carry the
+same log-normalisers and argmaxes as specv_verify's, the rows past each
+sequence's stage of rejection are reported as not read.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import GpuResult, compare, library_rejects_temperature, require_gpu, run_oracle, to_device
+from speculative_sampling_verification_specv_amd import Verifier
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _stages(N):
+    out, lo = [], 0
+    while lo < N:
+        hi = 1 if lo == 0 else min(N, 2 * lo)
+        out.append((lo, hi))
+        lo = hi
+    return out
+
+
+def _both(batch, v=None):
+    dev = require_gpu()
+    own = v is None
+    if own:
+        v = Verifier(batch.batch, batch.n_draft, batch.vocab, batch.dtype)
+    try:
+        args = to_device(batch, dev)
+        t_full, n_full = v.verify(**args)
+        lse_f, am_f = v.row_stats()
+        t_full, n_full = t_full.clone(), n_full.clone()
+        t_lazy, n_lazy = v.verify_lazy(**args)
+        lse_l, am_l = v.row_stats()
+        torch.cuda.synchronize()
+        full = GpuResult(t_full.cpu().numpy(), n_full.cpu().numpy(), lse_f.cpu().numpy(), am_f.cpu().numpy())
+        lazy = GpuResult(t_lazy.cpu().numpy(), n_lazy.cpu().numpy(), lse_l.cpu().numpy(), am_l.cpu().numpy())
+        return full, lazy
+    finally:
+        if own:
+            v.close()
+
+
+def _check(batch, full, lazy, label):
+    assert np.array_equal(lazy.n_accepted, full.n_accepted), label
+    assert np.array_equal(lazy.tokens, full.tokens), label
+    N = batch.n_draft
+    st = _stages(N)
+    for s in range(batch.batch):
+        T = float(batch.temperature[s])
+        j = int(full.n_accepted[s])
+        if j < 0 or library_rejects_temperature(T):
+            assert np.all(lazy.argmax[s] == -1) and np.all(np.isnan(lazy.lse[s])), (label, s)
+            continue
+        hi_last = [hi for lo, hi in st if lo <= min(j, N - 1)][-1]
+        read = np.zeros(2 * N + 1, bool)
+        if T > 0:
+            read[:hi_last] = True
+        read[N:N + hi_last] = True
+        if hi_last == N:
+            read[2 * N] = True
+        assert np.array_equal(lazy.argmax[s][read], full.argmax[s][read]), (label, s)
+        assert np.array_equal(lazy.lse[s][read].view(np.uint32), full.lse[s][read].view(np.uint32)), (label, s)
+        assert np.all(lazy.argmax[s][~read] == -1) and np.all(np.isnan(lazy.lse[s][~read])), (label, s)
+
+
+CASES = [
+    ("b64_n5_v128256_bf16", 16, 3 * 32768 + 517),
+    ("b256_n7_v151936_bf16_mixed", 32, 2 * 32768 + 4099),
+    ("b32_n16_v128256_f32", 8, 3 * 16384 + 37),
+    ("b1_n5_v32000_f32", 1, 32000),
+    ("tiny_b1_n4_v16_f32", 1, 16),
+]
+
+
+@pytest.mark.parametrize("name,batch,vocab", CASES, ids=[c[0] for c in CASES])
+def test_lazy_matches_full(name, batch, vocab):
+    wl = synth.workload(name).with_sizes(batch=batch, vocab=vocab)
+    for seed in range(4 if batch > 1 else 24):
+        b = synth.make_batch(wl, seed=200 + seed)
+        full, lazy = _both(b)
+        _check(b, full, lazy, f"{name} seed={seed}")
+        compare(b, lazy, run_oracle(b)).check(f"lazy {name} seed={seed}")
+
+
+@pytest.mark.parametrize("name", ["b64_n5_v128256_bf16", "b256_n7_v151936_bf16_mixed", "b32_n16_v128256_f32"])
+def test_lazy_full_size(name):
+    wl = synth.workload(name)
+    b = synth.make_batch(wl, seed=7)
+    full, lazy = _both(b)
+    _check(b, full, lazy, name)
+    compare(b, lazy, run_oracle(b)).check(f"lazy full {name}")
+    _say(f"[lazy] {name}: mean n_accepted {np.mean(lazy.n_accepted):.2f}")
+
+
+@pytest.mark.parametrize("n_draft", [1, 2, 3, 9, 64])
+def test_lazy_stage_counts(n_draft):
+    wl = synth.Workload("lazyN", 14, 6, n_draft, 700, "bf16", 1.0, 1.1, (0.01, 0.2), (1.0, 0.0))
+    b = synth.make_batch(wl, seed=n_draft)
+    full, lazy = _both(b)
+    _check(b, full, lazy, f"N={n_draft}")
+
+
+def test_lazy_invalid_and_repeated_calls():
+    """Invalid sequences, then calls of other shapes on the same handle (the
+    stage states of one call never leak into the next)."""
+    wl = synth.workload("b1_n5_v32000_f32").with_sizes(batch=7, vocab=500, n_draft=5)
+    with Verifier(9, 8, 500, "f32") as v:
+        for B, N, seed in ((7, 5, 1), (9, 8, 2), (3, 2, 3), (7, 5, 4)):
+            wl2 = synth.Workload("lazyR", 15, B, N, 500, "f32", 2.5, 1.1, (0.1, 1.5), (1.0, 0.0))
+            b = synth.make_batch(wl2, seed)
+            if seed == 1:
+                b.temperature[1] = np.float32(np.nan)
+                b.draft_tokens[2, 3] = 999
+                b.temperature[4] = np.float32(1e-30)
+            full, lazy = _both(b, v)
+            _check(b, full, lazy, f"B={B} N={N}")
+
+
+def test_lazy_graph_replay():
+    """A captured lazy call (its stage launches) replays with new inputs correctly."""
+    dev = require_gpu()
+    wl = synth.workload("b32_n16_v128256_f32").with_sizes(batch=6, vocab=5000)
+    batches = [synth.make_batch(wl, s) for s in (31, 32)]
+    B, N = wl.batch, wl.n_draft
+    with Verifier(B, N, wl.vocab, wl.dtype) as v:
+        static = to_device(batches[0], dev)
+        out_t = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+        want = []
+        for bt in batches:
+            src = to_device(bt, dev)
+            t, n = v.verify(**src)
+            torch.cuda.synchronize()
+            want.append((t.cpu().numpy(), n.cpu().numpy()))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            v.verify_lazy(**static, out_tokens=out_t, out_n_accepted=out_n)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            v.verify_lazy(**static, out_tokens=out_t, out_n_accepted=out_n)
+        for rep in range(4):
+            i = rep % 2
+            src = to_device(batches[i], dev)
+            for k in static:
+                static[k].copy_(src[k])
+            out_t.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out_t.cpu().numpy(), want[i][0]), rep
+            assert np.array_equal(out_n.cpu().numpy(), want[i][1]), rep
