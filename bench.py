@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also", default="b256_n7_v151936_bf16_mixed,b32_n16_v128256_f32",
                     help="comma-separated workloads also timed (reported under 'also'); empty for none")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the lines of the steps around the verification (lazy verification, draft-side "
+                         "draw, acceptance rates, KV-cache commit)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MB (8 times) so that a "
                          "rocprofv3 --pmc run of this command also measures a copy of known size")
@@ -275,7 +278,30 @@ def device_logits(torch, a, dtype, dev):
     return t.to(dev)
 
 
-def measure(torch, dev, name: str, args) -> dict:
+def lazy_bytes(batch, n_accepted) -> dict:
+    """Rows the lazy verification reads: for each sequence the draft and target
+    rows of every stage up to the one where it ends (stages [0,1), [1,2),
+    [2,4), ...), target row N if that is the last stage, plus the draw's
+    re-read (as for the full path)."""
+    B, N, V = batch.batch, batch.n_draft, batch.vocab
+    e = 4 if batch.dtype == "f32" else 2
+    stages, lo = [], 0
+    while lo < N:
+        hi = 1 if lo == 0 else min(N, 2 * lo)
+        stages.append((lo, hi))
+        lo = hi
+    rows = 0
+    for s in range(B):
+        T, j = float(batch.temperature[s]), int(n_accepted[s])
+        if j < 0 or not np.isfinite(T) or T < 0:
+            continue
+        hi_last = [hi for lo, hi in stages if lo <= min(j, N - 1)][-1]
+        rows += hi_last * (2 if T > 0 else 1) + (1 if hi_last == N else 0)
+    reread = algorithmic_bytes(batch, n_accepted)["reread"]
+    return dict(stats=rows * V * e, reread=reread, total=rows * V * e + reread)
+
+
+def measure(torch, dev, name: str, args, lazy: bool = False) -> dict:
     """Time K calls of workload `name`; returns the numbers the JSON line reports."""
     import synth
     from speculative_sampling_verification_specv_amd import Verifier
@@ -299,7 +325,7 @@ def measure(torch, dev, name: str, args) -> dict:
     # Each input copy's call is checked once and then re-enqueued directly
     # (what a serving loop that refills its buffers does), so the timed loop
     # measures the GPU, not Python's per-call argument checks.
-    calls = [v.bind(d, t, out_tokens=out_tokens, out_n_accepted=out_n, **small) for d, t in sets]
+    calls = [v.bind(d, t, out_tokens=out_tokens, out_n_accepted=out_n, lazy=lazy, **small) for d, t in sets]
 
     def step(k):
         calls[k % copies]()
@@ -309,6 +335,8 @@ def measure(torch, dev, name: str, args) -> dict:
     torch.cuda.synchronize()
     n_acc = out_n.cpu().numpy()
     nbytes = algorithmic_bytes(batch, n_acc)
+    if lazy:
+        nbytes = dict(nbytes, **lazy_bytes(batch, n_acc))
 
     # Timed region: K whole calls, bracketed by device synchronisation, with
     # HIP events on the launch stream (torch's current stream, which the
@@ -339,6 +367,92 @@ def measure(torch, dev, name: str, args) -> dict:
         achieved=kernel_bytes / (stage_ms[dominant] * 1e-3) / 1e9,
         positions=B * N, n_accepted_mean=float(np.mean(n_acc)),
     )
+
+
+def _time_calls(torch, dev, step, steps: int, warmup: int) -> float:
+    """Mean ms of one call over `steps` back-to-back calls (events on the launch stream)."""
+    for k in range(warmup):
+        step(k)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_extras(torch, dev, args) -> dict:
+    """The steps around the verification, each on a workload-shaped input:
+    lazy verification (the long-draft and 64-sequence workloads), the
+    draft-side draw (the 64-sequence workload's draft rows), acceptance rates
+    after a verification, and the KV-cache commit of the accepted drafts."""
+    import synth
+    from speculative_sampling_verification_specv_amd import Verifier, _lib
+
+    out = {}
+    for name in ("b32_n16_v128256_f32", "b64_n5_v128256_bf16"):
+        m = measure(torch, dev, name, args, lazy=True)
+        out[f"lazy_{name}"] = {
+            "positions_per_sec": m["positions"] / (m["ms_per_step"] * 1e-3), "ms_per_step": m["ms_per_step"],
+            "bytes_per_call": m["nbytes"]["total"], "hbm_gbs": m["nbytes"]["total"] / (m["ms_per_step"] * 1e-3) / 1e9,
+            "mean_n_accepted": m["n_accepted_mean"]}
+    # Draft-side draw: 64 rows of the 64-sequence bf16 workload's draft logits.
+    wl = synth.workload("b64_n5_v128256_bf16")
+    rows = synth.make_sample_rows(wl, args.seed, 64)
+    V = wl.vocab
+    row_bytes = 64 * V * 2
+    copies = max(3, math.ceil(512e6 / row_bytes))
+    base = torch.from_numpy(np.ascontiguousarray(rows.logits).view(np.int16)).view(torch.bfloat16).to(dev)
+    logit_sets = [base] + [base.clone() for _ in range(copies - 1)]
+    temp = torch.from_numpy(rows.temperature).to(dev)
+    uni = torch.from_numpy(rows.uniforms).to(dev)
+    tok = torch.empty(64, dtype=torch.int32, device=dev)
+    with Verifier(64, 1, V, "bf16") as v:
+        ms = _time_calls(torch, dev, lambda k: v.sample(logit_sets[k % copies], temp, uni, tok), args.steps, args.warmup)
+    out["sample_b64_v128256_bf16"] = {"rows_per_sec": 64 / (ms * 1e-3), "ms_per_call": ms,
+                                      "bytes_per_call": 2 * row_bytes,
+                                      "hbm_gbs": 2 * row_bytes / (ms * 1e-3) / 1e9}
+    del logit_sets
+    # Acceptance rates after a verification (64-sequence workload). The rates
+    # read the rows again; copies of the same logits are rotated (the
+    # verification's row statistics hold for each), so the rows come from HBM.
+    batch = synth.make_batch(wl, args.seed)
+    d = device_logits(torch, batch.draft_logits, batch.dtype, dev)
+    t = device_logits(torch, batch.target_logits, batch.dtype, dev)
+    n_copies = max(3, math.ceil(512e6 / (d.numel() * 2 + t.numel() * 2)))
+    sets = [(d, t)] + [(d.clone(), t.clone()) for _ in range(n_copies - 1)]
+    small = dict(draft_tokens=torch.from_numpy(batch.draft_tokens).to(dev),
+                 accept_uniforms=torch.from_numpy(batch.accept_uniforms).to(dev),
+                 sample_uniforms=torch.from_numpy(batch.sample_uniforms).to(dev),
+                 temperature=torch.from_numpy(batch.temperature).to(dev))
+    B, N = batch.batch, batch.n_draft
+    with Verifier(B, N, V, batch.dtype) as v:
+        _, n_acc = v.verify(d, t, **small)
+        ms = _time_calls(torch, dev, lambda k: v.acceptance_rates(*sets[k % n_copies], small["draft_tokens"],
+                                                                  small["temperature"]), args.steps, args.warmup)
+        n_acc = n_acc.cpu().numpy()
+    del sets
+    rate_bytes = B * 2 * N * V * 2
+    out["rates_b64_n5_v128256_bf16"] = {"ms_per_call": ms, "bytes_per_call": rate_bytes,
+                                        "hbm_gbs": rate_bytes / (ms * 1e-3) / 1e9}
+    # KV-cache commit of the accepted drafts of that batch: 32 layers of keys and
+    # values (64 planes) of 8 heads x 128 bf16 (2 KB per entry), cache of 256.
+    P, E, L = 64, 2048, 256
+    cache = torch.empty((P, B, L, E // 2), dtype=torch.bfloat16, device=dev)
+    scratch = torch.randn((P, B, N, E // 2), device=dev).to(torch.bfloat16)
+    n_t = torch.from_numpy(n_acc.astype(np.int32)).to(dev)
+    lens = torch.full((B,), 100, dtype=torch.int32, device=dev)
+    new_len = torch.empty_like(lens)
+    ms = _time_calls(torch, dev, lambda k: _lib.specv_kv_commit(cache, lens, scratch, n_t, new_len),
+                     args.steps, args.warmup)
+    kv_bytes = 2 * int(np.clip(n_acc, 0, None).sum()) * P * E
+    out["kv_commit_b64_p64_e2048"] = {"ms_per_call": ms, "bytes_per_call": kv_bytes,
+                                      "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                                      "entries_committed": int(np.clip(n_acc, 0, None).sum()) * P}
+    return out
 
 
 def main() -> int:
@@ -411,6 +525,8 @@ def main() -> int:
         }
     if also:
         line["also"] = also
+    if not args.no_extras:
+        line["extras"] = measure_extras(torch, dev, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(batch, args.workload, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
