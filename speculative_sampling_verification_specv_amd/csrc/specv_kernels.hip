@@ -1730,7 +1730,11 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
     }
     critical_path();
     trace_at(1, b, 0);
-    finish<T>(P, sh, b, s);
+    // The decision read again from LDS rather than kept in registers across
+    // the member's work (where it made the fp32 build spill).
+    asm volatile("" ::: "memory");
+    const SeqInfo s_again = g_seq;
+    finish<T>(P, sh, b, s_again);
     trace_at(1, b, 4);
   }
 }

@@ -1,8 +1,12 @@
 """Host check of the kernels' fp64 exponentials (specv_math.h), built with g++.
 
-The draw sums fp64 exps of (z - max)/T; its parity with the oracle needs them
-to ~1e-10 relative. The header states 1e-13 for the polynomial form and about
-1 ulp for the table form, whose table entries are correctly rounded.
+The draw sums fp64 exps of (z - max)/T. A relative error e in them moves the
+draw's CDF edges by about e of the mass, so a draw flips only when u*S lies
+within that of an edge: about 2e per token with weight above it, 2.6e-8 per
+draw for e = 1e-13 at 1.3e5 tokens, against an allowed 1e-4 of cases (and each
+such flip has a margin far below 1e-5). The header states 1e-13 for the
+polynomial form (the decision's ratio) and 2.5e-13 for the table form (the
+draw), whose table entries are correctly rounded.
 """
 
 import os
@@ -27,7 +31,7 @@ def exp_report(tmp_path_factory):
     return dict(line.split(None, 1) for line in text.strip().splitlines())
 
 
-@pytest.mark.parametrize("form,bound", [("", 1e-13), ("tab_", 5e-16)])
+@pytest.mark.parametrize("form,bound", [("", 1e-13), ("tab_", 2.5e-13)])
 def test_relative_error_bound(exp_report, form, bound):
     assert float(exp_report[form + "max_rel_err"].split()[0]) < bound
 
@@ -41,11 +45,13 @@ def test_special_values(exp_report, form):
     assert float(exp_report[form + "exp_far_below"]) == 0.0
 
 
-@pytest.mark.parametrize("form", ["", "tab_"])
-def test_subnormal_range(exp_report, form):
-    # Below -708 the results are subnormal or tiny normals; they stay within a
-    # few units of the smallest subnormal (4.9e-324) of the exact value.
-    assert float(exp_report[form + "subnormal_abs_err"].split()[0]) <= 2.0e-323
+@pytest.mark.parametrize("form,bound", [("", 2.0e-323), ("tab_", 6.0e-321)])
+def test_subnormal_range(exp_report, form, bound):
+    # Below -708 the results are subnormal or tiny normals: the polynomial form
+    # stays within a few units of the smallest subnormal (4.9e-324) of the
+    # exact value, the table form within its relative bound of the largest of
+    # them (2.5e-13 * 2.2e-308).
+    assert float(exp_report[form + "subnormal_abs_err"].split()[0]) <= bound
 
 
 def test_table_correctly_rounded(exp_report):
