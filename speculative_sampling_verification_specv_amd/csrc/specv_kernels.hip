@@ -1152,7 +1152,10 @@ __device__ __forceinline__ DrawRows<T> draw_rows(const Params& P, int b, const S
 // Argument z/T - max/T of a token's exp; every step forms it the same way.
 __device__ __forceinline__ double exp_arg(float z, double nm, double inv_t) { return fma(double(z), inv_t, nm); }
 
-// max(0, et/Zt - ed/Zd) with rt = 1/Zt, rd = 1/Zd; the rounding is spelled
+// The residual weight max(0, et/Zt - ed/Zd) scaled by Zt*Zd: max(0, et*rt -
+// ed*rd) with rt = Zd, rd = Zt (the draw only compares weights with each
+// other and with u times their sum, so a common scale changes nothing, and
+// it spares two divisions on the finisher's path). The rounding is spelled
 // out so every place that forms a weight gets the same bits.
 __device__ __forceinline__ double resid_weight(double et, double ed, double rt, double rd) {
   return fmax(0.0, fma(et, rt, -__dmul_rn(ed, rd)));
@@ -1390,8 +1393,8 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
 
 // Exact weights of sub-chunk `sub` of member c (whole workgroup): each thread
 // takes kPer/8 consecutive tokens; returns this thread's weights' sum and its
-// weights through w. rd = 0 after a rejection gives et/Zt instead of the
-// residual. The exps are the members' (the same function and table), bit
+// weights through w. rd = 0 after a rejection gives et*rt (q, scaled)
+// instead of the residual. The exps are the members' (the same function and table), bit
 // for bit.
 template <typename T>
 __device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>& d, const double* tab, int c, int sub,
@@ -1538,14 +1541,15 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
   if (tid < 64) {
     // Normalisers (fixed-order DPP sums over the members), then member lane's
-    // sub-chunk weights: A/Zt - B/Zd of the certain tokens plus the listed
-    // uncertain ones in token order.
+    // sub-chunk weights scaled by Zt*Zd: A*Zd - B*Zt of the certain tokens
+    // plus the listed uncertain ones in token order (the bonus: A, scaled by
+    // Zt).
     double zt = mine ? bits_to_double(r[MemberRec::kZt]) : 0.0;
     double zd = mine ? bits_to_double(r[MemberRec::kZd]) : 0.0;
     zt = wave_sum(zt);
     zd = wave_sum(zd);
-    const double rt = 1.0 / zt;
-    const double rd = residual ? 1.0 / zd : 0.0;
+    const double rt = residual ? zd : 1.0;
+    const double rd = residual ? zt : 0.0;
     const int nunc = mine ? int(r[MemberRec::kNUnc]) : 0;
 #pragma unroll
     for (int k = 0; k < kSubs; ++k) {
