@@ -109,7 +109,8 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
   const size_t off_state = off;
   off = align_up(off + size_t(2) * max_batch * sizeof(int), 256);
   const size_t off_rates = off;
-  if (rates) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nch * sizeof(double), 256);
+  const int nrc = specv::ceil_div(vocab, specv::rate_chunk_elems(dtype));
+  if (rates) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nrc * sizeof(double), 256);
   if (ws != nullptr) {
     ws->partials = base + off_partials;
     ws->seq = base + off_seq;
@@ -120,6 +121,7 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
     ws->rate_parts = rates ? reinterpret_cast<double*>(base + off_rates) : nullptr;
     ws->lazy_state = reinterpret_cast<int*>(base + off_state);
     ws->n_stat_chunks = nch;
+    ws->n_rate_chunks = nrc;
     ws->n_members = nm;
     ws->stat_chunk = chunk;
   }

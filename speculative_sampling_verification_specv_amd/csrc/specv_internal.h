@@ -28,6 +28,11 @@ constexpr float kMinTemperature = 0x1p-60f;
 
 inline int stat_chunk_elems(int dtype) { return kStatBytes / (dtype == 0 ? 4 : 2); }
 
+// Acceptance-rate item: 32 KB of a draft row and the same span of its target
+// row (both in flight at once: 16 16-byte loads per thread).
+constexpr int kRateBytes = 32768;
+inline int rate_chunk_elems(int dtype) { return kRateBytes / (dtype == 0 ? 4 : 2); }
+
 constexpr int kCounterStride = 64;
 
 // What a sampled sequence's draw does: a residual or bonus draw, nothing because an
@@ -54,9 +59,10 @@ struct Workspace {
   // kCounterStride ints (its own 256-byte line), so that atomics on different
   // sequences' counters never contend for a line.
   int* draw_done;    // [max_batch * kCounterStride]
-  double* rate_parts;  // [max_batch][max_draft][n_stat_chunks] acceptance-rate partial sums (handles only)
+  double* rate_parts;  // [max_batch][max_draft][n_rate_chunks] acceptance-rate partial sums (handles only)
   int* lazy_state;     // [2][max_batch] lazy stages' per-sequence states
   int n_stat_chunks;
+  int n_rate_chunks;
   int resident_blocks;  // workgroups of the verification kernel the device holds at once
   int n_members;     // draw members per sequence
   int stat_chunk;    // logits per row-statistics item

@@ -9,9 +9,10 @@
 // log-normalisers the verification left in the workspace (fp64), so the
 // rates take one more pass over the 2N draft and target rows:
 //
-//   rate_parts_kernel    one workgroup per (sequence, position, 64 KB item of
-//                        the row): sum of min(p, q) over the item, stored as
-//                        one fp64 partial. Bandwidth-bound.
+//   rate_parts_kernel    one workgroup per (sequence, position, 32 KB span of
+//                        the draft row and the same span of the target row):
+//                        sum of min(p, q) over the span, stored as one fp64
+//                        partial. Bandwidth-bound.
 //   rate_finish_kernel   one wave per sequence: the partials summed in item
 //                        order, tau from the alphas. At T = 0 both
 //                        distributions are point masses (the draft token, the
@@ -70,47 +71,71 @@ __device__ __forceinline__ float min_pq(float zd, float zt, double c, double ld,
   return fminf(p, q);
 }
 
+// A 16-byte load marked non-temporal: each logit is read once.
+typedef unsigned RateV4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const RateV4 t = __builtin_nontemporal_load(reinterpret_cast<const RateV4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void rate_parts_kernel(RateParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void rate_parts_kernel(RateParams P) {
   __shared__ double red[4];
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLoads = kRateBytes / 16 / 256;  // 16-byte loads per thread and row
   const int N = P.n_draft, R = 2 * N + 1;
   const int c = int(blockIdx.x % unsigned(P.nch));
   const int bi = int(blockIdx.x / unsigned(P.nch));
   const int i = bi % N, b = bi / N;
+  const int tid = int(threadIdx.x);
   double* out = P.parts + (int64_t(b) * N + i) * P.nch + c;
   const float t = P.temperature[b];
   const double ld = P.row_lse[int64_t(b) * R + i], lt = P.row_lse[int64_t(b) * R + N + i];
   if (!sampled_temperature(t) || isnan(ld) || isnan(lt)) {
-    if (threadIdx.x == 0) *out = NAN;
+    if (tid == 0) *out = NAN;
     return;
   }
-  const double cf = kLog2eD / double(t);
-  const double nld = -ld * kLog2eD, nlt = -lt * kLog2eD;
   const T* drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + i) * P.vocab;
   const T* trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + i) * P.vocab;
   const int e0 = c * P.chunk, e1 = min(P.vocab, e0 + P.chunk);
-  constexpr int kVec = Elem<T>::kVec;
-  float acc = 0.0f;
-  int tail = e0;
-  if (P.vec_ok) {
-    // Rows start 16-byte aligned and so does every item (chunk * element size is 64 KB).
-    const int nv = (e1 - e0) / kVec;
+  // Every 16-byte load of both rows is issued (at a clamped, valid index)
+  // before any arithmetic, so the item's 64 KB are in flight at once.
+  const int nv = P.vec_ok ? (e1 - e0) / kVec : 0;
+  uint4 xd[kLoads], xt[kLoads];
+  if (nv > 0) {
     const uint4* dv = reinterpret_cast<const uint4*>(drow + e0);
     const uint4* tv = reinterpret_cast<const uint4*>(trow + e0);
-    for (int v = threadIdx.x; v < nv; v += 256) {
-      const uint4 xd = dv[v], xt = tv[v];
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) acc += min_pq(Elem<T>::get(xd, k), Elem<T>::get(xt, k), cf, nld, nlt);
+    for (int u = 0; u < kLoads; ++u) {
+      const int v = min(tid + u * 256, nv - 1);
+      xd[u] = load_stream(dv + v);
+      xt[u] = load_stream(tv + v);
     }
-    tail = e0 + nv * kVec;
   }
-  for (int e = tail + int(threadIdx.x); e < e1; e += 256) acc += min_pq(Elem<T>::at(drow, e), Elem<T>::at(trow, e), cf, nld, nlt);
+  const double cf = kLog2eD / double(t);
+  const double nld = -ld * kLog2eD, nlt = -lt * kLog2eD;
+  float acc = 0.0f;
+  if (nv > 0) {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      // Each group taken as it arrives: the empty asm keeps the compiler from
+      // widening every logit of the item to fp64 ahead of time (which needs
+      // far more registers than the loads themselves).
+      asm volatile("" : "+v"(xd[u].x), "+v"(xd[u].y), "+v"(xd[u].z), "+v"(xd[u].w));
+      asm volatile("" : "+v"(xt[u].x), "+v"(xt[u].y), "+v"(xt[u].z), "+v"(xt[u].w));
+      float part = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) part += min_pq(Elem<T>::get(xd[u], k), Elem<T>::get(xt[u], k), cf, nld, nlt);
+      acc += tid + u * 256 < nv ? part : 0.0f;
+    }
+  }
+  for (int e = e0 + nv * kVec + tid; e < e1; e += 256) acc += min_pq(Elem<T>::at(drow, e), Elem<T>::at(trow, e), cf, nld, nlt);
   // Fixed-order block sum in fp64.
   double s = acc;
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) *out = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) *out = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 __global__ __launch_bounds__(64) void rate_finish_kernel(RateParams P) {
@@ -165,11 +190,11 @@ hipError_t launch_rates(const RatesArgs& a, const Workspace& w, hipStream_t stre
   p.batch = a.batch;
   p.n_draft = a.n_draft;
   p.vocab = a.vocab;
-  p.nch = w.n_stat_chunks;
-  p.chunk = w.stat_chunk;
+  p.chunk = rate_chunk_elems(a.dtype);
+  p.nch = ceil_div(a.vocab, p.chunk);
   const int esz = a.dtype == 0 ? 4 : 2;
   p.vec_ok = (int64_t(a.vocab) * esz) % 16 == 0;
-  const int64_t blocks = int64_t(a.batch) * a.n_draft * w.n_stat_chunks;
+  const int64_t blocks = int64_t(a.batch) * a.n_draft * p.nch;
   if (a.dtype == 0)
     hipLaunchKernelGGL(rate_parts_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   else
