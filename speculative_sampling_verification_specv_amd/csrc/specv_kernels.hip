@@ -490,7 +490,7 @@ struct Params {
   uint32_t wait_ticks;  // bound of every wait, in ticks of the 100 MHz wall clock
   // The positions [lo, hi) this launch verifies: bits 0-7 lo, 8-15 hi, bit 16
   // the parity of a lazy stage, bit 17 set for a lazy stage. A whole call is
-  // [0, N) and not lazy. A lazy call runs stages [0,1), [1,2), [2,4), ... as
+  // [0, N) and not lazy. A lazy call runs stages [0,2), [2,8), [8,32), ... as
   // launches of their own; stage k reads each sequence's state from
   // state[parity * batch + b] (the position it is alive at, -1 when done) and
   // writes the next stage's to state[(1 - parity) * batch + b].

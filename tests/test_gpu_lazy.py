@@ -24,7 +24,7 @@ def _say(*a):
 def _stages(N):
     out, lo = [], 0
     while lo < N:
-        hi = 1 if lo == 0 else min(N, 2 * lo)
+        hi = min(N, 2) if lo == 0 else min(N, 4 * lo)
         out.append((lo, hi))
         lo = hi
     return out
