@@ -135,12 +135,14 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
  * 채점합니다", section "몇 글자를 미리 쓰게 할까요": position k is reached with
  * probability alpha^k, so most rows past an early rejection need never be
  * read). The positions go in stages [0,2), [2,8), [8,32), ... up to
- * n_draft, each a kernel launch of its own on `stream` over the sequences
- * still alive at its first position; the row statistics, the accept tests
- * and the draw are those of specv_verify, so tokens and n_accepted are
- * identical to its. Bytes read fall from 2N+1 rows per sequence toward the
- * rows up to the first rejection (plus the draw's re-read), at the cost of
- * one launch per stage (1 + ceil(log4(n_draft / 2)) of them). Afterwards
+ * n_draft, one after the other in one kernel launch on `stream`: a stage
+ * reads the rows of the sequences still going on at its first position,
+ * which its workgroups learn from the previous stage's decisions. The row
+ * statistics, the accept tests and the draw are those of specv_verify, so
+ * tokens and n_accepted are identical to its. Bytes read fall from 2N+1
+ * rows per sequence toward the rows up to the first rejection (plus the
+ * draw's re-read). A sequence whose wait gave up (-2) may keep the row
+ * diagnostics of its earlier stages. Afterwards
  * specv_row_stats reports NaN / -1 for the rows not read, and
  * specv_acceptance_rates NaN for the positions not reached.
  * Errors: as specv_verify.

@@ -85,10 +85,11 @@ __global__ void narrow_to_float(const double* in, float* out, size_t n) {
 
 // Lays out a workspace for calls up to (max_batch, max_draft) at `vocab` and
 // `dtype` from `base` (which may be null to only size it); returns its size
-// in bytes. The regions are 256-byte aligned if `base` is. `rates`: also the
-// acceptance-rate partials (handles only).
+// in bytes. The regions are 256-byte aligned if `base` is. `handle`: also
+// the acceptance-rate partials and the lazy calls' go-on words (handles
+// only).
 size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char* base, specv::Workspace* ws,
-                        bool rates) {
+                        bool handle) {
   const int chunk = specv::stat_chunk_elems(dtype);
   const int nch = specv::ceil_div(vocab, chunk);
   const int nm = specv::ceil_div(vocab, specv::member_elems(dtype));
@@ -106,11 +107,13 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
   off = align_up(off + rows * sizeof(int), 256);
   const size_t off_counters = off;
   off = align_up(off + size_t(max_batch) * specv::kCounterStride * sizeof(int), 256);
-  const size_t off_state = off;
-  off = align_up(off + size_t(2) * max_batch * sizeof(int), 256);
+  const size_t off_alive = off;
+  if (handle)
+    off = align_up(off + size_t(max_batch) * (size_t(2 * max_draft + 1) * nch + specv::kMaxLazyStages) * sizeof(uint64_t),
+                   256);
   const size_t off_rates = off;
   const int nrc = specv::ceil_div(vocab, specv::rate_chunk_elems(dtype));
-  if (rates) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nrc * sizeof(double), 256);
+  if (handle) off = align_up(off + size_t(max_batch) * size_t(max_draft) * nrc * sizeof(double), 256);
   if (ws != nullptr) {
     ws->partials = base + off_partials;
     ws->seq = base + off_seq;
@@ -118,8 +121,8 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
     ws->row_lse = reinterpret_cast<double*>(base + off_lse);
     ws->row_argmax = reinterpret_cast<int*>(base + off_argmax);
     ws->draw_done = reinterpret_cast<int*>(base + off_counters);
-    ws->rate_parts = rates ? reinterpret_cast<double*>(base + off_rates) : nullptr;
-    ws->lazy_state = reinterpret_cast<int*>(base + off_state);
+    ws->rate_parts = handle ? reinterpret_cast<double*>(base + off_rates) : nullptr;
+    ws->alive = handle ? reinterpret_cast<uint64_t*>(base + off_alive) : nullptr;
     ws->n_stat_chunks = nch;
     ws->n_rate_chunks = nrc;
     ws->n_members = nm;
@@ -130,11 +133,11 @@ size_t layout_workspace(int max_batch, int max_draft, int vocab, int dtype, char
 
 // Whether a launch of (batch, n_draft) at `vocab` and `dtype` has a grid the
 // runtime takes (one workgroup per row-statistics item, decision and draw
-// member, below 2^31).
+// member, below 2^31; a lazy call has a decision per stage).
 bool grid_fits(int batch, int n_draft, int vocab, int dtype) {
   const int64_t nch = specv::ceil_div(vocab, specv::stat_chunk_elems(dtype));
   const int64_t nm = specv::ceil_div(vocab, specv::member_elems(dtype));
-  return int64_t(batch) * (2 * n_draft + 1) * nch + int64_t(batch) * (nm + 1) < (int64_t(1) << 31);
+  return int64_t(batch) * (2 * n_draft + 1) * nch + int64_t(batch) * (nm + specv::kMaxLazyStages) < (int64_t(1) << 31);
 }
 
 }  // namespace
@@ -244,8 +247,6 @@ int specv_verify(specv_handle h, int batch, int n_draft, const void* draft_logit
   a.tag = h->next_tag;
   a.debug = h->debug;
   a.wait_ticks = h->wait_ticks;
-  a.pos_lo = 0;
-  a.pos_hi = n_draft;
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, h->timing ? h->events : nullptr, &stages) != hipSuccess) return SPECV_EHIP;
   h->next_tag = next_call_tag(h->next_tag);
@@ -289,24 +290,13 @@ int specv_verify_lazy(specv_handle h, int batch, int n_draft, const void* draft_
   a.debug = h->debug;
   a.wait_ticks = h->wait_ticks;
   a.lazy = 1;
-  a.state = h->ws.lazy_state;
-  // Stages [0,2), [2,8), [8,32), ...: each a launch of its own, over the
-  // sequences still alive at its first position. (Every stage pays a launch
-  // and a decision -> draw chain; of the schedules measured, [0,1), [1,2),
-  // [2,4), ... and [0,1), [1,N) and [0,2), [2,N) and [0,2), [2,6), [6,18),
-  // this one was fastest or level at every workload.)
-  int k = 0;
-  for (int lo = 0; lo < n_draft; ++k) {
-    const int hi = lo == 0 ? std::min(n_draft, 2) : std::min(n_draft, 4 * lo);
-    a.pos_lo = lo;
-    a.pos_hi = hi;
-    a.parity = k & 1;
-    a.tag = h->next_tag;
-    int stages = 0;
-    if (specv::launch_verify(a, h->ws, s, nullptr, &stages) != hipSuccess) return SPECV_EHIP;
-    h->next_tag = next_call_tag(h->next_tag);
-    lo = hi;
-  }
+  a.tag = h->next_tag;
+  // One launch: the stages [0,2), [2,8), [8,32), ... one after the other in
+  // the launch order, each over the sequences still going on at its first
+  // position, then the draws.
+  int stages = 0;
+  if (specv::launch_verify(a, h->ws, s, nullptr, &stages) != hipSuccess) return SPECV_EHIP;
+  h->next_tag = next_call_tag(h->next_tag);
   h->last_batch = batch;
   h->last_n_draft = n_draft;
   h->timed_call = false;
@@ -339,8 +329,6 @@ int specv_sample(specv_handle h, int n_rows, const void* logits, const float* te
   a.temperature = temperature;
   a.out_tokens = out_tokens;
   a.out_n = nullptr;
-  a.pos_lo = 0;
-  a.pos_hi = 0;
   a.tag = h->next_tag;
   a.debug = h->debug;
   a.wait_ticks = h->wait_ticks;
@@ -581,8 +569,6 @@ extern "C" int specv_verify_static(int batch, int n_draft, int vocab, specv_dtyp
   a.tag = take_tag(sd.tag);
   a.debug = sd.debug;
   a.wait_ticks = sd.wait_ticks;
-  a.pos_lo = 0;
-  a.pos_hi = n_draft;
   int stages = 0;
   return specv::launch_verify(a, ws, s, nullptr, &stages) == hipSuccess ? SPECV_OK : SPECV_EHIP;
 }

@@ -35,16 +35,30 @@ inline int rate_chunk_elems(int dtype) { return kRateBytes / (dtype == 0 ? 4 : 2
 
 constexpr int kCounterStride = 64;
 
+// A lazy call verifies positions in stages [0,2), [2,8), [8,32), ... (each
+// stage's decision ends the sequences it rejects or completes, so later
+// stages read the rows of fewer sequences). Writes bounds[0..k] and returns
+// the number of stages k (at most kMaxLazyStages for n_draft <= 64).
+constexpr int kMaxLazyStages = 4;
+inline int lazy_stage_bounds(int n_draft, int* bounds) {
+  int k = 0, lo = 0;
+  bounds[0] = 0;
+  while (lo < n_draft && k < kMaxLazyStages) {
+    const int hi = lo == 0 ? (n_draft < 2 ? n_draft : 2) : (n_draft < 4 * lo ? n_draft : 4 * lo);
+    bounds[++k] = hi;
+    lo = hi;
+  }
+  return k;
+}
+
 // What a sampled sequence's draw does: a residual or bonus draw, nothing because an
 // input is invalid (-1 outputs), or nothing because a wait gave up (-2 outputs).
-// A lazy stage's sequence whose drafts so far are all accepted continues in the next stage (no draw yet).
 enum SeqMode : int {
   kModeNone = 0,
   kModeResidual = 1,
   kModeBonus = 2,
   kModeInvalid = 3,
-  kModeFailed = 4,
-  kModeContinue = 5
+  kModeFailed = 4
 };
 
 // Device workspace: records one launch writes and the next reads.
@@ -60,7 +74,7 @@ struct Workspace {
   // sequences' counters never contend for a line.
   int* draw_done;    // [max_batch * kCounterStride]
   double* rate_parts;  // [max_batch][max_draft][n_rate_chunks] acceptance-rate partial sums (handles only)
-  int* lazy_state;     // [2][max_batch] lazy stages' per-sequence states
+  uint64_t* alive;     // [max_batch][(2*max_draft+1)*n_stat_chunks + kMaxLazyStages] lazy calls' go-on words (handles only)
   int n_stat_chunks;
   int n_rate_chunks;
   int resident_blocks;  // workgroups of the verification kernel the device holds at once
@@ -84,11 +98,8 @@ struct VerifyArgs {
   uint32_t tag;         // the call's number (never 0), carried by every hand-off word
   uint32_t debug;       // also check that the uniforms lie in [0, 1)
   uint64_t wait_ticks;  // bound of every wait between workgroups, in wall-clock ticks
-  // Positions [pos_lo, pos_hi) of this launch ([0, n_draft) for a whole
-  // call); a lazy stage (lazy != 0) reads and writes per-sequence states in
-  // `state` ([2][batch] ints, read half `parity`).
-  int pos_lo = 0, pos_hi = 0, lazy = 0, parity = 0;
-  int* state = nullptr;
+  // Nonzero: the lazy verification (stages of positions, one launch).
+  int lazy = 0;
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -92,8 +92,6 @@ __device__ __forceinline__ void trace(int, int) {}
 
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__shared__ int g_vote[kThreads / 64];
-
 // Uniform ORs of two per-thread flags over the workgroup (bit 0: a, bit 1: b).
 __shared__ int g_vote2[kThreads / 64];
 __device__ __forceinline__ int block_any2(bool a, bool b) {
@@ -107,17 +105,6 @@ __device__ __forceinline__ int block_any2(bool a, bool b) {
   return r;
 }
 
-// Uniform OR of a per-thread flag over the workgroup.
-__device__ __forceinline__ bool block_any(bool v) {
-  const unsigned long long m = __ballot(v);
-  if ((threadIdx.x & 63) == 0) g_vote[threadIdx.x >> 6] = m != 0ull;
-  barrier();
-  bool r = false;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) r = r || g_vote[w];
-  barrier();
-  return r;
-}
 
 // ---------------------------------------------------------------------------
 // Cross-lane steps within a wave through DPP (data-parallel primitives: an
@@ -208,16 +195,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // A read-only value at a uniform address, through the constant address space
 // (a scalar load: counted apart from the vector loads in flight, so using it
 // does not wait for them). Only for inputs the kernel never writes.
-template <typename V>
-__device__ __forceinline__ V load_uniform(const V* p);
-__device__ __forceinline__ uint32_t load_uniform_bits(const float* p) { return __float_as_uint(load_uniform(p)); }
-// A bfloat16 through the aligned 32-bit word holding it (scalar loads are at
-// least 32 bits wide).
-__device__ __forceinline__ uint32_t load_uniform_bits(const uint16_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t w = load_uniform(reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3)));
-  return (a & 2) ? (w >> 16) : (w & 0xffffu);
-}
 template <typename V>
 __device__ __forceinline__ V load_uniform(const V* p) {
   typedef const __attribute__((address_space(4))) V ConstV;
@@ -407,9 +384,6 @@ __device__ __forceinline__ void put_d(double* p, double v) { put_u64(p, double_t
 __device__ __forceinline__ void put_i(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
-  return uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
-}
 
 // Records written by one workgroup and read by another within a launch. Every
 // word is a 32-bit payload in its low half and the call's tag in its high half
@@ -477,8 +451,8 @@ struct Params {
   SeqRec* seq;           // [batch]
   MemberRec* records;    // [batch][nm]
   int* draw_done;        // [batch * kCounterStride] draw members done (zero between launches)
-  int items_per_seq;     // row-statistics items per sequence: (2N+1) * nch
-  int lag;               // draw members of sequence b follow the row statistics of sequence b + lag
+  int items_per_seq;     // whole call: row-statistics items per sequence, (2N+1) * nch
+  int lag;               // whole call: draw members of sequence b follow the row statistics of sequence b + lag
   int batch;
   int n_draft;
   int vocab;
@@ -488,14 +462,17 @@ struct Params {
   uint32_t flags;       // kVecOk: rows start 16-byte aligned; kDebug: check that the uniforms lie in [0, 1)
   uint32_t tag;         // this call's number (never 0): the high half of every hand-off word
   uint32_t wait_ticks;  // bound of every wait, in ticks of the 100 MHz wall clock
-  // The positions [lo, hi) this launch verifies: bits 0-7 lo, 8-15 hi, bit 16
-  // the parity of a lazy stage, bit 17 set for a lazy stage. A whole call is
-  // [0, N) and not lazy. A lazy call runs stages [0,2), [2,8), [8,32), ... as
-  // launches of their own; stage k reads each sequence's state from
-  // state[parity * batch + b] (the position it is alive at, -1 when done) and
-  // writes the next stage's to state[(1 - parity) * batch + b].
-  uint32_t stage;
-  int* state;
+  // A whole call verifies positions [0, N) in one stage. A lazy call runs
+  // stages s = 0 .. n_stages-1 over positions [st_bound[s], st_bound[s+1])
+  // in the same launch: the statistics groups of every sequence for stage 0,
+  // then for stage 1, ..., then every sequence's draw members. The decision
+  // of stage s leaves each workgroup of the sequence's stage s+1 a go-on word
+  // (see alive_item): 1 if its drafts so far are all accepted, else 0.
+  int lazy;
+  int n_stages;
+  int st_bound[kMaxLazyStages + 1];
+  int st_base[kMaxLazyStages + 1];  // lazy: first workgroup of stage s; st_base[n_stages]: the draw members
+  uint64_t* alive;                  // lazy: the go-on words, [batch][(2N+1) * nch + kMaxLazyStages]
 };
 constexpr uint32_t kVecOk = 1, kDebug = 2;
 
@@ -504,30 +481,34 @@ __device__ __forceinline__ PartialRec* partial_at(const Params& P, int b, int r,
   return P.partials + (int64_t(b) * (2 * P.n_draft + 1) + r) * P.nch + c;
 }
 
-__device__ __forceinline__ int stage_lo(const Params& P) { return int(P.stage & 0xffu); }
-__device__ __forceinline__ int stage_hi(const Params& P) { return int((P.stage >> 8) & 0xffu); }
-__device__ __forceinline__ bool stage_lazy(const Params& P) { return (P.stage >> 17) & 1u; }
-__device__ __forceinline__ int stage_parity(const Params& P) { return int((P.stage >> 16) & 1u); }
-// Rows a sequence reads in this launch: draft and target rows lo..hi-1, and
+// Stage s: positions [lo, hi).
+struct Stage {
+  int s, lo, hi;
+};
+__device__ __forceinline__ Stage stage_at(const Params& P, int s) { return Stage{s, P.st_bound[s], P.st_bound[s + 1]}; }
+// Rows a sequence reads in a stage: draft and target rows lo..hi-1, and
 // target row N if hi = N.
-__device__ __forceinline__ int stage_rows(const Params& P) {
-  return 2 * (stage_hi(P) - stage_lo(P)) + (stage_hi(P) == P.n_draft ? 1 : 0);
+__device__ __forceinline__ int stage_rows(const Params& P, const Stage& st) {
+  return 2 * (st.hi - st.lo) + (st.hi == P.n_draft ? 1 : 0);
 }
-// Row lr of this launch's rows as a row of the sequence (draft rows 0..N-1,
+// Row lr of a stage's rows as a row of the sequence (draft rows 0..N-1,
 // then target rows 0..N).
-__device__ __forceinline__ int global_row(const Params& P, int lr) {
-  const int lo = stage_lo(P), n = stage_hi(P) - lo;
-  return lr < n ? lo + lr : (lr < 2 * n ? P.n_draft + lo + (lr - n) : 2 * P.n_draft);
+__device__ __forceinline__ int global_row(const Params& P, const Stage& st, int lr) {
+  const int n = st.hi - st.lo;
+  return lr < n ? st.lo + lr : (lr < 2 * n ? P.n_draft + st.lo + (lr - n) : 2 * P.n_draft);
 }
-// Whether sequence b is verified in this launch (every sequence, except in a
-// lazy stage after the first: those still alive at its first position).
-__device__ __forceinline__ bool seq_alive(const Params& P, int b) {
-  if (!stage_lazy(P) || stage_lo(P) == 0) return true;
-  return load_uniform(P.state + stage_parity(P) * P.batch + b) == stage_lo(P);
+// The go-on words of a lazy call: one per row-statistics item (row r, chunk
+// c) and one per decision of stage s of sequence b, each written by the
+// sequence's decision of the stage before and taken (and zeroed) by the
+// workgroup it is for.
+__device__ __forceinline__ int64_t alive_per_seq(const Params& P) {
+  return int64_t(2 * P.n_draft + 1) * P.nch + kMaxLazyStages;
 }
-// A lazy stage records where sequence b goes on (-1: done).
-__device__ __forceinline__ void set_next_state(const Params& P, int b, int v) {
-  if (stage_lazy(P)) P.state[(1 - stage_parity(P)) * P.batch + b] = v;
+__device__ __forceinline__ uint64_t* alive_item(const Params& P, int b, int r, int c) {
+  return P.alive + int64_t(b) * alive_per_seq(P) + int64_t(r) * P.nch + c;
+}
+__device__ __forceinline__ uint64_t* alive_dec(const Params& P, int b, int s) {
+  return P.alive + int64_t(b) * alive_per_seq(P) + int64_t(2 * P.n_draft + 1) * P.nch + s;
 }
 
 // One row-statistics item: chunk c of row r of sequence b.
@@ -543,18 +524,16 @@ struct Item {
 };
 
 template <typename T>
-__device__ __forceinline__ Item item_at(const Params& P, int64_t t) {
+__device__ __forceinline__ Item item_at(const Params& P, const Stage& st, int b, int idx) {
   constexpr int kVec = Logit<T>::kVec;
   Item it;
   it.live = false;
   const int N = P.n_draft;
-  const int Rs = stage_rows(P);
-  const int64_t rc = t / P.nch;
-  it.c = int(t - rc * P.nch);
-  it.b = int(rc / Rs);
-  it.r = global_row(P, int(rc - int64_t(it.b) * Rs));
+  it.c = idx % P.nch;
+  it.b = b;
+  it.r = global_row(P, st, idx / P.nch);
   const float temp = load_uniform(P.temperature + it.b);
-  if (!temperature_valid(temp) || (temp == 0.0f && it.r < N) || !seq_alive(P, it.b)) return it;
+  if (!temperature_valid(temp) || (temp == 0.0f && it.r < N)) return it;
   it.live = true;
   it.sampled = temp != 0.0f;
   it.coef = it.sampled ? exp2_coef(temp) : 0.0f;
@@ -838,6 +817,42 @@ constexpr int kStageParts = 256;  // row partials the decision holds in LDS at o
 __device__ __forceinline__ uint64_t deadline_after(uint64_t ticks) { return wall_clock64() + ticks; }
 __device__ __forceinline__ bool before(uint64_t deadline) { return wall_clock64() < deadline; }
 
+__shared__ int g_go;
+
+// A lazy call's go-on word for this workgroup (stage >= 1): waits for it
+// (until the call's wait bound), takes and zeroes it. Returns 1 (the
+// sequence goes on in this stage), 0 (it ended in an earlier stage) or -1
+// (the wait gave up), the same in every thread.
+__device__ __forceinline__ int take_go(const Params& P, uint64_t* w) {
+  if (threadIdx.x == 0) {
+    uint64_t v = get_u64(w);
+    if (!has_tag(v, P.tag)) {
+      const uint64_t deadline = deadline_after(P.wait_ticks);
+      while (!has_tag(v, P.tag) && before(deadline)) {
+        __builtin_amdgcn_s_sleep(8);
+        v = get_u64(w);
+      }
+    }
+    const bool ok = P.wait_ticks != 0 && has_tag(v, P.tag);
+    put_u64(w, 0);
+    g_go = ok ? int(uint32_t(v) & 1u) : -1;
+  }
+  barrier();
+  return g_go;
+}
+
+// The decision of stage st of sequence b leaves the go-on words of the
+// sequence's next stage (whole workgroup; nothing after a lazy call's last
+// stage or in a whole call).
+__device__ __forceinline__ void signal_go(const Params& P, const Stage& st, int b, bool go) {
+  if (!P.lazy || st.s + 1 >= P.n_stages) return;
+  const Stage nx = stage_at(P, st.s + 1);
+  const int n = stage_rows(P, nx) * P.nch;
+  const uint64_t v = tagged(P.tag, go ? 1u : 0u);
+  for (int k = int(threadIdx.x); k <= n; k += kThreads)
+    put_u64(k < n ? alive_item(P, b, global_row(P, nx, k / P.nch), k % P.nch) : alive_dec(P, b, nx.s), v);
+}
+
 struct DecideShared {
   float row_m[kMaxRows];
   double row_logz[kMaxRows];
@@ -911,26 +926,51 @@ __device__ __forceinline__ bool take_partial(const Params& P, PartialRec* q, int
   return ok;
 }
 
-// The decision for sequence b (whole workgroup, once per sequence and
-// launch): per-row log-normalisers and argmaxes from the row partials of the
-// launch's rows, the accept tests of its positions [lo, hi), the first
-// rejection. Writes the row diagnostics and the accepted prefix; a greedy
-// sequence's emitted token and n_accepted too, while a sampled sequence's are
-// written by its draw's finisher, from the record published here. In a lazy
-// stage a sequence whose drafts lo..hi-1 are all accepted (hi < N) goes on to
-// the next stage: its drafts so far are written and nothing is drawn.
+// Row diagnostics lse = NaN, argmax = -1 for sequence b's rows at positions
+// >= from (target row N counting as the last position), all of them rows
+// that no other workgroup writes: those of later stages when the sequence
+// ends in stage st, or its own and later ones when the stage fails.
+__device__ __forceinline__ void mark_unread(const Params& P, int b, const Stage& st, int from) {
+  const int N = P.n_draft, R = 2 * N + 1;
+  double* lse = P.row_lse + int64_t(b) * R;
+  int* amax = P.row_argmax + int64_t(b) * R;
+  for (int r = int(threadIdx.x); r < R; r += kThreads) {
+    const bool mark = r < N ? r >= from : (r < 2 * N ? r - N >= from : (from < N || st.hi == N));
+    if (mark) {
+      lse[r] = NAN;
+      amax[r] = -1;
+    }
+  }
+}
+
+// The decision of stage st for sequence b (whole workgroup, once per
+// sequence and stage): per-row log-normalisers and argmaxes from the row
+// partials of the stage's rows, the accept tests of its positions [lo, hi),
+// the first rejection. Writes the row diagnostics and the accepted prefix; a
+// greedy sequence's emitted token and n_accepted too, while a sampled
+// sequence's are written by its draw's finisher, from the record published
+// here. In a lazy call a sequence whose drafts lo..hi-1 are all accepted
+// (hi < N) goes on to the next stage: its drafts so far are written, nothing
+// is drawn, and the next stage's workgroups are told to go on. `go` is the
+// stage's go-on word (1 for stage 0): 0 means the sequence ended in an
+// earlier stage (its items read nothing, so nothing is taken), -1 that the
+// wait for the word gave up.
 //
 // The normalisers come from fp32 row sums (relative error ~1e-6); logs and
 // the ratio are taken in fp64, so a decision can only differ from exact
 // arithmetic when u is within a few 1e-6 of the ratio.
 template <typename T>
-__device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
+__device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage& st, int b, int go) {
+  if (go == 0) {
+    signal_go(P, st, b, false);
+    return;
+  }
   DecideShared& ds = sh.u.dec;
   const int N = P.n_draft;
   const int R = 2 * N + 1;
-  const int lo = stage_lo(P), hi = stage_hi(P), ns = hi - lo;
+  const int lo = st.lo, hi = st.hi, ns = hi - lo;
   const bool last = hi == N;
-  const int Rs = stage_rows(P);
+  const int Rs = go > 0 ? stage_rows(P, st) : 0;  // no partials are taken after a failed wait
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -938,7 +978,6 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   int* otok = P.out_tokens + int64_t(b) * (N + 1);
   double* lse = P.row_lse + int64_t(b) * R;
   int* amax = P.row_argmax + int64_t(b) * R;
-  const bool alive = seq_alive(P, b);
   // Every row partial of the launch's rows is taken (and zeroed) whatever the
   // outcome, a group of rows at a time (thread i takes partial i of the
   // group).
@@ -967,7 +1006,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   // Thread i < ns: the logits of draft token d at position lo + i in its draft
   // and target rows (requested now; used by the accept test).
   float zt = 0.0f, zd = 0.0f;
-  if (tid < ns && alive && !greedy && d >= 0 && d < P.vocab) {
+  if (tid < ns && go > 0 && !greedy && d >= 0 && d < P.vocab) {
     zt = Logit<T>::at(static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + pos) * P.vocab, d);
     zd = Logit<T>::at(static_cast<const T*>(P.draft) + (int64_t(b) * N + pos) * P.vocab, d);
   }
@@ -975,24 +1014,13 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   const float c = greedy ? 0.0f : exp2_coef(t);
   const double inv_t = greedy ? 0.0 : 1.0 / double(t);
   const int r_first = greedy ? N : 0;
-  // The first stage of a lazy call marks the rows it does not read; later
-  // stages fill in the ones they read.
-  if (stage_lazy(P) && lo == 0) {
-    for (int r = tid; r < R; r += kThreads) {
-      const bool in_stage = r < N ? (r >= lo && r < hi) : (r < 2 * N ? (r - N >= lo && r - N < hi) : last);
-      if (!in_stage) {
-        lse[r] = NAN;
-        amax[r] = -1;
-      }
-    }
-  }
   // Quads of lanes each merge one row: lane k of a quad folds partials k,
   // k + 4, ... of the row in order, then two exchange steps within the quad.
   constexpr int cs = 4;
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
   const uint64_t deadline = deadline_after(P.wait_ticks);
-  bool timed_out = false, any_bad = false;
+  bool timed_out = go < 0, any_bad = false;
   for (int rg = 0; rg < Rs; rg += rows_per_group) {
     const int nr = min(rows_per_group, Rs - rg);
     const int np = nr * pr;
@@ -1000,7 +1028,7 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     if (tid < np) {
       Partial q;
       const int kc = tid % pr;
-      late = !take_partial(P, part_b + int64_t(global_row(P, rg + tid / pr)) * pr + kc, kc * P.chunk, deadline, q);
+      late = !take_partial(P, part_b + int64_t(global_row(P, st, rg + tid / pr)) * pr + kc, kc * P.chunk, deadline, q);
       ds.part[tid] = q;
     }
     // (also the barrier that makes the group's partials visible); the input
@@ -1009,11 +1037,11 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     const int vote = block_any2(rg == 0 && bad, late);
     any_bad = any_bad || (vote & 1);
     timed_out = timed_out || (vote & 2);
-    if (any_bad || timed_out || !alive) continue;
+    if (any_bad || timed_out) continue;
     if (rg == 0) trace(2, 4);
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
       const int rr = r0 + seg;
-      const int r = global_row(P, rg + min(rr, nr - 1));
+      const int r = global_row(P, st, rg + min(rr, nr - 1));
       const bool row_ok = rr < nr && r >= r_first;
       float m = -INFINITY, s = 0.0f;
       int idx = INT_MAX;
@@ -1049,20 +1077,12 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
     }
     barrier();
   }
-  if (!alive) {
-    // Done in an earlier stage: its partials are cleared, nothing else.
-    if (tid == 0) set_next_state(P, b, -1);
-    return;
-  }
   if (any_bad || timed_out) {
     // Invalid inputs give -1 everywhere; a partial that never came (not
     // expected: a workgroup that was not dispatched in time) gives -2.
     const int code = any_bad ? -1 : -2;
-    for (int r = tid; r < R; r += kThreads) {
-      lse[r] = NAN;
-      amax[r] = -1;
-    }
-    if (tid == 0) set_next_state(P, b, -1);
+    mark_unread(P, b, st, lo);
+    signal_go(P, st, b, false);
     if (draws) {
       // The finisher writes the sentinels.
       if (tid == 0) publish(P, b, any_bad ? kModeInvalid : kModeFailed, 0, 0.0f, 0.0f, 0.0);
@@ -1104,15 +1124,18 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, int b) {
   trace(2, 6);
   const unsigned long long rej = ds.rej_mask;
   const int j = rej ? lo + (__ffsll(rej) - 1) : hi;
-  const bool go_on = j == hi && !last;  // a lazy stage's sequence that continues
-  const int mode = go_on ? kModeContinue : (greedy ? kModeNone : (j < N ? kModeResidual : kModeBonus));
-  // The draw's record first: the draw members wait for it.
-  if (tid == 0 && !greedy) {
-    const float md = (j < N && !go_on) ? ds.row_m[j] : 0.0f;
-    const double log_rho = (j < N && !go_on) ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
-    publish(P, b, mode, j, go_on ? 0.0f : ds.row_m[N + j], md, log_rho);
+  const bool go_on = j == hi && !last;  // a lazy call's sequence that goes on to the next stage
+  // The draw's record first (the draw members wait for it), or the next
+  // stage's go-on words.
+  if (tid == 0 && !greedy && !go_on) {
+    const float md = j < N ? ds.row_m[j] : 0.0f;
+    const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
+    publish(P, b, j < N ? kModeResidual : kModeBonus, j, ds.row_m[N + j], md, log_rho);
   }
-  if (tid == 0) set_next_state(P, b, go_on ? hi : -1);
+  // Rows of the stages after this one are never read when the sequence ends
+  // here.
+  if (!go_on && !last) mark_unread(P, b, st, hi);
+  signal_go(P, st, b, go_on);
   for (int i = lo + tid; i <= N; i += kThreads) {
     if (i < j)
       otok[i] = ds.tok[i];
@@ -1522,15 +1545,11 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (lane == 0) ws.fail = bad;
   }
   barrier();
-  if (ws.fail == 0ull && s.mode == kModeContinue) return;  // a lazy stage's sequence goes on
   if (ws.fail != 0ull || !(s.mode == kModeResidual || s.mode == kModeBonus)) {
     const int code = s.mode == kModeInvalid ? -1 : -2;
     int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
     for (int i = tid; i <= P.n_draft; i += kThreads) otok[i] = code;
-    if (tid == 0) {
-      if (P.out_n != nullptr) P.out_n[b] = code;
-      set_next_state(P, b, -1);
-    }
+    if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
     return;
   }
   const DrawRows<T> d = draw_rows<T>(P, b, s);
@@ -1638,13 +1657,16 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
 // fp64 sums: their waves take issue priority.
 __device__ __forceinline__ void critical_path() { __builtin_amdgcn_s_setprio(3); }
 
-// Row-statistics item `idx` of sequence b: stores the item's partial (a
-// placeholder when the item is not read) and is done.
+// Row-statistics item `idx` of sequence b in stage st: stores the item's
+// partial (a placeholder when the item is not read) and is done. In a lazy
+// call's later stages it first takes its go-on word, and stores nothing for a
+// sequence that ended earlier (its decision takes nothing either).
 template <typename T>
-__device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
+__device__ __forceinline__ void stat_role(const Params& P, const Stage& st, int b, int idx) {
   trace_set(unsigned(b) * unsigned(P.items_per_seq + 1) + unsigned(idx));
   trace(2, 0);
-  const Item it = item_at<T>(P, int64_t(b) * P.items_per_seq + idx);
+  if (st.s > 0 && take_go(P, alive_item(P, b, global_row(P, st, idx / P.nch), idx % P.nch)) != 1) return;
+  const Item it = item_at<T>(P, st, b, idx);
   Partial q{-INFINITY, 0.0f, INT_MAX - 1};
   if (it.live) {
     ItemRegs g;
@@ -1661,11 +1683,11 @@ __device__ __forceinline__ void stat_role(const Params& P, int b, int idx) {
 // The decision of sequence b, in a workgroup of its own that follows the
 // sequence's row-statistics items in the launch order.
 template <typename T>
-__device__ __forceinline__ void decision_role(const Params& P, Shared& sh, int b) {
+__device__ __forceinline__ void decision_role(const Params& P, Shared& sh, const Stage& st, int b) {
   trace_set(unsigned(b) * unsigned(P.items_per_seq + 1) + unsigned(P.items_per_seq));
   trace(2, 0);
   critical_path();
-  decide<T>(P, sh, b);
+  decide<T>(P, sh, st, b, st.s > 0 ? take_go(P, alive_dec(P, b, st.s)) : 1);
   trace(2, 3);
 }
 
@@ -1712,9 +1734,7 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp
 template <typename T>
 __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
   const float temp = load_uniform(P.temperature + b);
-  // (a lazy stage's sequence that is already done has no decision here: its
-  // members all leave at once, so its counter stays at zero)
-  if (!has_draw_members(temp) || !seq_alive(P, b)) return;
+  if (!has_draw_members(temp)) return;
   trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
   SeqInfo s;
@@ -1743,18 +1763,42 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
   }
 }
 
-// What workgroup x of the launch does. A sequence's statistics group is its
-// row-statistics items followed by its decision workgroup. Launch order: the
-// statistics groups of sequences 0..lag-1, then for each sequence p the
-// statistics group of sequence p + lag (while there is one) followed by the
-// draw members of sequence p.
+// What workgroup x of the launch does. A sequence's statistics group (for a
+// stage) is its row-statistics items followed by its decision workgroup.
+// Whole call: the statistics groups of sequences 0..lag-1, then for each
+// sequence p the statistics group of sequence p + lag (while there is one)
+// followed by the draw members of sequence p. Lazy call: every sequence's
+// statistics group of stage 0, then of stage 1, ..., then every sequence's
+// draw members (each waits for the decision of whichever stage ends its
+// sequence, which precedes it).
 struct Role {
   int kind;  // 0 row statistics, 1 decision, 2 draw member
+  int s;     // stage
   int b;
-  int idx;   // row-statistics item within the sequence, or draw member
+  int idx;   // row-statistics item within the sequence's stage, or draw member
 };
 
 __device__ __forceinline__ Role role_of(const Params& P, int x) {
+  Role w;
+  if (P.lazy) {
+    int s = 0;
+    while (s < P.n_stages && x >= P.st_base[s + 1]) ++s;
+    if (s == P.n_stages) {
+      x -= P.st_base[s];
+      w.kind = 2;
+      w.s = s - 1;
+      w.b = x / P.nm;
+      w.idx = x - w.b * P.nm;
+      return w;
+    }
+    const int A = stage_rows(P, stage_at(P, s)) * P.nch + 1;
+    x -= P.st_base[s];
+    w.s = s;
+    w.b = x / A;
+    w.idx = x - w.b * A;
+    w.kind = w.idx < A - 1 ? 0 : 1;
+    return w;
+  }
   const int A = P.items_per_seq + 1, M = P.nm, L = P.lag;
   int b, z;
   bool stat;
@@ -1779,8 +1823,8 @@ __device__ __forceinline__ Role role_of(const Params& P, int x) {
       z = x - p * M;
     }
   }
-  Role w;
   w.kind = stat ? (z < A - 1 ? 0 : 1) : 2;
+  w.s = 0;
   w.b = b;
   w.idx = z;
   return w;
@@ -1792,9 +1836,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   Shared& sh = g_shared;
   const Role w = role_of(P, int(blockIdx.x));
   if (w.kind == 0)
-    stat_role<T>(P, w.b, w.idx);
+    stat_role<T>(P, stage_at(P, w.s), w.b, w.idx);
   else if (w.kind == 1)
-    decision_role<T>(P, sh, w.b);
+    decision_role<T>(P, sh, stage_at(P, w.s), w.b);
   else
     draw_role<T>(P, sh, w.b, w.idx);
 }
@@ -1825,20 +1869,35 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.nch = w.n_stat_chunks;
   p.chunk = w.stat_chunk;
   p.nm = w.n_members;
-  p.stage = uint32_t(a.pos_lo) | (uint32_t(a.pos_hi) << 8) | (uint32_t(a.parity & 1) << 16) |
-            (a.lazy ? (1u << 17) : 0u);
-  p.state = a.state;
-  const int rows = 2 * (a.pos_hi - a.pos_lo) + (a.pos_hi == a.n_draft ? 1 : 0);
-  p.items_per_seq = rows * w.n_stat_chunks;
-  // The lag: about three chip-fulls of resident workgroups of (row
-  // statistics, draw) pairs, so a sequence's decision is normally out before
-  // its draw members start.
-  p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + 1 + p.nm)));
+  p.lazy = a.lazy ? 1 : 0;
+  p.alive = w.alive;
+  p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
+  int64_t blocks;
+  if (p.lazy) {
+    p.n_stages = lazy_stage_bounds(a.n_draft, p.st_bound);
+    int64_t base = 0;
+    for (int s = 0; s < p.n_stages; ++s) {
+      p.st_base[s] = int(base);
+      const int hi = p.st_bound[s + 1], lo = p.st_bound[s];
+      base += int64_t(a.batch) * ((2 * (hi - lo) + (hi == a.n_draft ? 1 : 0)) * w.n_stat_chunks + 1);
+    }
+    p.st_base[p.n_stages] = int(base);
+    p.lag = 0;
+    blocks = base + int64_t(a.batch) * p.nm;
+  } else {
+    p.n_stages = 1;
+    p.st_bound[0] = 0;
+    p.st_bound[1] = a.n_draft;
+    // The lag: about three chip-fulls of resident workgroups of (row
+    // statistics, draw) pairs, so a sequence's decision is normally out before
+    // its draw members start.
+    p.lag = max(1, min(a.batch, ceil_div(3 * w.resident_blocks, p.items_per_seq + 1 + p.nm)));
+    blocks = int64_t(a.batch) * (p.items_per_seq + 1 + p.nm);
+  }
   p.flags = ((int64_t(a.vocab) * int64_t(sizeof(T))) % 16 == 0 ? kVecOk : 0u) | (a.debug ? kDebug : 0u);
   p.tag = a.tag;
   // (not min(): on the host it takes ints)
   p.wait_ticks = a.wait_ticks > uint64_t(UINT32_MAX) ? UINT32_MAX : uint32_t(a.wait_ticks);
-  const int64_t blocks = int64_t(a.batch) * (p.items_per_seq + 1 + p.nm);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
   hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
