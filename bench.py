@@ -281,13 +281,15 @@ def device_logits(torch, a, dtype, dev):
 def lazy_bytes(batch, n_accepted) -> dict:
     """Rows the lazy verification reads: for each sequence the draft and target
     rows of every stage up to the one where it ends (stages [0,2), [2,8),
-    [8,32), ...), target row N if that is the last stage, plus the draw's
+    [8,32), ..., or [0,2), [2,4), [4,8), ... when one position of the batch
+    is 96 MB or more), target row N if that is the last stage, plus the draw's
     re-read (as for the full path)."""
     B, N, V = batch.batch, batch.n_draft, batch.vocab
     e = 4 if batch.dtype == "f32" else 2
+    growth = 2 if B * V * e * 2 >= 96_000_000 else 4
     stages, lo = [], 0
     while lo < N:
-        hi = min(N, 2) if lo == 0 else min(N, 4 * lo)
+        hi = min(N, 2) if lo == 0 else min(N, growth * lo)
         stages.append((lo, hi))
         lo = hi
     rows = 0

@@ -135,7 +135,9 @@ SPECV_API int specv_verify(specv_handle h, int batch, int n_draft,
  * 채점합니다", section "몇 글자를 미리 쓰게 할까요": position k is reached with
  * probability alpha^k, so most rows past an early rejection need never be
  * read). The positions go in stages [0,2), [2,8), [8,32), ... up to
- * n_draft, one after the other in one kernel launch on `stream`: a stage
+ * n_draft ([0,2), [2,4), [4,8), ... when one position of the batch, its
+ * draft and target rows, is 96 MB or more), one after the other in one
+ * kernel launch on `stream`: a stage
  * reads the rows of the sequences still going on at its first position,
  * which its workgroups learn from the previous stage's decisions. The row
  * statistics, the accept tests and the draw are those of specv_verify, so

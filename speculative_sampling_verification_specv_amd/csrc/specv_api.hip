@@ -291,8 +291,8 @@ int specv_verify_lazy(specv_handle h, int batch, int n_draft, const void* draft_
   a.wait_ticks = h->wait_ticks;
   a.lazy = 1;
   a.tag = h->next_tag;
-  // One launch: the stages [0,2), [2,8), [8,32), ... one after the other in
-  // the launch order, each over the sequences still going on at its first
+  // One launch: the stages (lazy_stage_bounds) one after the other in the
+  // launch order, each over the sequences still going on at its first
   // position, then the draws.
   int stages = 0;
   if (specv::launch_verify(a, h->ws, s, nullptr, &stages) != hipSuccess) return SPECV_EHIP;

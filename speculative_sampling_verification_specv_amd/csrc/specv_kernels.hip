@@ -1874,7 +1874,7 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
   int64_t blocks;
   if (p.lazy) {
-    p.n_stages = lazy_stage_bounds(a.n_draft, p.st_bound);
+    p.n_stages = lazy_stage_bounds(a.n_draft, lazy_growth(a.batch, a.vocab, a.dtype), p.st_bound);
     int64_t base = 0;
     for (int s = 0; s < p.n_stages; ++s) {
       p.st_base[s] = int(base);

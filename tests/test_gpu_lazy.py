@@ -21,10 +21,13 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _stages(N):
+def _stages(N, B, V, dtype):
+    """The stages of a lazy call: [0,2), [2,8), [8,32), ..., or [0,2), [2,4),
+    [4,8), ... when one position of the batch is 96 MB or more."""
+    growth = 2 if B * V * (4 if dtype == "f32" else 2) * 2 >= 96_000_000 else 4
     out, lo = [], 0
     while lo < N:
-        hi = min(N, 2) if lo == 0 else min(N, 4 * lo)
+        hi = min(N, 2) if lo == 0 else min(N, growth * lo)
         out.append((lo, hi))
         lo = hi
     return out
@@ -55,7 +58,7 @@ def _check(batch, full, lazy, label):
     assert np.array_equal(lazy.n_accepted, full.n_accepted), label
     assert np.array_equal(lazy.tokens, full.tokens), label
     N = batch.n_draft
-    st = _stages(N)
+    st = _stages(N, batch.batch, batch.vocab, batch.dtype)
     for s in range(batch.batch):
         T = float(batch.temperature[s])
         j = int(full.n_accepted[s])
