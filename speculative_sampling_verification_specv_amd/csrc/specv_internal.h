@@ -108,6 +108,8 @@ struct VerifyArgs {
   uint64_t wait_ticks;  // bound of every wait between workgroups, in wall-clock ticks
   // Nonzero: the lazy verification (stages of positions, one launch).
   int lazy = 0;
+  // Nonzero: a sampling call (n_draft = 0; draw members only, see Params).
+  int sample = 0;
 };
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

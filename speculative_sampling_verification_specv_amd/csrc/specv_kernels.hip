@@ -430,6 +430,11 @@ struct MemberRec {
   static constexpr int kEt = kPos + kUncMax;  // + i: their exps in the target row
   static constexpr int kEd = kEt + kUncMax;   // + i: and in the draft row
   static constexpr int kWords = kEd + kUncMax;
+  // A sampling call's members have no draft row and no uncertain tokens; those
+  // slots hold the member's largest logit (the reference of its exps) and
+  // the first index where it occurs.
+  static constexpr int kMax = kZd;
+  static constexpr int kArg = kNUnc;
   uint64_t w[kWords];
 };
 
@@ -469,6 +474,11 @@ struct Params {
   // of stage s leaves each workgroup of the sequence's stage s+1 a go-on word
   // (see alive_item): 1 if its drafts so far are all accepted, else 0.
   int lazy;
+  // A sampling call (specv_sample): every row is a sequence with no drafts,
+  // and the launch holds only draw members, each taking its own largest logit
+  // as the reference of its exps (the finisher rescales): no statistics pass,
+  // no decision.
+  int sample;
   int n_stages;
   int st_bound[kMaxLazyStages + 1];
   int st_base[kMaxLazyStages + 1];  // lazy: first workgroup of stage s; st_base[n_stages]: the draw members
@@ -877,6 +887,10 @@ struct DrawShared {
     uint64_t stage[kMaxMembers * MemberRec::kWords];  // finisher: the sequence's member records
   };
   double tw[32 * 16];  // finisher: the crossing sub-chunk's token weights
+  double lane_scale[kMaxMembers];  // sampling finisher: member c's exps times this are relative to the row's maximum
+  float lane_max[kMaxMembers];     // sampling finisher: member c's largest logit
+  float wave_m[kWaves];            // sampling member: each wave's largest logit and its first index
+  int wave_i[kWaves];
   int unc_base[kWaves];
   int slots[kWaves];
   int pick;
@@ -1269,12 +1283,13 @@ constexpr double kSignBand = 1e-4;
 template <typename T>
 __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b, int c, const SeqInfo& s) {
   const bool residual = s.mode == kModeResidual;
+  const bool draw = residual || s.mode == kModeBonus;  // (a sampling call's greedy row: the maximum only)
   constexpr int kPer = Logit<T>::kPer;
   constexpr int kG = kPer / Logit<T>::kVec;  // 16-byte groups per row
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const DrawRows<T> d = draw_rows<T>(P, b, s);
+  DrawRows<T> d = draw_rows<T>(P, b, s);
   const int e = (c * kThreads + tid) * kPer;
   // The exp table first (a cached read that arrives before the rows), then
   // the rows.
@@ -1284,11 +1299,42 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   if (residual) load_packed(d.drow, e, P.vocab, (P.flags & kVecOk) != 0, xd);
   trace(0, 1);
   ws.exp2_tab[tid] = tab_v;
+  float mc = -INFINITY;  // sampling call: this member's largest logit and its first index
+  int ic = INT_MAX;
+  if (P.sample) {
+    float tm = -INFINITY;
+    int ti = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float v = Logit<T>::element(xt, k);
+      ti = v > tm ? e + k : ti;  // strict: the first place (a thread's tokens ascend)
+      tm = fmaxf(v, tm);
+    }
+    const float wm = wave_max(tm);
+    const int wi = wave_min(tm == wm ? ti : INT_MAX);
+    if (lane == 0) {
+      ws.wave_m[tid >> 6] = wm;
+      ws.wave_i[tid >> 6] = wi;
+    }
+  }
   barrier();
+  if (P.sample) {
+    mc = ws.wave_m[0];
+    ic = ws.wave_i[0];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) {
+      ic = ws.wave_m[wv] > mc ? ws.wave_i[wv] : ic;  // waves hold ascending runs: an equal one comes later
+      mc = fmaxf(ws.wave_m[wv], mc);
+    }
+    // (a chunk of -inf logits only: any finite reference gives exps of 0)
+    d.nmt = mc == -INFINITY ? 0.0 : -double(mc) * d.inv_t;
+  }
   const double* tab = ws.exp2_tab;
   double st = 0.0, sd = 0.0, sa = 0.0, sb = 0.0;
   uint32_t unc = 0;  // bit k: token k of this thread has an uncertain sign
-  if (residual) {
+  if (!draw) {
+    // nothing to sum
+  } else if (residual) {
     // The sign of w_x follows log(et/ed) = at - ad (the exps' fp64 arguments,
     // exact to about 1e-16 of their size) against log(rho).
     const double hi = s.log_rho + kSignBand, lo = s.log_rho - kSignBand;
@@ -1409,8 +1455,13 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
       zd += ws.red[kWaves + wv];
     }
     put_d_word(rec, MemberRec::kZt, zt);
-    put_d_word(rec, MemberRec::kZd, zd);
-    put_u64(&rec->w[MemberRec::kNUnc], uint64_t(min(total, kUncMax + 1)));
+    if (P.sample) {
+      put_d_word(rec, MemberRec::kMax, double(mc));
+      put_u64(&rec->w[MemberRec::kArg], uint64_t(uint32_t(ic)));
+    } else {
+      put_d_word(rec, MemberRec::kZd, zd);
+      put_u64(&rec->w[MemberRec::kNUnc], uint64_t(min(total, kUncMax + 1)));
+    }
   }
 }
 
@@ -1436,7 +1487,7 @@ __device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>
       const double ed = exp_nonpos_tab(exp_arg(zd, d.nmd, d.inv_t), tab);
       w[q] = rd > 0.0 ? resid_weight(et, ed, rt, rd) : et * rt;
     } else {
-      w[q] = et;
+      w[q] = et * rt;  // (rt = 1 for a verification's bonus draw: exact)
     }
     sum += w[q];
   }
@@ -1512,6 +1563,11 @@ __device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, 
   return -1;
 }
 
+// Member `lane`'s largest logit from its staged record (-inf past the members).
+__device__ __forceinline__ float mine_sample_max(const DrawShared& ws, int lane, int nm, int kW) {
+  return lane < nm ? float(bits_to_double(ws.stage[lane * kW + MemberRec::kMax])) : -INFINITY;
+}
+
 template <typename T>
 __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s) {
   const bool residual = s.mode == kModeResidual;
@@ -1522,6 +1578,7 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int nm = P.nm;  // <= 64
+  const bool mine = lane < nm;
   const double us = double(load_uniform(P.sample_u + b));  // in flight from the start
   // The sequence's member records, in one coalesced round trip: every load
   // is issued (at a clamped index) before any is stored.
@@ -1545,6 +1602,33 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (lane == 0) ws.fail = bad;
   }
   barrier();
+  if (P.sample) {
+    // A sampling call: the row's largest logit M and its first index from
+    // the members' own; each member's exps rescaled by exp((m_c - M)/T).
+    // Its row diagnostics are written here (there is no decision).
+    if (tid < 64) {
+      const float m = mine_sample_max(ws, lane, nm, kW);
+      const float M = wave_max(m);
+      int idx = wave_min(lane < nm && m == M ? int(uint32_t(ws.stage[lane * kW + MemberRec::kArg])) : INT_MAX);
+      if (idx == INT_MAX) idx = 0;  // every logit -inf: every index ties
+      const bool valid = s.mode != kModeInvalid && ws.fail == 0ull;
+      const bool sampled = valid && s.mode == kModeBonus;
+      const double inv_t = sampled ? 1.0 / double(s.temp) : 0.0;
+      const double scale = sampled && lane < nm ? exp_nonpos((double(m) - double(M)) * inv_t) : 0.0;
+      const double zt = wave_sum(lane < nm ? scale * bits_to_double(ws.stage[lane * kW + MemberRec::kZt]) : 0.0);
+      if (lane < nm) {
+        ws.lane_scale[lane] = scale;
+        ws.lane_max[lane] = m;
+      }
+      if (lane == 0) {
+        P.row_lse[b] = sampled ? double(M) * inv_t + log(zt) : double(NAN);
+        P.row_argmax[b] = valid ? idx : -1;
+        if (valid && s.mode == kModeNone) P.out_tokens[b] = idx;  // greedy: the first argmax
+      }
+    }
+    barrier();
+    if (ws.fail == 0ull && s.mode == kModeNone) return;
+  }
   if (ws.fail != 0ull || !(s.mode == kModeResidual || s.mode == kModeBonus)) {
     const int code = s.mode == kModeInvalid ? -1 : -2;
     int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
@@ -1552,11 +1636,10 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
     return;
   }
-  const DrawRows<T> d = draw_rows<T>(P, b, s);
+  DrawRows<T> d = draw_rows<T>(P, b, s);
   double w[kSubs];
 #pragma unroll
   for (int k = 0; k < kSubs; ++k) w[k] = 0.0;
-  const bool mine = lane < nm;
   const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
   if (tid < 64) {
     // Normalisers (fixed-order DPP sums over the members), then member lane's
@@ -1573,7 +1656,10 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
 #pragma unroll
     for (int k = 0; k < kSubs; ++k) {
       const double ak = bits_to_double(r[MemberRec::kA + k]);
-      w[k] = !mine ? 0.0 : residual ? fma(ak, rt, -__dmul_rn(bits_to_double(r[MemberRec::kB + k]), rd)) : ak;
+      w[k] = !mine ? 0.0
+             : residual ? fma(ak, rt, -__dmul_rn(bits_to_double(r[MemberRec::kB + k]), rd))
+             : P.sample ? ak * ws.lane_scale[lane]
+                        : ak;
     }
     if (residual && nunc <= kUncMax) {
       for (int i = 0; i < nunc; ++i) {
@@ -1626,10 +1712,14 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   const double rem = ws.rem;
   trace_at(1, b, 2);
   // The crossing sub-chunk's exact token weights (kQ per thread, in token
-  // order), then wave 0 finds the token: lane l takes weights 8l .. 8l+7.
+  // order), then wave 0 finds the token: lane l takes weights 8l .. 8l+7. (A
+  // sampling call's member exps are relative to its own maximum, scaled.)
   double wq[kQ];
   int e0;
-  sub_weights<T>(P, d, ws.exp2_tab, pick / kSubs, pick % kSubs, residual, rt, from_q ? 0.0 : rd, wq, e0);
+  const int pc = pick / kSubs;
+  if (P.sample) d.nmt = ws.lane_max[pc] == -INFINITY ? 0.0 : -double(ws.lane_max[pc]) * d.inv_t;
+  sub_weights<T>(P, d, ws.exp2_tab, pc, pick % kSubs, residual, P.sample ? ws.lane_scale[pc] : rt,
+                 from_q ? 0.0 : rd, wq, e0);
   trace_at(1, b, 3);
 #pragma unroll
   for (int q = 0; q < kQ; ++q) ws.tw[tid * kQ + q] = wq[q];
@@ -1734,13 +1824,26 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp
 template <typename T>
 __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
   const float temp = load_uniform(P.temperature + b);
-  if (!has_draw_members(temp)) return;
+  if (!P.sample && !has_draw_members(temp)) return;
   trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
   SeqInfo s;
-  const bool saw = wait_decision(P, b, temp, s);
+  bool saw = true;
+  if (P.sample) {
+    // No decision: the row's own draw (the first argmax when greedy).
+    bool bad = !temperature_valid(temp);
+    if (P.flags & kDebug) {
+      const float us = load_uniform(P.sample_u + b);
+      bad = bad || (temp > 0.0f && !(us >= 0.0f && us < 1.0f));
+    }
+    s = SeqInfo{temp, bad ? kModeInvalid : (temp == 0.0f ? kModeNone : kModeBonus), 0, 0.0f, 0.0f, 0.0};
+    if (threadIdx.x == 0) g_seq = s;
+  } else {
+    saw = wait_decision(P, b, temp, s);
+  }
   trace(0, 5);
-  if (s.mode == kModeResidual || s.mode == kModeBonus) member_record<T>(P, sh, b, c, s);
+  if (s.mode == kModeResidual || s.mode == kModeBonus || (P.sample && s.mode == kModeNone))
+    member_record<T>(P, sh, b, c, s);
   if (threadIdx.x == 0) put_u64(&P.records[int64_t(b) * P.nm + c].w[MemberRec::kStatus], tagged(P.tag, saw ? 1u : 0u));
   trace(0, 3);
   const bool last = last_arrival(P.draw_done + b * kCounterStride, P.nm);
@@ -1780,6 +1883,13 @@ struct Role {
 
 __device__ __forceinline__ Role role_of(const Params& P, int x) {
   Role w;
+  if (P.sample) {
+    w.kind = 2;
+    w.s = 0;
+    w.b = x / P.nm;
+    w.idx = x - w.b * P.nm;
+    return w;
+  }
   if (P.lazy) {
     int s = 0;
     while (s < P.n_stages && x >= P.st_base[s + 1]) ++s;
@@ -1870,10 +1980,17 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.chunk = w.stat_chunk;
   p.nm = w.n_members;
   p.lazy = a.lazy ? 1 : 0;
+  p.sample = a.sample ? 1 : 0;
   p.alive = w.alive;
   p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
   int64_t blocks;
-  if (p.lazy) {
+  if (p.sample) {
+    p.n_stages = 1;
+    p.st_bound[0] = 0;
+    p.st_bound[1] = 0;
+    p.lag = 0;
+    blocks = int64_t(a.batch) * p.nm;
+  } else if (p.lazy) {
     p.n_stages = lazy_stage_bounds(a.n_draft, lazy_growth(a.batch, a.vocab, a.dtype), p.st_bound);
     int64_t base = 0;
     for (int s = 0; s < p.n_stages; ++s) {
