@@ -11,14 +11,16 @@
 // precede it in the launch order, and every wait is bounded.
 //
 //   row statistics  one workgroup per item (kStatBytes of one row): fp32
-//                   max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T, first
-//                   argmax, and the logit at the row's draft token, stored as
-//                   the item's partial. Pure streaming, HBM-bound; greedy
-//                   sequences skip their draft rows.
-//   decision        one workgroup per sequence, after its items: merges the
-//                   row partials into log-normalisers, takes the N accept
-//                   decisions, writes them out (the token itself when greedy)
-//                   and publishes the draw's record.
+//                   max, sum of 2^(z*c - fl(max*c)) with c = log2(e)/T and
+//                   first argmax, stored as the item's partial. Pure
+//                   streaming, HBM-bound; greedy sequences skip their draft
+//                   rows.
+//   decision        one workgroup per sequence (and stage, in a lazy call),
+//                   after its items: merges the row partials into
+//                   log-normalisers, takes the accept decisions, writes them
+//                   out (the token itself when greedy) and publishes the
+//                   draw's record, or in a lazy call lets the sequence's next
+//                   stage go on.
 //   draw member     one workgroup per (sampled sequence, kMemberElems logits of
 //                   each of the draw's row(s)), after the decision: fp64 exps
 //                   of its logits summed into a member record. The last member
@@ -26,6 +28,9 @@
 //                   normalisers and sub-chunk weights from the records, the
 //                   sub-chunk where the inverse CDF crosses u*S, an exact
 //                   rescan of it, the token.
+//
+// A sampling call (no drafts) holds draw members only, each taking its own
+// largest logit as its reference (see Params::sample).
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
@@ -564,8 +569,8 @@ __device__ __forceinline__ const T* item_row(const Params& P, const Item& it) {
   return static_cast<const T*>(it.r < P.n_draft ? P.draft : P.target) + it.row_flat;
 }
 
-// An item's logits in flight: this thread's 16-byte vectors tid + u*kThreads,
-// its head and tail element, and the draft token's logit (raw bits). Every
+// An item's logits in flight: this thread's 16-byte vectors tid + u*kThreads
+// and its head and tail element (raw bits). Every
 // load is issued unconditionally at a clamped, valid address (the fold
 // ignores what lies outside the item): loads under per-thread branches make
 // the compiler wait for every load in flight where the branches join.
