@@ -134,3 +134,71 @@ def test_sample_greedy_ties():
         toks, lse, amax = _draw(v, rows, dev)
     assert np.array_equal(toks, np.argmax(coarse, axis=-1))
     assert np.array_equal(amax, np.argmax(coarse, axis=-1))
+
+
+def _masked_rows(dtype: str):
+    """Rows whose finite logits sit in a few 4096-logit spans (the rest -inf),
+    with the largest logit in various spans, ties across spans, and spans far
+    apart in level: every member's own reference is then -inf, low or high."""
+    rng = np.random.default_rng(31)
+    V = 20000  # members of 4096: four whole, one ragged
+    z = np.full((10, V), -np.inf, np.float32)
+    z[0, 17000:17100] = rng.normal(0.0, 2.0, 100)            # only the ragged last span
+    z[1, 8192:12288] = rng.normal(0.0, 2.0, 4096)            # only the third span
+    z[2] = rng.normal(0.0, 1.0, V)
+    z[2, 19990] = 9.0                                        # the maximum in the last span
+    z[3] = z[0]                                              # as row 0, greedy
+    z[4, 100:200] = 3.0                                      # equal maxima in two spans
+    z[4, 9000:9100] = 3.0
+    z[5] = rng.normal(0.0, 1.0, V)
+    z[5, 4096:8192] += 40.0                                  # one span far above the others
+    z[6] = rng.normal(0.0, 1.0, V)
+    z[6, 12288:16384] += 0.5                                 # one span slightly above
+    z[7] = rng.normal(0.0, 3.0, V)
+    z[7, :4096] = -np.inf                                    # the first span masked
+    z[8] = z[5]                                              # greedy
+    z[9] = z[4]                                              # greedy ties
+    T = np.array([1.0, 0.7, 1.0, 0.0, 1.0, 0.5, 1.0, 2.0, 0.0, 0.0], np.float32)
+    logits = synth.to_bf16_bits(z) if dtype == "bf16" else z
+    return synth.SampleRows(dtype, np.ascontiguousarray(logits), T, synth.grid_uniforms(rng, (10,)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_masked_spans(dtype):
+    """One-pass draws where whole member spans are -inf, the maximum sits in
+    the last (ragged) span, maxima tie across spans, or spans differ in level
+    by up to 40/T: tokens, log-normalisers and argmaxes against the oracle,
+    over 200 uniforms per row."""
+    dev = require_gpu()
+    rows = _masked_rows(dtype)
+    rng = np.random.default_rng(32)
+    excused = 0
+    with Verifier(10, 1, rows.logits.shape[1], dtype) as v:
+        for k in range(200):
+            u = rows.uniforms if k == 0 else synth.grid_uniforms(rng, (10,))
+            toks, lse, amax = _draw(v, rows, dev, u)
+            excused += _check(rows, toks, lse, amax, u, label=f"{dtype} set {k}")
+    assert excused <= MAX_EXCUSED_RATE * 2000
+
+
+def test_sample_debug_uniforms(monkeypatch):
+    """With SPECV_DEBUG set when the handle is created, a sampled row whose
+    uniform lies outside [0, 1) is invalid (-1, NaN, -1); a greedy row does
+    not use its uniform; the other rows match the oracle."""
+    dev = require_gpu()
+    monkeypatch.setenv("SPECV_DEBUG", "1")
+    base = synth.workload("b1_n5_v32000_f32")
+    wl = synth.Workload("sampledbg", 22, 8, 4, 5000, "f32", base.scale, base.zipf_s, (0.2, 1.0), (1.0, 1.0))
+    rows = synth.make_sample_rows(wl, seed=4, n_rows=8)
+    rows.temperature[6] = 0.0
+    rows.uniforms[1] = np.float32(1.0)
+    rows.uniforms[2] = np.float32(-0.5)
+    rows.uniforms[3] = np.float32(np.nan)
+    rows.uniforms[6] = np.float32(7.0)  # greedy: unused
+    with Verifier(8, 1, 5000, "f32") as v:
+        toks, lse, amax = _draw(v, rows, dev)
+    for r in (1, 2, 3):
+        assert toks[r] == -1 and amax[r] == -1 and np.isnan(lse[r]), r
+    good = [0, 4, 5, 6, 7]
+    sub = synth.SampleRows("f32", rows.logits[good], rows.temperature[good], rows.uniforms[good])
+    _check(sub, toks[good], lse[good], amax[good], label="debug")
