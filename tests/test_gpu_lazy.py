@@ -165,3 +165,27 @@ def test_lazy_graph_replay():
             torch.cuda.synchronize()
             assert np.array_equal(out_t.cpu().numpy(), want[i][0]), rep
             assert np.array_equal(out_n.cpu().numpy(), want[i][1]), rep
+
+
+def test_lazy_wait_limit_zero_then_normal():
+    """A lazy call with a wait bound of 0: every wait (partials, go-on words,
+    decisions) gives up, every sequence reports -2 and every workgroup exits,
+    leaving words that their producers wrote after the give-up. Lazy and full
+    calls on the same handle with the default bound then match each other
+    and the oracle: no word a gave-up call left behind is taken."""
+    dev = require_gpu()
+    wl = synth.Workload("lazy0", 16, 24, 9, 2 * 32768 + 517, "bf16", 2.5, 1.1, (0.1, 1.0), (0.0, 1.0))
+    b = synth.make_batch(wl, seed=5)
+    with Verifier(wl.batch, wl.n_draft, wl.vocab, wl.dtype) as v:
+        v.set_wait_limit(0)
+        args = to_device(b, dev)
+        for _ in range(3):
+            _, n = v.verify_lazy(**args)
+            torch.cuda.synchronize()
+            assert np.all(n.cpu().numpy() == -2)
+        v.set_wait_limit(100000)
+        for k in range(2):
+            full, lazy = _both(b, v)
+            _check(b, full, lazy, f"after wait 0, call {k}")
+            compare(b, lazy, run_oracle(b)).check(f"lazy after wait 0, call {k}")
+    _say("[lazy wait 0] 3 gave-up calls, then 2 exact calls")
