@@ -489,7 +489,7 @@ def main() -> int:
                              args.calibrate_copy_mb or 256)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(sequences shard across GPUs with no exchange but the outputs); run with --gpus 1",
               file=sys.stderr)
         return 2
