@@ -358,8 +358,8 @@ def measure(torch, dev, name: str, args, lazy: bool = False) -> dict:
     kernel_ms = e0.elapsed_time(e1) / args.steps
     v.close()
     # Algorithmic bytes of the launch: every row the method needs once, plus
-    # the draw's re-read of the drawn row(s) (the finishers' rescan of one
-    # sub-chunk per sequence is counted with them).
+    # the draw's re-read of the drawn row(s) (the finishers' load of one
+    # member's tokens per sequence is counted with them).
     kernel_bytes = nbytes["stats"] + nbytes["reread"]
     dominant = "verify"
     stage_ms = {dominant: kernel_ms}
@@ -430,7 +430,7 @@ def measure_extras(torch, dev, args) -> dict:
         calls = [_direct(lib.specv_sample, v.handle, 64, _lib._ptr(x), _lib._ptr(temp), _lib._ptr(uni), _lib._ptr(tok),
                          _lib._stream_ptr(None, dev)) for x in logit_sets]
         ms = _time_calls(torch, dev, lambda k: calls[k % copies](), args.steps, args.warmup)
-    # One pass over each row (plus the rescan of one sub-chunk of 32 * 16 tokens per row).
+    # One pass over each row (plus the finisher's load of one member's 4096 tokens per row).
     out["sample_b64_v128256_bf16"] = {"rows_per_sec": 64 / (ms * 1e-3), "ms_per_call": ms,
                                       "bytes_per_call": row_bytes,
                                       "hbm_gbs": row_bytes / (ms * 1e-3) / 1e9}

@@ -457,7 +457,7 @@ namespace {
 
 constexpr int kStaticMaxBatch = 256;
 constexpr int kStaticMaxDraft = 16;
-// layout_workspace(256, 16, 2^18, float32) = 8107008 bytes; checked at set-up.
+// layout_workspace(256, 16, 2^18, float32) = 8367104 bytes; checked at set-up.
 constexpr size_t kStaticBytes = size_t(8) << 20;
 constexpr int kStaticMaxDevices = 64;
 

@@ -25,12 +25,14 @@
 //                   each of the draw's row(s)), after the decision: fp64 exps
 //                   of its logits summed into a member record. The last member
 //                   of a sequence to report is its finisher: the fp64
-//                   normalisers and sub-chunk weights from the records, the
-//                   sub-chunk where the inverse CDF crosses u*S, an exact
-//                   rescan of it, the token.
+//                   normalisers and member weights from the records, the
+//                   member and then its sub-chunk where the inverse CDF
+//                   crosses u*S, an exact rescan of that sub-chunk's tokens
+//                   (loaded while the sub-chunk is picked), the token.
 //
-// A sampling call (no drafts) holds draw members only, each taking its own
-// largest logit as its reference (see Params::sample).
+// A sampling call (no drafts) is a launch of its own kernel (sample_kernel)
+// of draw members only, each taking its own largest logit as the reference of
+// its exps; the finisher rescales them.
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
@@ -434,7 +436,9 @@ struct MemberRec {
   static constexpr int kPos = kNUnc + 1;    // + i: their positions, ascending
   static constexpr int kEt = kPos + kUncMax;  // + i: their exps in the target row
   static constexpr int kEd = kEt + kUncMax;   // + i: and in the draft row
-  static constexpr int kWords = kEd + kUncMax;
+  static constexpr int kAt = kEd + kUncMax;   // the member's sums of et and ed over certainly positive tokens
+  static constexpr int kBt = kAt + 1;
+  static constexpr int kWords = kBt + 1;
   // A sampling call's members have no draft row and no uncertain tokens; those
   // slots hold the member's largest logit (the reference of its exps) and
   // the first index where it occurs.
@@ -479,11 +483,6 @@ struct Params {
   // of stage s leaves each workgroup of the sequence's stage s+1 a go-on word
   // (see alive_item): 1 if its drafts so far are all accepted, else 0.
   int lazy;
-  // A sampling call (specv_sample): every row is a sequence with no drafts,
-  // and the launch holds only draw members, each taking its own largest logit
-  // as the reference of its exps (the finisher rescales): no statistics pass,
-  // no decision.
-  int sample;
   int n_stages;
   int st_bound[kMaxLazyStages + 1];
   int st_base[kMaxLazyStages + 1];  // lazy: first workgroup of stage s; st_base[n_stages]: the draw members
@@ -892,17 +891,9 @@ struct DrawShared {
     uint64_t stage[kMaxMembers * MemberRec::kWords];  // finisher: the sequence's member records
   };
   double tw[32 * 16];  // finisher: the crossing sub-chunk's token weights
-  double lane_scale[kMaxMembers];  // sampling finisher: member c's exps times this are relative to the row's maximum
-  float lane_max[kMaxMembers];     // sampling finisher: member c's largest logit
   float wave_m[kWaves];            // sampling member: each wave's largest logit and its first index
   int wave_i[kWaves];
   int unc_base[kWaves];
-  int slots[kWaves];
-  int pick;
-  double rem;
-  double rt, rd, total;
-  unsigned long long over;
-  unsigned long long fail;  // finisher: members that did not see this call's decision
 };
 
 struct Shared {
@@ -922,6 +913,17 @@ struct SeqInfo {
   float m_draft;
   double log_rho;  // log(Zt/Zd) of row j from the fp32 row sums (residual only)
 };
+
+// A SeqInfo the workgroup holds in common (read from LDS), as wave-uniform
+// values: scalar address arithmetic and branches.
+__device__ __forceinline__ SeqInfo uniform(const SeqInfo& s) {
+  auto f = [](float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); };
+  const uint64_t lr = double_to_bits(s.log_rho);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(lr))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(lr >> 32))));
+  return SeqInfo{f(s.temp), __builtin_amdgcn_readfirstlane(s.mode), __builtin_amdgcn_readfirstlane(s.j), f(s.m_target),
+                 f(s.m_draft), bits_to_double((uint64_t(hi) << 32) | lo)};
+}
 
 // Waits (until `deadline`) for partial q of this call (its item starts at
 // element e0 of the row), then takes it and zeroes its words. Returns false
@@ -1203,69 +1205,6 @@ __device__ __forceinline__ double resid_weight(double et, double ed, double rt, 
   return fmax(0.0, fma(et, rt, -__dmul_rn(ed, rd)));
 }
 
-// Lowest (kFirst) or highest thread index whose flag is set, kThreads or -1
-// if none; the same in every thread.
-template <bool kFirst>
-__device__ __forceinline__ int block_pick(bool flag, int* slots) {
-  const unsigned long long m = __ballot(flag);
-  const int wave = threadIdx.x >> 6;
-  barrier();
-  if ((threadIdx.x & 63) == 0) {
-    if (kFirst)
-      slots[wave] = m ? wave * 64 + __ffsll(m) - 1 : kThreads;
-    else
-      slots[wave] = m ? wave * 64 + 63 - __clzll(m) : -1;
-  }
-  barrier();
-  int r = slots[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = kFirst ? min(r, slots[w]) : max(r, slots[w]);
-  return r;
-}
-
-// Inverse-CDF step over n values per thread, in thread order then value
-// order: thread `pre` is its exclusive prefix. Picks the first value with
-// positive weight whose inclusive prefix exceeds `target`, else the last
-// positive one; ws.pick = thread * n + index and ws.rem = target minus the
-// prefix before it (-1 and target if no value is positive).
-template <int n>
-__device__ __forceinline__ void block_inverse_cdf(DrawShared& ws, const double (&w)[n], double pre, double target) {
-  double cum = pre, hit_pre = 0.0, last_pre = 0.0;
-  int hit = -1, lastp = -1;
-#pragma unroll
-  for (int k = 0; k < n; ++k) {
-    const double x = w[k];
-    if (x > 0.0) {
-      if (hit < 0 && cum + x > target) {
-        hit = k;
-        hit_pre = cum;
-      }
-      lastp = k;
-      last_pre = cum;
-    }
-    cum += x;
-  }
-  const int tid = threadIdx.x;
-  const int first = block_pick<true>(hit >= 0, ws.slots);
-  if (first < kThreads) {
-    if (tid == first) {
-      ws.pick = tid * n + hit;
-      ws.rem = target - hit_pre;
-    }
-  } else {
-    const int last = block_pick<false>(lastp >= 0, ws.slots);
-    if (tid == last) {
-      ws.pick = tid * n + lastp;
-      ws.rem = target - last_pre;
-    }
-    if (last < 0 && tid == 0) {
-      ws.pick = -1;
-      ws.rem = target;
-    }
-  }
-  barrier();
-}
-
 // ---------------------------------------------------------------------------
 // Draw members.
 //
@@ -1286,27 +1225,40 @@ constexpr double kSignBand = 1e-4;
 // draw's row(s) (target row j and draft row j after a rejection, target row N
 // for the bonus), summed and classified; writes the member's record.
 template <typename T>
-__device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b, int c, const SeqInfo& s) {
+struct MemberRows {
+  static constexpr int kG = Logit<T>::kPer / Logit<T>::kVec;  // 16-byte groups per row
+  double tab_v;  // this thread's entry of kExp2Table
+  uint4 xt[kG], xd[kG];
+  // The exp table entry first (a cached read that arrives before the rows),
+  // then member c's logits of the target row (and the draft row after a
+  // rejection).
+  __device__ __forceinline__ void load(const Params& P, const DrawRows<T>& d, int c, bool residual) {
+    const int e = (c * kThreads + int(threadIdx.x)) * Logit<T>::kPer;
+    tab_v = kExp2Table[threadIdx.x];
+    load_packed(d.trow, e, P.vocab, (P.flags & kVecOk) != 0, xt);
+    if (residual) load_packed(d.drow, e, P.vocab, (P.flags & kVecOk) != 0, xd);
+  }
+};
+
+template <typename T, bool kSample>
+__device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b, int c, const SeqInfo& s,
+                                              MemberRows<T>& rows) {
   const bool residual = s.mode == kModeResidual;
   const bool draw = residual || s.mode == kModeBonus;  // (a sampling call's greedy row: the maximum only)
   constexpr int kPer = Logit<T>::kPer;
-  constexpr int kG = kPer / Logit<T>::kVec;  // 16-byte groups per row
+  constexpr int kG = MemberRows<T>::kG;
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   DrawRows<T> d = draw_rows<T>(P, b, s);
   const int e = (c * kThreads + tid) * kPer;
-  // The exp table first (a cached read that arrives before the rows), then
-  // the rows.
-  const double tab_v = kExp2Table[tid];  // one entry per thread
-  uint4 xt[kG], xd[kG];
-  load_packed(d.trow, e, P.vocab, (P.flags & kVecOk) != 0, xt);
-  if (residual) load_packed(d.drow, e, P.vocab, (P.flags & kVecOk) != 0, xd);
+  uint4 (&xt)[kG] = rows.xt;
+  uint4 (&xd)[kG] = rows.xd;
   trace(0, 1);
-  ws.exp2_tab[tid] = tab_v;
+  ws.exp2_tab[tid] = rows.tab_v;
   float mc = -INFINITY;  // sampling call: this member's largest logit and its first index
   int ic = INT_MAX;
-  if (P.sample) {
+  if (kSample) {
     float tm = -INFINITY;
     int ti = INT_MAX;
 #pragma unroll
@@ -1323,7 +1275,7 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     }
   }
   barrier();
-  if (P.sample) {
+  if (kSample) {
     mc = ws.wave_m[0];
     ic = ws.wave_i[0];
 #pragma unroll
@@ -1421,7 +1373,7 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
     put_d_word(rec, MemberRec::kA + (tid >> 5), sa);
     put_d_word(rec, MemberRec::kB + (tid >> 5), sb);
   }
-  // One exchange through LDS for the wave totals of st and sd and the wave
+  // One exchange through LDS for the wave totals of st, sd, sa and sb and the wave
   // counts of uncertain tokens (in ascending token order: threads own
   // ascending runs; a thread past its staging capacity overflows the record).
   const int cnt = !residual ? 0 : (n_unc <= 2) ? n_unc : kUncMax + 1;
@@ -1432,10 +1384,14 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
   sd += dpp_f64<kBcast15, 0xa>(sd);
   st += dpp_f64<kBcast31, 0xc>(st);  // lane 63: the wave's totals
   sd += dpp_f64<kBcast31, 0xc>(sd);
+  sa += dpp_f64<kBcast31, 0xc>(sa);
+  sb += dpp_f64<kBcast31, 0xc>(sb);
   const int wave = tid >> 6;
   if (lane == 63) {
     ws.red[wave] = st;
     ws.red[kWaves + wave] = sd;
+    ws.red[2 * kWaves + wave] = sa;
+    ws.red[3 * kWaves + wave] = sb;
     ws.unc_base[wave] = incl;
   }
   barrier();
@@ -1460,12 +1416,22 @@ __device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b
       zd += ws.red[kWaves + wv];
     }
     put_d_word(rec, MemberRec::kZt, zt);
-    if (P.sample) {
+    if (kSample) {
       put_d_word(rec, MemberRec::kMax, double(mc));
       put_u64(&rec->w[MemberRec::kArg], uint64_t(uint32_t(ic)));
     } else {
       put_d_word(rec, MemberRec::kZd, zd);
       put_u64(&rec->w[MemberRec::kNUnc], uint64_t(min(total, kUncMax + 1)));
+      if (residual) {
+        double at = ws.red[2 * kWaves], bt = ws.red[3 * kWaves];
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) {
+          at += ws.red[2 * kWaves + wv];
+          bt += ws.red[3 * kWaves + wv];
+        }
+        put_d_word(rec, MemberRec::kAt, at);
+        put_d_word(rec, MemberRec::kBt, bt);
+      }
     }
   }
 }
@@ -1500,27 +1466,82 @@ __device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>
 }
 
 // Exact weights of the kSubs sub-chunks of member c (whole workgroup, a rare
-// path); thread c receives them in w.
+// path): they replace the member's staged A words, which the finisher then
+// takes as the sub-chunk weights themselves. The caller makes them visible
+// with a barrier.
 template <typename T>
 __device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared& ws, const DrawRows<T>& d, int c,
-                                                     double rt, double rd, double (&w)[kSubs]) {
+                                                     double rt, double rd) {
 #pragma unroll 1
   for (int sub = 0; sub < kSubs; ++sub) {
     double wq[Logit<T>::kPer / 8];
     int e0;
     const double v = block_sum(sub_weights<T>(P, d, ws.exp2_tab, c, sub, true, rt, rd, wq, e0), ws.red);
-#pragma unroll
-    for (int k = 0; k < kSubs; ++k)
-      if (k == sub && int(threadIdx.x) == c) w[k] = v;
+    if (threadIdx.x == 0) ws.stage[c * MemberRec::kWords + MemberRec::kA + sub] = double_to_bits(v);
   }
 }
 
+// Token pairs (x_k, x_k + 1), x_k = x0 + k*32*kPer (x0 even), k < kSubs, of
+// one row as stored, kept in registers until one k is chosen: each load is
+// issued at a clamped index with no branch, and tokens at and past `vocab`
+// become -inf when the pair is taken. Rows 16-byte aligned: one aligned load
+// per pair (the vocabulary is then even); else one load per token.
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+static_assert(kSubs == 8, "one vector lane per sub-chunk");
+
+template <typename T>
+struct PairRow {
+  u32x8 a, b;  // aligned bfloat16: a holds both tokens, b is unused; else a: token x_k, b: token x_k + 1
+  __device__ __forceinline__ void load(const T* __restrict__ row, int x0, int vocab, bool vec_ok) {
+    if (vec_ok) {
+#pragma unroll
+      for (int k = 0; k < kSubs; ++k) {
+        const int xc = min(x0 + k * 32 * Logit<T>::kPer, vocab - 2);
+        if constexpr (sizeof(T) == 2) {
+          a[k] = *reinterpret_cast<const uint32_t*>(row + xc);
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(row + xc);
+          a[k] = v.x;
+          b[k] = v.y;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSubs; ++k) {
+        const int x = x0 + k * 32 * Logit<T>::kPer;
+        a[k] = Logit<T>::bits(row, min(x, vocab - 1));
+        b[k] = Logit<T>::bits(row, min(x + 1, vocab - 1));
+      }
+    }
+  }
+  // Pair k (wave-uniform) as fp32 logits.
+  __device__ __forceinline__ void take(int k, int x0, int vocab, bool vec_ok, float& z0, float& z1) const {
+    const uint32_t wa = a[k];
+    if (sizeof(T) == 2 && vec_ok) {
+      z0 = Logit<T>::from_bits(wa & 0xffffu);
+      z1 = Logit<T>::from_bits(wa >> 16);
+    } else {
+      z0 = Logit<T>::from_bits(wa);
+      z1 = Logit<T>::from_bits(b[k]);
+    }
+    const int x = x0 + k * 32 * Logit<T>::kPer;
+    if (x >= vocab) z0 = -INFINITY;
+    if (x + 1 >= vocab) z1 = -INFINITY;
+  }
+};
+
 // ---------------------------------------------------------------------------
-// The finisher (the last member of a sequence to report): the member records
-// staged in LDS; wave 0 (lane c = member c) forms the normalisers, the
-// sub-chunk weights and the sub-chunk where the inverse CDF crosses u*S; the
-// workgroup forms the exact weights of that sub-chunk's tokens; wave 0 finds
-// the token.
+// The finisher (the last member of a sequence to report). The member records
+// are staged in LDS. Then every wave, on its own (lane l reading record l),
+// forms the normalisers and each member's weight, picks the member where the
+// inverse CDF crosses u*S, issues the loads of that member's tokens (two of
+// each sub-chunk per thread) and, while they are in flight, forms the
+// member's sub-chunk weights and picks the crossing sub-chunk. The workgroup
+// then forms the exact weights of that sub-chunk's tokens and wave 0 finds
+// the token. A member's weight comes from its certain-sign totals and its
+// uncertain tokens, a sub-chunk's from its own sums: they agree up to
+// rounding, and each search falls back to its last positive value when
+// rounding leaves no crossing.
 
 // Inverse CDF within wave 0 over n values per lane, in lane order then value
 // order, against `target`: the first value with positive weight whose
@@ -1568,17 +1589,12 @@ __device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, 
   return -1;
 }
 
-// Member `lane`'s largest logit from its staged record (-inf past the members).
-__device__ __forceinline__ float mine_sample_max(const DrawShared& ws, int lane, int nm, int kW) {
-  return lane < nm ? float(bits_to_double(ws.stage[lane * kW + MemberRec::kMax])) : -INFINITY;
-}
-
-template <typename T>
-__device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s) {
+template <typename T, bool kSample>
+__device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s_lds) {
+  const SeqInfo s = uniform(s_lds);
   const bool residual = s.mode == kModeResidual;
   constexpr int kPer = Logit<T>::kPer;
-  constexpr int kQ = kPer / 8;  // tokens per thread in the rescan
-  static_assert(32 * kPer <= 32 * 16, "rescan buffer");
+  static_assert(kPer / 8 == 2, "a sub-chunk holds two tokens per thread");
   DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1599,147 +1615,164 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     if (tid + u * kThreads < n_words) ws.stage[tid + u * kThreads] = words[u];
   barrier();
   trace_at(1, b, 1);
+  const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
   // Every member must have seen this call's decision, and the decision must
   // call for a draw; otherwise the sequence gets its sentinels here.
-  if (tid < 64) {
-    const unsigned long long bad =
-        __ballot(lane < nm && ws.stage[lane * kW + MemberRec::kStatus] != tagged(P.tag, 1u));
-    if (lane == 0) ws.fail = bad;
-  }
-  barrier();
-  if (P.sample) {
+  const bool failed = __ballot(mine && r[MemberRec::kStatus] != tagged(P.tag, 1u)) != 0ull;
+  const DrawRows<T> d = draw_rows<T>(P, b, s);
+  float m_l = 0.0f, M = 0.0f;  // sampling call: member lane's largest logit, the row's
+  int idx = 0;
+  double scale = 0.0;  // sampling call: member lane's exps times this are relative to the row's maximum
+  if (kSample) {
     // A sampling call: the row's largest logit M and its first index from
     // the members' own; each member's exps rescaled by exp((m_c - M)/T).
     // Its row diagnostics are written here (there is no decision).
-    if (tid < 64) {
-      const float m = mine_sample_max(ws, lane, nm, kW);
-      const float M = wave_max(m);
-      int idx = wave_min(lane < nm && m == M ? int(uint32_t(ws.stage[lane * kW + MemberRec::kArg])) : INT_MAX);
-      if (idx == INT_MAX) idx = 0;  // every logit -inf: every index ties
-      const bool valid = s.mode != kModeInvalid && ws.fail == 0ull;
-      const bool sampled = valid && s.mode == kModeBonus;
-      const double inv_t = sampled ? 1.0 / double(s.temp) : 0.0;
-      const double scale = sampled && lane < nm ? exp_nonpos((double(m) - double(M)) * inv_t) : 0.0;
-      const double zt = wave_sum(lane < nm ? scale * bits_to_double(ws.stage[lane * kW + MemberRec::kZt]) : 0.0);
-      if (lane < nm) {
-        ws.lane_scale[lane] = scale;
-        ws.lane_max[lane] = m;
-      }
-      if (lane == 0) {
-        P.row_lse[b] = sampled ? double(M) * inv_t + log(zt) : double(NAN);
+    m_l = mine ? float(bits_to_double(r[MemberRec::kMax])) : -INFINITY;
+    M = wave_max(m_l);
+    idx = wave_min(mine && m_l == M ? int(uint32_t(r[MemberRec::kArg])) : INT_MAX);
+    if (idx == INT_MAX) idx = 0;  // every logit -inf: every index ties
+    const bool valid = s.mode != kModeInvalid && !failed;
+    const bool sampled = valid && s.mode == kModeBonus;
+    scale = sampled && mine ? exp_nonpos((double(m_l) - double(M)) * d.inv_t) : 0.0;
+    if (!sampled) {
+      if (tid == 0) {
+        P.row_lse[b] = double(NAN);
         P.row_argmax[b] = valid ? idx : -1;
-        if (valid && s.mode == kModeNone) P.out_tokens[b] = idx;  // greedy: the first argmax
+        if (valid) P.out_tokens[b] = idx;  // greedy: the first argmax
       }
+      if (valid) return;
     }
-    barrier();
-    if (ws.fail == 0ull && s.mode == kModeNone) return;
   }
-  if (ws.fail != 0ull || !(s.mode == kModeResidual || s.mode == kModeBonus)) {
+  if (failed || !(residual || s.mode == kModeBonus)) {
     const int code = s.mode == kModeInvalid ? -1 : -2;
     int* otok = P.out_tokens + int64_t(b) * (P.n_draft + 1);
     for (int i = tid; i <= P.n_draft; i += kThreads) otok[i] = code;
     if (tid == 0 && P.out_n != nullptr) P.out_n[b] = code;
     return;
   }
-  DrawRows<T> d = draw_rows<T>(P, b, s);
-  double w[kSubs];
-#pragma unroll
-  for (int k = 0; k < kSubs; ++k) w[k] = 0.0;
-  const uint64_t* r = ws.stage + (mine ? lane : 0) * kW;
-  if (tid < 64) {
-    // Normalisers (fixed-order DPP sums over the members), then member lane's
-    // sub-chunk weights scaled by Zt*Zd: A*Zd - B*Zt of the certain tokens
-    // plus the listed uncertain ones in token order (the bonus: A, scaled by
-    // Zt).
-    double zt = mine ? bits_to_double(r[MemberRec::kZt]) : 0.0;
-    double zd = mine ? bits_to_double(r[MemberRec::kZd]) : 0.0;
-    zt = wave_sum(zt);
-    zd = wave_sum(zd);
-    const double rt = residual ? zd : 1.0;
-    const double rd = residual ? zt : 0.0;
-    const int nunc = mine ? int(r[MemberRec::kNUnc]) : 0;
-#pragma unroll
-    for (int k = 0; k < kSubs; ++k) {
-      const double ak = bits_to_double(r[MemberRec::kA + k]);
-      w[k] = !mine ? 0.0
-             : residual ? fma(ak, rt, -__dmul_rn(bits_to_double(r[MemberRec::kB + k]), rd))
-             : P.sample ? ak * ws.lane_scale[lane]
-                        : ak;
-    }
-    if (residual && nunc <= kUncMax) {
-      for (int i = 0; i < nunc; ++i) {
-        const int sub = (int(r[MemberRec::kPos + i]) - lane * kThreads * kPer) / (32 * kPer);
-        const double v = resid_weight(bits_to_double(r[MemberRec::kEt + i]), bits_to_double(r[MemberRec::kEd + i]), rt, rd);
-#pragma unroll
-        for (int k = 0; k < kSubs; ++k) w[k] += (k == sub) ? v : 0.0;
-      }
-    }
-    const unsigned long long over = __ballot(residual && mine && nunc > kUncMax);
-    if (lane == 0) {
-      ws.rt = rt;
-      ws.rd = rd;
-      ws.over = over;
-    }
+  // Normalisers (fixed-order DPP sums over the members). The draw's weights
+  // are scaled by Zt*Zd: et*Zd - ed*Zt after a rejection; the bonus: et
+  // (sampling call: et times the member's scale).
+  double rt = 1.0, rd = 0.0;
+  if (residual) {
+    rd = wave_sum(mine ? bits_to_double(r[MemberRec::kZt]) : 0.0);
+    rt = wave_sum(mine ? bits_to_double(r[MemberRec::kZd]) : 0.0);
   }
-  barrier();
-  const double rt = ws.rt, rd = ws.rd;
-  // Members whose uncertain tokens overflowed their record: exact weights
-  // (whole workgroup; lane c of wave 0 receives member c's).
-  for (unsigned long long over = ws.over; over != 0ull; over &= over - 1ull)
-    exact_member_weights<T>(P, ws, d, __ffsll(over) - 1, rt, rd, w);
+  const int nunc = residual && mine ? int(r[MemberRec::kNUnc]) : 0;
+  // Members whose uncertain tokens overflowed their record: exact sub-chunk
+  // weights (whole workgroup).
+  const unsigned long long over = __ballot(nunc > kUncMax);
+  for (unsigned long long o = over; o != 0ull; o &= o - 1ull) exact_member_weights<T>(P, ws, d, __ffsll(o) - 1, rt, rd);
+  if (over != 0ull) barrier();
   bool from_q = false;
-  if (tid < 64) {
-    double rem, total;
-    const int pick = wave_inverse_cdf<kSubs>(w, us, true, rem, total);
-    if (lane == 0) {
-      ws.pick = pick;
-      ws.rem = rem;
-      ws.total = total;
+  // Member lane's weight: the sum of its exact sub-chunk weights where the
+  // staged A words hold them; else A*Zd - B*Zt plus its uncertain tokens' in
+  // token order (the bonus: the member's sum of et, scaled when sampling).
+  auto member_weight = [&]() -> double {
+    if (!mine) return 0.0;
+    if (from_q || ((over >> lane) & 1ull)) {
+      double w = 0.0;
+#pragma unroll
+      for (int k = 0; k < kSubs; ++k) w += bits_to_double(r[MemberRec::kA + k]);
+      return w;
     }
-  }
-  barrier();
-  if (residual && !(ws.total > 0.0)) {
+    if (!residual) return kSample ? scale * bits_to_double(r[MemberRec::kZt]) : bits_to_double(r[MemberRec::kZt]);
+    double w = fma(bits_to_double(r[MemberRec::kAt]), rt, -__dmul_rn(bits_to_double(r[MemberRec::kBt]), rd));
+    for (int i = 0; i < nunc; ++i)
+      w += resid_weight(bits_to_double(r[MemberRec::kEt + i]), bits_to_double(r[MemberRec::kEd + i]), rt, rd);
+    return w;
+  };
+  double wl[1] = {member_weight()};
+  double rem, total;
+  int c = wave_inverse_cdf<1>(wl, us, true, rem, total);
+  if (residual && !(total > 0.0)) {
     // Every residual weight rounded to zero: draw from q_j itself, sub-chunk
     // by sub-chunk exactly.
     from_q = true;
-    for (int c = 0; c < nm; ++c) exact_member_weights<T>(P, ws, d, c, rt, 0.0, w);
-    if (tid < 64) {
-      double rem, total;
-      const int pick = wave_inverse_cdf<kSubs>(w, us, true, rem, total);
-      if (lane == 0) {
-        ws.pick = pick;
-        ws.rem = rem;
+    for (int cc = 0; cc < nm; ++cc) exact_member_weights<T>(P, ws, d, cc, rt, 0.0);
+    barrier();
+    wl[0] = member_weight();
+    c = wave_inverse_cdf<1>(wl, us, true, rem, total);
+  }
+  c = max(c, 0);
+  // Member c's tokens, two of each sub-chunk per thread (the crossing
+  // sub-chunk's are the ones used), requested before its sub-chunk weights
+  // are formed.
+  const bool two_rows = residual && !from_q;
+  const bool vec_ok = (P.flags & kVecOk) != 0;
+  const int x0 = c * kThreads * kPer + 2 * tid;
+  PairRow<T> pt, pd;
+  pt.load(d.trow, x0, P.vocab, vec_ok);
+  if (two_rows) pd.load(d.drow, x0, P.vocab, vec_ok);
+  // A sampling call's row log-normaliser, while the loads are in flight.
+  const double lse = kSample ? double(M) * d.inv_t + log(wave_sum(wl[0])) : 0.0;
+  // Member c's sub-chunk weights (lane k < kSubs holds sub-chunk k's) and
+  // the crossing sub-chunk, against what remains of u*S past the members
+  // before c.
+  const uint64_t* rc = ws.stage + c * kW;
+  const double scale_c = kSample ? read_lane(scale, c) : 1.0;
+  double wk = 0.0;
+  if (lane < kSubs) {
+    wk = bits_to_double(rc[MemberRec::kA + lane]);
+    if (!(from_q || ((over >> c) & 1ull))) {
+      if (residual) {
+        wk = fma(wk, rt, -__dmul_rn(bits_to_double(rc[MemberRec::kB + lane]), rd));
+        const int nu = int(rc[MemberRec::kNUnc]);  // <= kUncMax: the member's list is whole
+        for (int i = 0; i < nu; ++i) {
+          const int sub = (int(rc[MemberRec::kPos + i]) - c * kThreads * kPer) / (32 * kPer);
+          if (sub == lane)
+            wk += resid_weight(bits_to_double(rc[MemberRec::kEt + i]), bits_to_double(rc[MemberRec::kEd + i]), rt, rd);
+        }
+      } else if (kSample) {
+        wk *= scale_c;
       }
     }
-    barrier();
   }
-  const int pick = max(ws.pick, 0);
-  const double rem = ws.rem;
+  double wv[1] = {wk};
+  double rem2, total2;
+  const int sub = max(wave_inverse_cdf<1>(wv, rem, false, rem2, total2), 0);
   trace_at(1, b, 2);
-  // The crossing sub-chunk's exact token weights (kQ per thread, in token
+  // The crossing sub-chunk's exact token weights (two per thread, in token
   // order), then wave 0 finds the token: lane l takes weights 8l .. 8l+7. (A
   // sampling call's member exps are relative to its own maximum, scaled.)
-  double wq[kQ];
-  int e0;
-  const int pc = pick / kSubs;
-  if (P.sample) d.nmt = ws.lane_max[pc] == -INFINITY ? 0.0 : -double(ws.lane_max[pc]) * d.inv_t;
-  sub_weights<T>(P, d, ws.exp2_tab, pc, pick % kSubs, residual, P.sample ? ws.lane_scale[pc] : rt,
-                 from_q ? 0.0 : rd, wq, e0);
-  trace_at(1, b, 3);
+  float zt[2], zd[2] = {0.0f, 0.0f};
+  pt.take(sub, x0, P.vocab, vec_ok, zt[0], zt[1]);
+  if (two_rows) pd.take(sub, x0, P.vocab, vec_ok, zd[0], zd[1]);
+  double nmt = d.nmt;
+  if (kSample) {
+    const float m_c = __int_as_float(read_lane(__float_as_int(m_l), c));
+    nmt = m_c == -INFINITY ? 0.0 : -double(m_c) * d.inv_t;
+  }
+  const double rts = kSample ? scale_c : rt;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) ws.tw[tid * kQ + q] = wq[q];
+  for (int q = 0; q < 2; ++q) {
+    const double et = exp_nonpos_tab(exp_arg(zt[q], nmt, d.inv_t), ws.exp2_tab);
+    double wq;
+    if (two_rows) {
+      const double ed = exp_nonpos_tab(exp_arg(zd[q], d.nmd, d.inv_t), ws.exp2_tab);
+      wq = rd > 0.0 ? resid_weight(et, ed, rts, rd) : et * rts;
+    } else {
+      wq = et * rts;  // (rt = 1 for a verification's bonus draw: exact)
+    }
+    ws.tw[tid * 2 + q] = wq;
+  }
+  trace_at(1, b, 3);
   barrier();
   if (tid < 64) {
     constexpr int kL = 32 * kPer / 64;  // token weights per lane
     double v[kL];
 #pragma unroll
     for (int k = 0; k < kL; ++k) v[k] = ws.tw[lane * kL + k];
-    double rem2, total2;
-    const int k = wave_inverse_cdf<kL>(v, rem, false, rem2, total2);
+    double rem3, total3;
+    const int k = wave_inverse_cdf<kL>(v, rem2, false, rem3, total3);
     if (lane == 0) {
-      const int first = (pick / kSubs) * kThreads * kPer + (pick % kSubs) * 32 * kPer;
+      const int first = c * kThreads * kPer + sub * 32 * kPer;
       P.out_tokens[int64_t(b) * (P.n_draft + 1) + s.j] = k >= 0 ? first + k : 0;
       if (P.out_n != nullptr) P.out_n[b] = s.j;
+      if (kSample) {
+        P.row_lse[b] = lse;
+        P.row_argmax[b] = idx;
+      }
     }
   }
 }
@@ -1826,15 +1859,19 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp
 // (with whether it saw this call's decision) when done; the last one clears
 // the decision's record and finishes the sequence: its token and n_accepted,
 // or its sentinels.
-template <typename T>
+template <typename T, bool kSample>
 __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
+  // A sampling call's row is known from the start: its logits are requested
+  // before anything waits for the temperature.
+  MemberRows<T> rows;
+  if (kSample) rows.load(P, DrawRows<T>{static_cast<const T*>(P.target) + int64_t(b) * P.vocab, nullptr, 0.0, 0.0, 0.0}, c, false);
   const float temp = load_uniform(P.temperature + b);
-  if (!P.sample && !has_draw_members(temp)) return;
+  if (!kSample && !has_draw_members(temp)) return;
   trace_set(unsigned(b) * unsigned(P.nm) + unsigned(c));
   trace(0, 0);
   SeqInfo s;
   bool saw = true;
-  if (P.sample) {
+  if (kSample) {
     // No decision: the row's own draw (the first argmax when greedy).
     bool bad = !temperature_valid(temp);
     if (P.flags & kDebug) {
@@ -1847,8 +1884,10 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
     saw = wait_decision(P, b, temp, s);
   }
   trace(0, 5);
-  if (s.mode == kModeResidual || s.mode == kModeBonus || (P.sample && s.mode == kModeNone))
-    member_record<T>(P, sh, b, c, s);
+  if (s.mode == kModeResidual || s.mode == kModeBonus || (kSample && s.mode == kModeNone)) {
+    if (!kSample) rows.load(P, draw_rows<T>(P, b, s), c, s.mode == kModeResidual);
+    member_record<T, kSample>(P, sh, b, c, s, rows);
+  }
   if (threadIdx.x == 0) put_u64(&P.records[int64_t(b) * P.nm + c].w[MemberRec::kStatus], tagged(P.tag, saw ? 1u : 0u));
   trace(0, 3);
   const bool last = last_arrival(P.draw_done + b * kCounterStride, P.nm);
@@ -1866,7 +1905,7 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
     // the member's work (where it made the fp32 build spill).
     asm volatile("" ::: "memory");
     const SeqInfo s_again = g_seq;
-    finish<T>(P, sh, b, s_again);
+    finish<T, kSample>(P, sh, b, s_again);
     trace_at(1, b, 4);
   }
 }
@@ -1888,13 +1927,6 @@ struct Role {
 
 __device__ __forceinline__ Role role_of(const Params& P, int x) {
   Role w;
-  if (P.sample) {
-    w.kind = 2;
-    w.s = 0;
-    w.b = x / P.nm;
-    w.idx = x - w.b * P.nm;
-    return w;
-  }
   if (P.lazy) {
     int s = 0;
     while (s < P.n_stages && x >= P.st_base[s + 1]) ++s;
@@ -1955,7 +1987,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   else if (w.kind == 1)
     decision_role<T>(P, sh, stage_at(P, w.s), w.b);
   else
-    draw_role<T>(P, sh, w.b, w.idx);
+    draw_role<T, false>(P, sh, w.b, w.idx);
+}
+
+// The draft-side draw: draw members only, member c of row b being workgroup
+// b * nm + c; each row's draw is a bonus draw from the row alone.
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void sample_kernel(Params P) {
+  const int x = int(blockIdx.x);
+  const int b = x / P.nm;
+  draw_role<T, true>(P, g_shared, b, x - b * P.nm);
 }
 
 const char* const kStageNames[] = {"verify"};
@@ -1985,11 +2026,10 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   p.chunk = w.stat_chunk;
   p.nm = w.n_members;
   p.lazy = a.lazy ? 1 : 0;
-  p.sample = a.sample ? 1 : 0;
   p.alive = w.alive;
   p.items_per_seq = (2 * a.n_draft + 1) * w.n_stat_chunks;
   int64_t blocks;
-  if (p.sample) {
+  if (a.sample) {
     p.n_stages = 1;
     p.st_bound[0] = 0;
     p.st_bound[1] = 0;
@@ -2021,7 +2061,10 @@ hipError_t launch_typed(const VerifyArgs& a, const Workspace& w, hipStream_t str
   // (not min(): on the host it takes ints)
   p.wait_ticks = a.wait_ticks > uint64_t(UINT32_MAX) ? UINT32_MAX : uint32_t(a.wait_ticks);
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
+  if (a.sample)
+    hipLaunchKernelGGL(sample_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(verify_kernel<T>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
   return hipGetLastError();
 }
