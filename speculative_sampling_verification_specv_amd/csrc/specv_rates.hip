@@ -64,11 +64,10 @@ struct Elem<uint16_t> {  // bfloat16 bits
 };
 
 // min(p, q) of one token: p = 2^(zd*c - Ld*log2e), q likewise, each argument
-// formed in fp64 (exact to about 1e-16 of its size) and exponentiated in fp32.
+// formed in fp64 (exact to about 1e-16 of its size). exp2 is increasing, so
+// min(p, q) is 2^ of the smaller argument: one fp32 exp per token.
 __device__ __forceinline__ float min_pq(float zd, float zt, double c, double ld, double lt) {
-  const float p = __builtin_amdgcn_exp2f(float(fma(double(zd), c, ld)));
-  const float q = __builtin_amdgcn_exp2f(float(fma(double(zt), c, lt)));
-  return fminf(p, q);
+  return __builtin_amdgcn_exp2f(float(fmin(fma(double(zd), c, ld), fma(double(zt), c, lt))));
 }
 
 // A 16-byte load marked non-temporal: each logit is read once.
@@ -89,17 +88,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
   const int i = bi % N, b = bi / N;
   const int tid = int(threadIdx.x);
   double* out = P.parts + (int64_t(b) * N + i) * P.nch + c;
-  const float t = P.temperature[b];
-  const double ld = P.row_lse[int64_t(b) * R + i], lt = P.row_lse[int64_t(b) * R + N + i];
-  if (!sampled_temperature(t) || isnan(ld) || isnan(lt)) {
-    if (tid == 0) *out = NAN;
-    return;
-  }
   const T* drow = static_cast<const T*>(P.draft) + (int64_t(b) * N + i) * P.vocab;
   const T* trow = static_cast<const T*>(P.target) + (int64_t(b) * (N + 1) + i) * P.vocab;
   const int e0 = c * P.chunk, e1 = min(P.vocab, e0 + P.chunk);
   // Every 16-byte load of both rows is issued (at a clamped, valid index)
-  // before any arithmetic, so the item's 64 KB are in flight at once.
+  // before any arithmetic, and before the row's temperature and
+  // log-normalisers are waited for, so the item's 64 KB are in flight at once.
   const int nv = P.vec_ok ? (e1 - e0) / kVec : 0;
   uint4 xd[kLoads], xt[kLoads];
   if (nv > 0) {
@@ -111,6 +105,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
       xd[u] = load_stream(dv + v);
       xt[u] = load_stream(tv + v);
     }
+  }
+  const float t = P.temperature[b];
+  const double ld = P.row_lse[int64_t(b) * R + i], lt = P.row_lse[int64_t(b) * R + N + i];
+  if (!sampled_temperature(t) || isnan(ld) || isnan(lt)) {
+    if (tid == 0) *out = NAN;
+    return;
   }
   const double cf = kLog2eD / double(t);
   const double nld = -ld * kLog2eD, nlt = -lt * kLog2eD;
