@@ -880,7 +880,12 @@ static_assert(int64_t(kMaxVocab) * 4 / kStatBytes <= kStageParts, "a row's parti
 
 static_assert(sizeof(kExp2Table) == kThreads * sizeof(double), "the exp table is filled one entry per thread");
 
+// A draw workgroup's LDS. The sampling kernel stages only the first words of
+// each member record (it has no draft row and no uncertain tokens), which
+// keeps its LDS small enough for eight workgroups per CU.
+template <bool kSample>
 struct DrawShared {
+  static constexpr int kStageWords = kSample ? MemberRec::kNUnc + 1 : MemberRec::kWords;
   double red[4 * kWaves];
   double exp2_tab[kThreads];  // kExp2Table, for exp_nonpos_tab (members and the finisher)
   union {
@@ -888,7 +893,7 @@ struct DrawShared {
       double unc_et[2][kThreads];  // member: staged uncertain tokens (two per thread)
       double unc_ed[2][kThreads];
     } mem;
-    uint64_t stage[kMaxMembers * MemberRec::kWords];  // finisher: the sequence's member records
+    uint64_t stage[kMaxMembers * kStageWords];  // finisher: the sequence's member records
   };
   double tw[32 * 16];  // finisher: the crossing sub-chunk's token weights
   float wave_m[kWaves];            // sampling member: each wave's largest logit and its first index
@@ -899,11 +904,12 @@ struct DrawShared {
 struct Shared {
   union {
     DecideShared dec;
-    DrawShared drw;
+    DrawShared<false> drw;
   } u;
 };
 
 __shared__ Shared g_shared;
+__shared__ DrawShared<true> g_sample_shared;
 
 struct SeqInfo {
   float temp;
@@ -1241,13 +1247,12 @@ struct MemberRows {
 };
 
 template <typename T, bool kSample>
-__device__ __forceinline__ void member_record(const Params& P, Shared& sh, int b, int c, const SeqInfo& s,
-                                              MemberRows<T>& rows) {
-  const bool residual = s.mode == kModeResidual;
+__device__ __forceinline__ void member_record(const Params& P, DrawShared<kSample>& ws, int b, int c,
+                                              const SeqInfo& s, MemberRows<T>& rows) {
+  const bool residual = !kSample && s.mode == kModeResidual;
   const bool draw = residual || s.mode == kModeBonus;  // (a sampling call's greedy row: the maximum only)
   constexpr int kPer = Logit<T>::kPer;
   constexpr int kG = MemberRows<T>::kG;
-  DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   DrawRows<T> d = draw_rows<T>(P, b, s);
@@ -1470,7 +1475,7 @@ __device__ __forceinline__ double sub_weights(const Params& P, const DrawRows<T>
 // takes as the sub-chunk weights themselves. The caller makes them visible
 // with a barrier.
 template <typename T>
-__device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared& ws, const DrawRows<T>& d, int c,
+__device__ __forceinline__ void exact_member_weights(const Params& P, DrawShared<false>& ws, const DrawRows<T>& d, int c,
                                                      double rt, double rd) {
 #pragma unroll 1
   for (int sub = 0; sub < kSubs; ++sub) {
@@ -1590,26 +1595,29 @@ __device__ __forceinline__ int wave_inverse_cdf(const double (&w)[n], double u, 
 }
 
 template <typename T, bool kSample>
-__device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const SeqInfo& s_lds) {
+__device__ __forceinline__ void finish(const Params& P, DrawShared<kSample>& ws, int b, const SeqInfo& s_lds) {
   const SeqInfo s = uniform(s_lds);
-  const bool residual = s.mode == kModeResidual;
+  const bool residual = !kSample && s.mode == kModeResidual;
   constexpr int kPer = Logit<T>::kPer;
   static_assert(kPer / 8 == 2, "a sub-chunk holds two tokens per thread");
-  DrawShared& ws = sh.u.drw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int nm = P.nm;  // <= 64
   const bool mine = lane < nm;
   const double us = double(load_uniform(P.sample_u + b));  // in flight from the start
-  // The sequence's member records, in one coalesced round trip: every load
-  // is issued (at a clamped index) before any is stored.
-  constexpr int kW = MemberRec::kWords;
+  // The sequence's member records (their first kW words each), in one
+  // coalesced round trip: every load is issued (at a clamped index) before
+  // any is stored.
+  constexpr int kW = DrawShared<kSample>::kStageWords;
   constexpr int kStageIters = (kMaxMembers * kW + kThreads - 1) / kThreads;
-  const uint64_t* src = P.records[0].w + (int64_t(b) * nm) * kW;
+  const uint64_t* src = P.records[0].w + (int64_t(b) * nm) * MemberRec::kWords;
   const int n_words = nm * kW;
   uint64_t words[kStageIters];
 #pragma unroll
-  for (int u = 0; u < kStageIters; ++u) words[u] = get_u64(src + min(tid + u * kThreads, n_words - 1));
+  for (int u = 0; u < kStageIters; ++u) {
+    const int i = min(tid + u * kThreads, n_words - 1);
+    words[u] = get_u64(src + (kW == MemberRec::kWords ? i : (i / kW) * MemberRec::kWords + i % kW));
+  }
 #pragma unroll
   for (int u = 0; u < kStageIters; ++u)
     if (tid + u * kThreads < n_words) ws.stage[tid + u * kThreads] = words[u];
@@ -1662,8 +1670,10 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
   // Members whose uncertain tokens overflowed their record: exact sub-chunk
   // weights (whole workgroup).
   const unsigned long long over = __ballot(nunc > kUncMax);
-  for (unsigned long long o = over; o != 0ull; o &= o - 1ull) exact_member_weights<T>(P, ws, d, __ffsll(o) - 1, rt, rd);
-  if (over != 0ull) barrier();
+  if constexpr (!kSample) {
+    for (unsigned long long o = over; o != 0ull; o &= o - 1ull) exact_member_weights<T>(P, ws, d, __ffsll(o) - 1, rt, rd);
+    if (over != 0ull) barrier();
+  }
   bool from_q = false;
   // Member lane's weight: the sum of its exact sub-chunk weights where the
   // staged A words hold them; else A*Zd - B*Zt plus its uncertain tokens' in
@@ -1689,8 +1699,10 @@ __device__ __forceinline__ void finish(const Params& P, Shared& sh, int b, const
     // Every residual weight rounded to zero: draw from q_j itself, sub-chunk
     // by sub-chunk exactly.
     from_q = true;
-    for (int cc = 0; cc < nm; ++cc) exact_member_weights<T>(P, ws, d, cc, rt, 0.0);
-    barrier();
+    if constexpr (!kSample) {
+      for (int cc = 0; cc < nm; ++cc) exact_member_weights<T>(P, ws, d, cc, rt, 0.0);
+      barrier();
+    }
     wl[0] = member_weight();
     c = wave_inverse_cdf<1>(wl, us, true, rem, total);
   }
@@ -1860,7 +1872,7 @@ __device__ __forceinline__ bool wait_decision(const Params& P, int b, float temp
 // the decision's record and finishes the sequence: its token and n_accepted,
 // or its sentinels.
 template <typename T, bool kSample>
-__device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, int c) {
+__device__ __forceinline__ void draw_role(const Params& P, DrawShared<kSample>& ws, int b, int c) {
   // A sampling call's row is known from the start: its logits are requested
   // before anything waits for the temperature.
   MemberRows<T> rows;
@@ -1886,7 +1898,7 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
   trace(0, 5);
   if (s.mode == kModeResidual || s.mode == kModeBonus || (kSample && s.mode == kModeNone)) {
     if (!kSample) rows.load(P, draw_rows<T>(P, b, s), c, s.mode == kModeResidual);
-    member_record<T, kSample>(P, sh, b, c, s, rows);
+    member_record<T, kSample>(P, ws, b, c, s, rows);
   }
   if (threadIdx.x == 0) put_u64(&P.records[int64_t(b) * P.nm + c].w[MemberRec::kStatus], tagged(P.tag, saw ? 1u : 0u));
   trace(0, 3);
@@ -1905,7 +1917,7 @@ __device__ __forceinline__ void draw_role(const Params& P, Shared& sh, int b, in
     // the member's work (where it made the fp32 build spill).
     asm volatile("" ::: "memory");
     const SeqInfo s_again = g_seq;
-    finish<T, kSample>(P, sh, b, s_again);
+    finish<T, kSample>(P, ws, b, s_again);
     trace_at(1, b, 4);
   }
 }
@@ -1987,16 +1999,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))
   else if (w.kind == 1)
     decision_role<T>(P, sh, stage_at(P, w.s), w.b);
   else
-    draw_role<T, false>(P, sh, w.b, w.idx);
+    draw_role<T, false>(P, sh.u.drw, w.b, w.idx);
 }
 
 // The draft-side draw: draw members only, member c of row b being workgroup
-// b * nm + c; each row's draw is a bonus draw from the row alone.
+// b * nm + c; each row's draw is a bonus draw from the row alone. Eight
+// waves per SIMD (its registers and LDS allow eight workgroups per CU).
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 8))) void sample_kernel(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void sample_kernel(Params P) {
   const int x = int(blockIdx.x);
   const int b = x / P.nm;
-  draw_role<T, true>(P, g_shared, b, x - b * P.nm);
+  draw_role<T, true>(P, g_sample_shared, b, x - b * P.nm);
 }
 
 const char* const kStageNames[] = {"verify"};
