@@ -52,7 +52,7 @@ constexpr float kFltMax = 3.402823466e38f;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRows = 2 * 64 + 1;
 constexpr int kStatVecs = kStatBytes / 16 / kThreads;  // 16-byte vectors per thread per item
-static_assert(kMaxMembers <= 64, "one member per lane of the finisher's wave 0");
+static_assert(kMaxMembers <= 64, "one member per lane of each of the finisher's waves");
 
 
 __device__ __forceinline__ bool temperature_valid(float t) {
@@ -1548,7 +1548,7 @@ struct PairRow {
 // rounding, and each search falls back to its last positive value when
 // rounding leaves no crossing.
 
-// Inverse CDF within wave 0 over n values per lane, in lane order then value
+// Inverse CDF within one wave over n values per lane, in lane order then value
 // order, against `target`: the first value with positive weight whose
 // inclusive prefix exceeds it, else the last positive one; returns lane*n +
 // index (-1 if none is positive) and rem = target minus the prefix before it.
