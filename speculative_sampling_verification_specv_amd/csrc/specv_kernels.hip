@@ -229,7 +229,6 @@ struct Logit<float> {
     const uint32_t w = (k % 4 == 0) ? v.x : (k % 4 == 1) ? v.y : (k % 4 == 2) ? v.z : v.w;
     return __uint_as_float(w);
   }
-  __device__ static float staged(const uint32_t (*st)[kThreads], int k, int tid) { return __uint_as_float(st[k][tid]); }
   __device__ static void unpack(const uint4& x, float (&v)[kVec]) {
     v[0] = __uint_as_float(x.x);
     v[1] = __uint_as_float(x.y);
@@ -254,10 +253,6 @@ struct Logit<uint16_t> {  // bfloat16 bits
     const uint32_t w = (h < 2) ? v.x : (h < 4) ? v.y : (h < 6) ? v.z : v.w;
     return __uint_as_float((h & 1) ? (w & 0xffff0000u) : (w << 16));
   }
-  __device__ static float staged(const uint32_t (*st)[kThreads], int k, int tid) {
-    const uint32_t w = st[k >> 1][tid];
-    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
   __device__ static void unpack(const uint4& x, float (&v)[kVec]) {
     v[0] = __uint_as_float(x.x << 16);
     v[1] = __uint_as_float(x.x & 0xffff0000u);
@@ -269,32 +264,6 @@ struct Logit<uint16_t> {  // bfloat16 bits
     v[7] = __uint_as_float(x.w & 0xffff0000u);
   }
 };
-
-// kPer consecutive logits of a row starting at element e, as fp32; -inf at
-// and past `vocab`. 16-byte loads when the row start is 16-byte aligned and
-// the run lies inside the row.
-template <typename T>
-__device__ __forceinline__ void load_run(const T* __restrict__ row, int e, int vocab, bool vec_ok,
-                                         float (&z)[Logit<T>::kPer]) {
-  constexpr int kVec = Logit<T>::kVec;
-  constexpr int kPer = Logit<T>::kPer;
-  if (vec_ok && e + kPer <= vocab) {
-    const uint4* __restrict__ p = reinterpret_cast<const uint4*>(row + e);
-    uint4 x[kPer / kVec];
-#pragma unroll
-    for (int u = 0; u < kPer / kVec; ++u) x[u] = p[u];
-#pragma unroll
-    for (int u = 0; u < kPer / kVec; ++u) {
-      float v[kVec];
-      Logit<T>::unpack(x[u], v);
-#pragma unroll
-      for (int k = 0; k < kVec; ++k) z[u * kVec + k] = v[k];
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) z[k] = (e + k < vocab) ? Logit<T>::at(row, e + k) : -INFINITY;
-  }
-}
 
 // kPer consecutive logits of a row from element e, packed as stored (16-byte
 // loads when aligned and inside the row; elements past `vocab` read as -inf).
