@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,6 +57,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "OUT"),
                     help="write the HBM traffic summary of the verification kernel from rocprofv3 --pmc "
                          "output (FETCH_SIZE and WRITE_SIZE runs under PMC_DIR) to OUT, then exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "OUT"),
+                    help="write per-launch durations from a rocprofv3 --kernel-trace CSV, grouped by kernel "
+                         "and grid size (the lazy and whole verifications share a kernel), to OUT, then exit")
     return ap.parse_args()
 
 
@@ -203,6 +207,39 @@ def _pmc_rows(pmc_dir: str):
                     for row in csv.DictReader(f):
                         yield (os.path.join(dirpath, fn), int(row["Dispatch_Id"])), row["Kernel_Name"], \
                             row["Counter_Name"], float(row["Counter_Value"])
+
+
+def summarize_trace(trace_csv: str, out: str) -> int:
+    """Launch durations of this library's kernels in a rocprofv3 kernel trace,
+    one line per (kernel, grid size): count, mean, median, min and max in us."""
+    import csv
+
+    groups: dict = {}
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if not re.search(r"\b(verify|sample|rate_parts|rate_finish|kv_commit)_kernel\b|narrow_to_float|zero_words",
+                             name):
+                continue
+            short = name
+            if short.endswith(")"):  # drop the parameter list: back to the parenthesis matching the last one
+                depth = 0
+                for i in range(len(short) - 1, -1, -1):
+                    depth += {")": 1, "(": -1}.get(short[i], 0)
+                    if depth == 0:
+                        short = short[:i]
+                        break
+            short = short.split("::")[-1]
+            key = (short, int(row["Grid_Size_X"]))
+            groups.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    lines = ["# kernel, grid size (work-items), launches, mean / median / min / max duration (us)\n"]
+    for (short, grid), d in sorted(groups.items()):
+        a = np.asarray(d)
+        lines.append(f"{short}, {grid}, {a.size}, {a.mean():.2f} / {np.median(a):.2f} / {a.min():.2f} / "
+                     f"{a.max():.2f}\n")
+    with open(out, "w") as f:
+        f.writelines(lines)
+    return 0
 
 
 def summarize_pmc(pmc_dir: str, out: str, workload: str, copy_mb: int, kernel: str = "verify") -> int:
@@ -487,6 +524,8 @@ def main() -> int:
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                              args.calibrate_copy_mb or 256)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
