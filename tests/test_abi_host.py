@@ -112,3 +112,50 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load_library(str(tmp_path / "libspecv.so"))
+
+
+def test_header_is_c_and_links(tmp_path):
+    """include/specv.h compiles as strict C11, a C program links every declared
+    entry point from libspecv.so, and its host-side argument checks answer
+    from C as they do through the binding."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    specv.load_library()  # the built library must exist (fails loudly otherwise)
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    names = _declared_functions()
+    src = tmp_path / "abi.c"
+    src.write_text("\n".join([
+        "#include <stdio.h>",
+        "#include \"specv.h\"",
+        "typedef void (*any_fn)(void);",
+        "static any_fn const entry_points[] = {",
+        *[f"  (any_fn){n}," for n in names],
+        "};",
+        "int main(void) {",
+        "  specv_handle h = NULL;",
+        "  int bad = 0;",
+        "  bad |= specv_create(&h, 0, 1, 16, SPECV_F32, 0) != SPECV_EINVAL || h != NULL;",
+        "  bad |= specv_create(&h, 1, SPECV_MAX_DRAFT + 1, 16, SPECV_BF16, 0) != SPECV_EINVAL;",
+        "  bad |= specv_verify(NULL, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) != SPECV_EINVAL;",
+        "  bad |= specv_verify_static(257, 1, 16, SPECV_F32, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL)",
+        "         != SPECV_ERANGE;",
+        "  bad |= specv_strerror(SPECV_OK) == NULL;",
+        "  specv_destroy(NULL);",
+        "  printf(\"%d entry points, checks %s\\n\", (int)(sizeof entry_points / sizeof entry_points[0]),",
+        "         bad ? \"failed\" : \"passed\");",
+        "  return bad;",
+        "}",
+        "",
+    ]))
+    exe = tmp_path / "abi"
+    cmd = [cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.dirname(HEADER), str(src), "-L", lib_dir, "-lspecv", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stdout + proc.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert f"{len(names)} entry points, checks passed" in run.stdout
