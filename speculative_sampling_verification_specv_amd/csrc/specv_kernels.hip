@@ -900,6 +900,14 @@ __device__ __forceinline__ SeqInfo uniform(const SeqInfo& s) {
                  f(s.m_draft), bits_to_double((uint64_t(hi) << 32) | lo)};
 }
 
+// Whether a whole call reads each sequence's target row N late in the launch
+// (after the accept tests; see decide and role_of). Row N only matters to a
+// sequence's draw when every draft is accepted, which long drafts rarely
+// are; there this takes 1.5 us off B = 32, N = 16 and moves nothing for
+// shorter drafts (B = 64, N = 5 level, B = 256, N = 7 2 us slower).
+constexpr int kLateRowNDrafts = 8;
+__device__ __forceinline__ bool late_row_n(const Params& P) { return !P.lazy && P.n_draft >= kLateRowNDrafts; }
+
 // Waits (until `deadline`) for partial q of this call (its item starts at
 // element e0 of the row), then takes it and zeroes its words. Returns false
 // if the wait gave up (always, when the wait bound is 0: the host's way to
@@ -967,6 +975,13 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
   const int lo = st.lo, hi = st.hi, ns = hi - lo;
   const bool last = hi == N;
   const int Rs = go > 0 ? stage_rows(P, st) : 0;  // no partials are taken after a failed wait
+  // A long draft's target row N is read by items placed later in the launch
+  // (just before the sequence's draw members; see role_of): the accept tests
+  // do not need it, so its partials are taken after them, and only a
+  // sequence that accepts every draft waits for them before its draw is
+  // published.
+  const bool split = late_row_n(P) && last && Rs > 0;
+  const int Rs_main = split ? Rs - 1 : Rs;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1015,10 +1030,15 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
   constexpr int cs = 4;
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
-  const uint64_t deadline = deadline_after(P.wait_ticks);
   bool timed_out = go < 0, any_bad = false;
-  for (int rg = 0; rg < Rs; rg += rows_per_group) {
-    const int nr = min(rows_per_group, Rs - rg);
+  // Takes the partials of the stage's rows [r0, r1) a group at a time and
+  // merges them (unless the sequence has failed); returns whether a partial
+  // of these rows came too late.
+  auto take_rows = [&](int r0, int r1) -> bool {
+    const uint64_t deadline = deadline_after(P.wait_ticks);
+    bool rows_late = false;
+    for (int rg = r0; rg < r1; rg += rows_per_group) {
+    const int nr = min(rows_per_group, r1 - rg);
     const int np = nr * pr;
     bool late = false;
     if (tid < np) {
@@ -1032,8 +1052,8 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
     // before anything waits for the draft tokens.
     const int vote = block_any2(rg == 0 && bad, late);
     any_bad = any_bad || (vote & 1);
-    timed_out = timed_out || (vote & 2);
-    if (any_bad || timed_out) continue;
+    rows_late = rows_late || (vote & 2);
+    if (any_bad || timed_out || rows_late) continue;
     if (rg == 0) trace(2, 4);
     for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
       const int rr = r0 + seg;
@@ -1072,7 +1092,11 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
       }
     }
     barrier();
-  }
+    }
+    return rows_late;
+  };
+  timed_out = take_rows(0, Rs_main) || timed_out;
+  if (split && (any_bad || timed_out)) take_rows(Rs_main, Rs);  // taken (and zeroed) all the same
   if (any_bad || timed_out) {
     // Invalid inputs give -1 everywhere; a partial that never came (not
     // expected: a workgroup that was not dispatched in time) gives -2.
@@ -1121,9 +1145,10 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
   const unsigned long long rej = ds.rej_mask;
   const int j = rej ? lo + (__ffsll(rej) - 1) : hi;
   const bool go_on = j == hi && !last;  // a lazy call's sequence that goes on to the next stage
+  const bool needs_row_n = split && j == N;  // the bonus (greedy: the argmax of row N) waits for row N
   // The draw's record first (the draw members wait for it), or the next
   // stage's go-on words.
-  if (tid == 0 && !greedy && !go_on) {
+  if (tid == 0 && !greedy && !go_on && !needs_row_n) {
     const float md = j < N ? ds.row_m[j] : 0.0f;
     const double log_rho = j < N ? ds.row_logz[N + j] - ds.row_logz[j] : 0.0;
     publish(P, b, j < N ? kModeResidual : kModeBonus, j, ds.row_m[N + j], md, log_rho);
@@ -1139,10 +1164,36 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
       break;
     else if (i > j)
       otok[i] = -1;
-    else if (greedy)
+    else if (greedy && !needs_row_n)
       otok[i] = ds.row_idx[N + j];
   }
-  if (tid == 0 && greedy && !go_on && P.out_n != nullptr) P.out_n[b] = j;
+  if (tid == 0 && greedy && !go_on && !needs_row_n && P.out_n != nullptr) P.out_n[b] = j;
+  if (!split) return;
+  // Target row N: its diagnostics, and the draw or the greedy token of a
+  // sequence that accepted every draft.
+  if (take_rows(Rs_main, Rs)) {
+    if (tid == 0) {
+      lse[2 * N] = NAN;
+      amax[2 * N] = -1;
+    }
+    if (needs_row_n) {
+      if (draws) {
+        if (tid == 0) publish(P, b, kModeFailed, 0, 0.0f, 0.0f, 0.0);
+      } else {
+        for (int i = tid; i <= N; i += kThreads) otok[i] = -2;
+        if (tid == 0 && P.out_n != nullptr) P.out_n[b] = -2;
+      }
+    }
+    return;
+  }
+  if (needs_row_n && tid == 0) {
+    if (greedy) {
+      otok[N] = ds.row_idx[2 * N];
+      if (P.out_n != nullptr) P.out_n[b] = N;
+    } else {
+      publish(P, b, kModeBonus, N, ds.row_m[2 * N], 0.0f, 0.0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1927,34 +1978,45 @@ __device__ __forceinline__ Role role_of(const Params& P, int x) {
     w.kind = w.idx < A - 1 ? 0 : 1;
     return w;
   }
-  const int A = P.items_per_seq + 1, M = P.nm, L = P.lag;
-  int b, z;
-  bool stat;
-  if (x < L * A) {
-    stat = true;
-    b = x / A;
-    z = x - b * A;
-  } else {
-    x -= L * A;
-    const int n1 = P.batch - L;  // pairs (statistics group of p + L, draw of p)
-    if (x < n1 * (A + M)) {
-      const int p = x / (A + M);
-      z = x - p * (A + M);
-      stat = z < A;
-      b = stat ? p + L : p;
-      if (!stat) z -= A;
-    } else {
-      x -= n1 * (A + M);
-      const int p = x / M;
-      stat = false;
-      b = n1 + p;
-      z = x - p * M;
-    }
-  }
-  w.kind = stat ? (z < A - 1 ? 0 : 1) : 2;
+  // With a late row N (long drafts), a sequence's statistics group holds only
+  // the items of its draft rows and target rows 0..N-1 and its decision; the
+  // K items of its target row N come just before its draw members.
+  const int K = late_row_n(P) ? P.nch : 0;
+  const int A = P.items_per_seq - K + 1, M = P.nm, L = P.lag, D = K + M;
   w.s = 0;
-  w.b = b;
-  w.idx = z;
+  if (x < L * A) {
+    w.b = x / A;
+    const int z = x - w.b * A;
+    w.kind = z < A - 1 ? 0 : 1;
+    w.idx = z;
+    return w;
+  }
+  x -= L * A;
+  const int n1 = P.batch - L;  // pairs (statistics group of p + L, row N and draw of p)
+  int p, z;
+  if (x < n1 * (A + D)) {
+    p = x / (A + D);
+    z = x - p * (A + D);
+    if (z < A) {
+      w.b = p + L;
+      w.kind = z < A - 1 ? 0 : 1;
+      w.idx = z;
+      return w;
+    }
+    z -= A;
+  } else {
+    x -= n1 * (A + D);
+    p = n1 + x / D;
+    z = x - (p - n1) * D;
+  }
+  w.b = p;
+  if (z < K) {
+    w.kind = 0;
+    w.idx = A - 1 + z;  // the items of target row N follow the sequence's other items
+  } else {
+    w.kind = 2;
+    w.idx = z - K;
+  }
   return w;
 }
 
