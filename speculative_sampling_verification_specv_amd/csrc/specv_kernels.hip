@@ -903,8 +903,9 @@ __device__ __forceinline__ SeqInfo uniform(const SeqInfo& s) {
 // Whether a whole call reads each sequence's target row N late in the launch
 // (after the accept tests; see decide and role_of). Row N only matters to a
 // sequence's draw when every draft is accepted, which long drafts rarely
-// are; there this takes 1.5 us off B = 32, N = 16 and moves nothing for
-// shorter drafts (B = 64, N = 5 level, B = 256, N = 7 2 us slower).
+// are; there it takes about 1.7 us off B = 32, N = 16 fp32, while for
+// shorter drafts it moves nothing or costs (B = 64, N = 5 level, B = 256,
+// N = 7 2 us slower).
 constexpr int kLateRowNDrafts = 8;
 __device__ __forceinline__ bool late_row_n(const Params& P) { return !P.lazy && P.n_draft >= kLateRowNDrafts; }
 
@@ -1031,67 +1032,67 @@ __device__ __forceinline__ void decide(const Params& P, Shared& sh, const Stage&
   const int rows_per_wave = 64 / cs;
   const int seg = lane / cs, k_in_seg = lane - seg * cs;
   bool timed_out = go < 0, any_bad = false;
-  // Takes the partials of the stage's rows [r0, r1) a group at a time and
-  // merges them (unless the sequence has failed); returns whether a partial
-  // of these rows came too late.
-  auto take_rows = [&](int r0, int r1) -> bool {
+  // Takes the partials of the stage's rows [first, end) a group at a time
+  // and merges them (unless the sequence has failed); returns whether a
+  // partial of these rows came too late.
+  auto take_rows = [&](int first, int end) -> bool {
     const uint64_t deadline = deadline_after(P.wait_ticks);
     bool rows_late = false;
-    for (int rg = r0; rg < r1; rg += rows_per_group) {
-    const int nr = min(rows_per_group, r1 - rg);
-    const int np = nr * pr;
-    bool late = false;
-    if (tid < np) {
-      Partial q;
-      const int kc = tid % pr;
-      late = !take_partial(P, part_b + int64_t(global_row(P, st, rg + tid / pr)) * pr + kc, kc * P.chunk, deadline, q);
-      ds.part[tid] = q;
-    }
-    // (also the barrier that makes the group's partials visible); the input
-    // checks join the first group's vote, so the partials are requested
-    // before anything waits for the draft tokens.
-    const int vote = block_any2(rg == 0 && bad, late);
-    any_bad = any_bad || (vote & 1);
-    rows_late = rows_late || (vote & 2);
-    if (any_bad || timed_out || rows_late) continue;
-    if (rg == 0) trace(2, 4);
-    for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
-      const int rr = r0 + seg;
-      const int r = global_row(P, st, rg + min(rr, nr - 1));
-      const bool row_ok = rr < nr && r >= r_first;
-      float m = -INFINITY, s = 0.0f;
-      int idx = INT_MAX;
-      if (row_ok) {
-        for (int k = k_in_seg; k < pr; k += cs) {
-          const Partial& q = ds.part[rr * pr + k];
-          if (greedy)
-            acc_merge<false>(m, s, idx, q.m, q.s, q.idx, c);
-          else
-            acc_merge<true>(m, s, idx, q.m, q.s, q.idx, c);
+    for (int rg = first; rg < end; rg += rows_per_group) {
+      const int nr = min(rows_per_group, end - rg);
+      const int np = nr * pr;
+      bool late = false;
+      if (tid < np) {
+        Partial q;
+        const int kc = tid % pr;
+        late = !take_partial(P, part_b + int64_t(global_row(P, st, rg + tid / pr)) * pr + kc, kc * P.chunk, deadline, q);
+        ds.part[tid] = q;
+      }
+      // (also the barrier that makes the group's partials visible); the input
+      // checks join the first group's vote, so the partials are requested
+      // before anything waits for the draft tokens.
+      const int vote = block_any2(rg == 0 && bad, late);
+      any_bad = any_bad || (vote & 1);
+      rows_late = rows_late || (vote & 2);
+      if (any_bad || timed_out || rows_late) continue;
+      if (rg == 0) trace(2, 4);
+      for (int r0 = wave * rows_per_wave; r0 < nr; r0 += kWaves * rows_per_wave) {
+        const int rr = r0 + seg;
+        const int r = global_row(P, st, rg + min(rr, nr - 1));
+        const bool row_ok = rr < nr && r >= r_first;
+        float m = -INFINITY, s = 0.0f;
+        int idx = INT_MAX;
+        if (row_ok) {
+          for (int k = k_in_seg; k < pr; k += cs) {
+            const Partial& q = ds.part[rr * pr + k];
+            if (greedy)
+              acc_merge<false>(m, s, idx, q.m, q.s, q.idx, c);
+            else
+              acc_merge<true>(m, s, idx, q.m, q.s, q.idx, c);
+          }
+        }
+        if (greedy) {
+          merge_step<false, kXor1>(m, s, idx, c);
+          merge_step<false, kXor2>(m, s, idx, c);
+        } else {
+          merge_step<true, kXor1>(m, s, idx, c);
+          merge_step<true, kXor2>(m, s, idx, c);
+        }
+        if (row_ok && k_in_seg == 0) {
+          if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
+          // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c)
+          // exactly; log2 s in fp32 (within 1e-7 of |log2 s|: s carries fp32
+          // rounding already).
+          const double logz =
+              greedy ? 0.0 : kLn2 * (double(__builtin_amdgcn_logf(s)) - double(fmaf(m, c, -scaled_max(m, c))));
+          ds.row_m[r] = m;
+          ds.row_logz[r] = logz;
+          ds.row_idx[r] = idx;
+          lse[r] = greedy ? double(NAN) : double(m) * inv_t + logz;
+          amax[r] = idx;
         }
       }
-      if (greedy) {
-        merge_step<false, kXor1>(m, s, idx, c);
-        merge_step<false, kXor2>(m, s, idx, c);
-      } else {
-        merge_step<true, kXor1>(m, s, idx, c);
-        merge_step<true, kXor2>(m, s, idx, c);
-      }
-      if (row_ok && k_in_seg == 0) {
-        if (idx == INT_MAX) idx = 0;  // an all -inf row: every index ties, the first wins
-        // log sum_x exp((z_x - m)/T) = ln2 * (log2 s - r), r = m*c - fl(m*c)
-        // exactly; log2 s in fp32 (within 1e-7 of |log2 s|: s carries fp32
-        // rounding already).
-        const double logz =
-            greedy ? 0.0 : kLn2 * (double(__builtin_amdgcn_logf(s)) - double(fmaf(m, c, -scaled_max(m, c))));
-        ds.row_m[r] = m;
-        ds.row_logz[r] = logz;
-        ds.row_idx[r] = idx;
-        lse[r] = greedy ? double(NAN) : double(m) * inv_t + logz;
-        amax[r] = idx;
-      }
-    }
-    barrier();
+      barrier();
     }
     return rows_late;
   };
