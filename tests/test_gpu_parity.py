@@ -183,6 +183,25 @@ def test_n_draft_limits(n_draft):
     tally.check(f"N={n_draft}")
 
 
+@pytest.mark.parametrize("sigma", [(0.02, 0.1), (1.0, 2.0)], ids=["mostly_bonus", "mostly_residual"])
+@pytest.mark.parametrize("n_draft", [7, 8, 9])
+def test_row_n_layouts(n_draft, sigma):
+    """Drafts of 8 or more read target row N late in the launch, after the
+    accept tests, and only sequences that accept every draft wait for it;
+    shorter drafts read it with their other rows. Both layouts around the
+    switch, with draws that are mostly bonus (small draft noise) or mostly
+    residual (large), greedy and sampled sequences mixed; every sequence's
+    tokens and count and every row's lse and argmax (row N's included)."""
+    require_gpu()
+    wl = synth.Workload("rowN", 12, 16, n_draft, 3 * 16384 + 37, "bf16", 2.5, 1.1, sigma, (1.0, 0.0))
+    total = Tally()
+    for seed in range(3):
+        b = synth.make_batch(wl, seed=60 + seed)
+        _, t = _parity(b, label=f"row N layouts N={n_draft} sigma={sigma} seed={60 + seed}")
+        total = total.merge(t)
+    total.check(f"row N layouts N={n_draft}")
+
+
 @pytest.mark.parametrize("T", [1e-6, 1e-3, 0.05, 50.0, 1e4])
 def test_temperature_extremes(T):
     require_gpu()
